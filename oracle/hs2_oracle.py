@@ -1,0 +1,280 @@
+"""Plain CPU oracle for the HySparse2 inner-level attention path (float64, NumPy).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The library under
+``token_level_sparse_full_amd/`` never imports it and shares no code with it.
+
+Everything here is the plain definition written out, slowly and in float64:
+
+* ``full_attn_scored``   exact causal MQA attention plus the per-token score row
+* ``select_topk_window`` the token-level selection: forced recent window plus
+                         the top-k highest-scoring older tokens
+* ``sparse_attn_reuse``  attention restricted to a selected index set
+* ``bridge_kv_proj``     the KV-Bridging re-projection of hidden states
+
+Sources (the pages about "HySparse2: Hybrid Sparse Attention with Two-Level KV
+Sharing"):
+
+* agihunt.info technical summary, paragraph on the inner level (KV Reuse): the
+  block-level top-k becomes token-level; the full-attention layer scores tokens
+  and the following sparse layers reuse the K/V of the chosen tokens; the
+  separate SWA branch is dropped and instead the 128 most recent tokens are
+  always kept and the 1024 best-scoring tokens outside that window are added;
+  local and global reads use the same full-attention K/V.
+* same summary, paragraph on model shapes: MQA (one K/V head), NoPE in full and
+  sparse layers, the full layer acts as an oracle selector using its exact
+  attention scores; head dims 256/256 (QK/V) in the comparison paragraph.
+* same summary, paragraph on the outer level (KV Bridging): each cross-decoder
+  full layer re-projects a self-decoder full layer's hidden state with its own
+  K/V projection.
+* arXiv abstract: KV caches of cross-decoder full layers are generated from the
+  hidden states of self-decoder full layers; a sliding window of recent tokens
+  is forced into the sparse selection.
+
+Readings taken where the pages are silent (each is listed with its reason in the
+design notes of the repository):
+
+* the per-token score of key j for a query is the softmax probability P[h, j]
+  summed over the query heads h (the pages only say "exact attention scores");
+* the softmax scale is an argument, 1/sqrt(d) by default (the pages give none);
+* the window of a query at position p is [p-127, p], i.e. it contains the query's
+  own token; candidates for the top-k part are [0, p-128];
+* ties in score are broken towards the lower token index;
+* the sparse layer's softmax is renormalised over the selected set only;
+* the bridge projection is a plain linear map (no norm, no bias).
+
+Inputs are raw storage arrays (float32 values, bf16 bit patterns as uint16, or
+e4m3 codes as uint8 plus a per-row float32 scale); this module decodes them to
+float64 itself, exactly.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_to_f64",
+    "f64_to_bf16_bits",
+    "e4m3_decode_table",
+    "decode_rows",
+    "full_attn_scored",
+    "select_topk_window",
+    "sparse_attn_reuse",
+    "bridge_kv_proj",
+]
+
+
+# ----------------------------------------------------------------------------
+# Storage formats
+# ----------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> exact float64 values.
+
+    A bfloat16 number is the upper half of a float32 with the same sign,
+    exponent and leading seven mantissa bits, so widening the pattern to 32
+    bits with zero low half gives the exact float32, and float32 -> float64 is
+    exact.
+    """
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bfloat16 (round to nearest, ties to even).
+
+    bfloat16 keeps 8 significant bits and the float32 exponent range.  The
+    value is rounded to a multiple of its quantum 2**(e-8) (e from frexp, so
+    |x| in [2**(e-1), 2**e)), with the quantum never below the subnormal step
+    2**-133.  np.rint rounds halves to even.  Results beyond the largest finite
+    bfloat16 become infinity.  Used only to compare float64 products with a
+    bfloat16 output.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.float64)
+    finite = np.isfinite(x)
+    xf = x[finite]
+    _, e = np.frexp(xf)
+    qexp = np.maximum(e - 8, -133)
+    r = np.rint(np.ldexp(xf, -qexp))
+    r = np.ldexp(r, qexp)
+    big = np.abs(r) >= 2.0 ** 128
+    r[big] = np.copysign(np.inf, r[big])
+    out[finite] = r
+    out[~finite] = x[~finite]
+    f32 = out.astype(np.float32)  # exact: at most 8 significant bits
+    return (f32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def e4m3_decode_table() -> np.ndarray:
+    """The 256 float64 values of the OCP FP8 E4M3 ("e4m3fn") format.
+
+    Layout of a code: sign (1 bit), exponent E (4 bits, bias 7), mantissa M
+    (3 bits).  E == 0 encodes subnormals M * 2**-9; E == 15 with M == 7 is NaN
+    (there are no infinities); every other code is (1 + M/8) * 2**(E-7).  The
+    largest finite magnitude is 1.75 * 2**8 = 448.  The pages only say the
+    KV cache is stored in FP8; this format with one float32 scale per cache row
+    is the reading adopted here.
+    """
+    t = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        s = -1.0 if (code >> 7) & 1 else 1.0
+        E = (code >> 3) & 0xF
+        M = code & 0x7
+        if E == 15 and M == 7:
+            t[code] = np.nan
+        elif E == 0:
+            t[code] = s * M * 2.0 ** -9
+        else:
+            t[code] = s * (1.0 + M / 8.0) * 2.0 ** (E - 7)
+    return t
+
+
+def decode_rows(raw: np.ndarray, kind: str, scale: np.ndarray | None = None) -> np.ndarray:
+    """Decode a stored tensor to float64.
+
+    kind: "f32" (float32 values), "bf16" (uint16 bit patterns) or "e4m3"
+    (uint8 codes; ``scale`` holds one float32 multiplier per row, i.e. per
+    entry of the leading axes, broadcast over the last axis).
+    """
+    if kind == "f32":
+        return np.asarray(raw, dtype=np.float32).astype(np.float64)
+    if kind == "bf16":
+        return bf16_bits_to_f64(raw)
+    if kind == "e4m3":
+        if scale is None:
+            raise ValueError("e4m3 rows need a per-row scale")
+        vals = e4m3_decode_table()[np.asarray(raw, dtype=np.uint8)]
+        return vals * np.asarray(scale, dtype=np.float32).astype(np.float64)[..., None]
+    raise ValueError(f"unknown storage kind {kind!r}")
+
+
+# ----------------------------------------------------------------------------
+# Stage a2: scored full attention
+# ----------------------------------------------------------------------------
+
+def full_attn_scored(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos0: int,
+                     sm_scale: float | None = None):
+    """Exact causal MQA attention of one sequence, with per-token scores.
+
+    q: [n_q, H, d] float64 queries; query i sits at position p = q_pos0 + i and
+       attends to keys 0..p (causal, NoPE: no positional rotation).
+    k, v: [T, d] float64, the single shared K/V head (MQA).
+
+    For every query and head h:  l_j = scale * <q_h, k_j>,  P_hj = softmax_j(l),
+    O_h = sum_j P_hj v_j,  lse_h = log sum_j exp(l_j).
+    The score of key j is s_j = sum_h P_hj (probabilities summed over heads).
+
+    Returns (o [n_q, H, d], lse [n_q, H], scores: list of n_q arrays, entry i
+    of length q_pos0 + i + 1).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n_q, H, d = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    o = np.zeros((n_q, H, d))
+    lse = np.zeros((n_q, H))
+    scores = []
+    for i in range(n_q):
+        p = q_pos0 + i
+        keys = k[: p + 1]                       # keys 0..p
+        vals = v[: p + 1]
+        logits = sm_scale * (q[i] @ keys.T)     # [H, p+1]
+        m = logits.max(axis=1, keepdims=True)
+        e = np.exp(logits - m)
+        z = e.sum(axis=1, keepdims=True)
+        prob = e / z                            # softmax over keys, per head
+        o[i] = prob @ vals
+        lse[i] = m[:, 0] + np.log(z[:, 0])
+        scores.append(prob.sum(axis=0))         # sum over query heads
+    return o, lse, scores
+
+
+# ----------------------------------------------------------------------------
+# Stage a3: token-level top-k with the forced recent window
+# ----------------------------------------------------------------------------
+
+def select_topk_window(scores: np.ndarray, p: int, window: int = 128, topk: int = 1024):
+    """Selected key set of the query at position p.
+
+    scores: at least p+1 entries; entry j is the score of key j.
+    The window W = [max(0, p-window+1), p] is always selected.  From the
+    candidates C = [0, p-window] the ``topk`` entries with the highest score
+    are added, ties going to the lower index (order by (-s_j, j)).  When C has
+    at most ``topk`` entries every key 0..p is selected.
+
+    Returns (idx, count, tau): idx is the selected set in ascending order,
+    count = len(idx) = min(p+1, window+topk), and tau is the score of the
+    last candidate admitted by the top-k (None when no cut was needed).
+    """
+    n = p + 1
+    s = np.asarray(scores, dtype=np.float64)[:n]
+    n_cand = max(0, n - window)
+    if n_cand <= topk:
+        sel = np.arange(n, dtype=np.int64)
+        return sel, n, None
+    cand = np.arange(n_cand, dtype=np.int64)
+    # Python's sort on (-score, index) is the definition of the order.
+    order = sorted(cand.tolist(), key=lambda j: (-s[j], j))
+    top = np.array(order[:topk], dtype=np.int64)
+    tau = float(s[order[topk - 1]])
+    win = np.arange(n_cand, n, dtype=np.int64)
+    sel = np.sort(np.concatenate([top, win]))
+    return sel, len(sel), tau
+
+
+# ----------------------------------------------------------------------------
+# Stage a4: sparse attention over the reused index set
+# ----------------------------------------------------------------------------
+
+def sparse_attn_reuse(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel: np.ndarray,
+                      sm_scale: float | None = None):
+    """Attention of one query token restricted to the key set ``sel``.
+
+    q: [H, d] float64 (the sparse layer's own query); k, v: [T, d] float64, the
+    full layer's shared K/V; sel: indices of the selected keys (any order).
+    The softmax is taken over the selected keys only.
+
+    Returns (o [H, d], lse [H]); an empty set gives o = 0 and lse = -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    H, d = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    sel = np.asarray(sel, dtype=np.int64)
+    if sel.size == 0:
+        return np.zeros((H, d)), np.full(H, -np.inf)
+    keys = np.asarray(k, dtype=np.float64)[sel]
+    vals = np.asarray(v, dtype=np.float64)[sel]
+    logits = sm_scale * (q @ keys.T)            # [H, |sel|]
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    z = e.sum(axis=1, keepdims=True)
+    o = (e / z) @ vals
+    lse = m[:, 0] + np.log(z[:, 0])
+    return o, lse
+
+
+# ----------------------------------------------------------------------------
+# Stage a1: KV Bridging re-projection
+# ----------------------------------------------------------------------------
+
+def bridge_kv_proj(x: np.ndarray, w_k: np.ndarray, w_v: np.ndarray):
+    """K and V of every bridged cross-decoder full layer.
+
+    x: [L, D] float64 hidden states of a self-decoder full layer.
+    w_k, w_v: [n_layers, D, d] float64, one projection pair per cross-decoder
+    full layer (each layer keeps its own projection; what is shared is x).
+    Returns (k [n_layers, L, d], v [n_layers, L, d]) with k[m] = x @ w_k[m] and
+    v[m] = x @ w_v[m], in float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w_k = np.asarray(w_k, dtype=np.float64)
+    w_v = np.asarray(w_v, dtype=np.float64)
+    k = np.stack([x @ w_k[m] for m in range(w_k.shape[0])])
+    v = np.stack([x @ w_v[m] for m in range(w_v.shape[0])])
+    return k, v

@@ -1,0 +1,423 @@
+"""Checks that tie the CPU oracle to facts outside itself.
+
+Each ``pin_*`` function takes the oracle module and raises AssertionError when
+it disagrees with a library routine, a closed form, an invariant of the method,
+a hand-worked example or a brute-force count.  ``test_oracle_pins.py`` runs them
+on the real oracle; ``test_oracle_mutations.py`` runs them on deliberately
+broken copies and expects at least one to fail for every planted mistake.
+"""
+
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _sdpa_reference(q, k, v, q_pos0, scale):
+    """torch scaled_dot_product_attention (float64, CPU) with a causal mask."""
+    n_q, H, d = q.shape
+    T = k.shape[0]
+    pos = q_pos0 + np.arange(n_q)
+    mask = torch.from_numpy(np.arange(T)[None, :] <= pos[:, None])       # [n_q, T]
+    qt = torch.from_numpy(q).permute(1, 0, 2)                            # [H, n_q, d]
+    kt = torch.from_numpy(k)[None].expand(H, T, d)
+    vt = torch.from_numpy(v)[None].expand(H, T, d)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+    logits = scale * (qt @ kt.transpose(1, 2))                           # [H, n_q, T]
+    logits = logits.masked_fill(~mask[None], float("-inf"))
+    lse = torch.logsumexp(logits, dim=-1)                                # [H, n_q]
+    prob = torch.softmax(logits, dim=-1)
+    return o.permute(1, 0, 2).numpy(), lse.T.numpy(), prob.permute(1, 0, 2).numpy()
+
+
+# ---------------------------------------------------------------------------
+# full attention with scores
+# ---------------------------------------------------------------------------
+
+def pin_attn_vs_torch(orc):
+    """O, lse and the probabilities against torch SDPA / logsumexp / softmax."""
+    r = _rng(11)
+    for (n_q, H, d, T, q_pos0) in [(5, 3, 8, 9, 3), (1, 16, 16, 40, 39), (7, 2, 4, 7, 0)]:
+        q = r.standard_normal((n_q, H, d))
+        k = r.standard_normal((T, d))
+        v = r.standard_normal((T, d))
+        scale = 0.37
+        o, lse, scores = orc.full_attn_scored(q, k, v, q_pos0, scale)
+        o_ref, lse_ref, prob_ref = _sdpa_reference(q, k, v, q_pos0, scale)
+        np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+        for i in range(n_q):
+            p = q_pos0 + i
+            assert scores[i].shape == (p + 1,)
+            np.testing.assert_allclose(scores[i], prob_ref[i, :, : p + 1].sum(axis=0), rtol=1e-12, atol=1e-14)
+
+
+def pin_attn_default_scale(orc):
+    """Without an explicit scale the softmax uses 1/sqrt(d)."""
+    r = _rng(12)
+    q = r.standard_normal((3, 2, 16))
+    k = r.standard_normal((6, 16))
+    v = r.standard_normal((6, 16))
+    o, lse, _ = orc.full_attn_scored(q, k, v, 2)
+    o_ref, lse_ref, _ = _sdpa_reference(q, k, v, 2, 0.25)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_attn_zero_query(orc):
+    """q = 0: uniform attention, O = mean of v_0..v_p, lse = ln(p+1), s_j = H/(p+1)."""
+    r = _rng(13)
+    H, d, T = 4, 8, 10
+    q = np.zeros((3, H, d))
+    k = r.standard_normal((T, d))
+    v = r.standard_normal((T, d))
+    o, lse, scores = orc.full_attn_scored(q, k, v, 5, 0.5)
+    for i in range(3):
+        p = 5 + i
+        for h in range(H):
+            np.testing.assert_allclose(o[i, h], v[: p + 1].mean(axis=0), rtol=1e-13, atol=1e-14)
+            assert abs(lse[i, h] - math.log(p + 1)) < 1e-13
+        np.testing.assert_allclose(scores[i], np.full(p + 1, H / (p + 1)), rtol=1e-13)
+
+
+def pin_attn_one_hot_values(orc):
+    """V = identity rows: O_h equals the probability row, so sum_h O_h is the score row."""
+    r = _rng(14)
+    H, d, T = 3, 8, 8
+    q = r.standard_normal((4, H, d))
+    k = r.standard_normal((T, d))
+    v = np.eye(T, d)
+    o, _, scores = orc.full_attn_scored(q, k, v, 3, 0.8)
+    for i in range(4):
+        p = 3 + i
+        np.testing.assert_allclose(o[i].sum(axis=0)[: p + 1], scores[i], rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(o[i, :, p + 1:], 0.0, atol=0)
+        np.testing.assert_allclose(o[i].sum(axis=1), np.ones(H), rtol=1e-12)
+
+
+def pin_attn_two_keys(orc):
+    """p = 1: P_1 = 1 / (1 + exp(l_0 - l_1)) per head (logistic closed form)."""
+    r = _rng(15)
+    H, d = 5, 6
+    q = r.standard_normal((1, H, d))
+    k = r.standard_normal((2, d))
+    v = r.standard_normal((2, d))
+    scale = 0.3
+    o, lse, scores = orc.full_attn_scored(q, k, v, 1, scale)
+    s_exp = 0.0
+    for h in range(H):
+        l0 = scale * float(q[0, h] @ k[0])
+        l1 = scale * float(q[0, h] @ k[1])
+        p1 = 1.0 / (1.0 + math.exp(l0 - l1))
+        np.testing.assert_allclose(o[0, h], (1 - p1) * v[0] + p1 * v[1], rtol=1e-12, atol=1e-14)
+        assert abs(lse[0, h] - (max(l0, l1) + math.log1p(math.exp(-abs(l0 - l1))))) < 1e-12
+        s_exp += p1
+    np.testing.assert_allclose(scores[0], [H - s_exp, s_exp], rtol=1e-12)
+
+
+def pin_attn_scores_sum_to_heads(orc):
+    """Every score row sums to H (each head's probabilities sum to one)."""
+    r = _rng(16)
+    H = 6
+    q = r.standard_normal((9, H, 8)) * 3
+    k = r.standard_normal((30, 8))
+    v = r.standard_normal((30, 8))
+    _, _, scores = orc.full_attn_scored(q, k, v, 21, 0.5)
+    for s in scores:
+        assert abs(s.sum() - H) < 1e-12
+        assert (s >= 0).all()
+
+
+def pin_attn_causal(orc):
+    """Keys and values after the query position do not matter."""
+    r = _rng(17)
+    q = r.standard_normal((2, 2, 8))
+    k = r.standard_normal((12, 8))
+    v = r.standard_normal((12, 8))
+    a = orc.full_attn_scored(q, k, v, 4, 0.5)
+    k2, v2 = k.copy(), v.copy()
+    k2[6:] = 100.0 * r.standard_normal((6, 8))
+    v2[6:] = 100.0 * r.standard_normal((6, 8))
+    b = orc.full_attn_scored(q, k2, v2, 4, 0.5)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+    for x, y in zip(a[2], b[2]):
+        np.testing.assert_array_equal(x, y)
+    # and a key before the position does matter
+    k3 = k.copy()
+    k3[0] += 1.0
+    c = orc.full_attn_scored(q, k3, v, 4, 0.5)
+    assert not np.allclose(a[2][0], c[2][0])
+
+
+def pin_attn_shift_invariance(orc):
+    """Adding c to every key shifts head h's logits by scale*<q_h, c>: P is unchanged."""
+    r = _rng(18)
+    q = r.standard_normal((3, 4, 8))
+    k = r.standard_normal((9, 8))
+    v = r.standard_normal((9, 8))
+    c = 2.0 * r.standard_normal(8)
+    a = orc.full_attn_scored(q, k, v, 5, 0.6)
+    b = orc.full_attn_scored(q, k + c, v, 5, 0.6)
+    np.testing.assert_allclose(a[0], b[0], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(b[1] - a[1], 0.6 * (q @ c), rtol=1e-10, atol=1e-12)
+    for x, y in zip(a[2], b[2]):
+        np.testing.assert_allclose(x, y, rtol=1e-11, atol=1e-14)
+
+
+def pin_attn_brute_force(orc):
+    """Scalar loops with math.exp / math.fsum on tiny inputs."""
+    r = _rng(19)
+    n_q, H, d, T, q0 = 3, 2, 3, 6, 2
+    q = r.standard_normal((n_q, H, d))
+    k = r.standard_normal((T, d))
+    v = r.standard_normal((T, d))
+    scale = 0.9
+    o, lse, scores = orc.full_attn_scored(q, k, v, q0, scale)
+    for i in range(n_q):
+        p = q0 + i
+        s_bf = [0.0] * (p + 1)
+        for h in range(H):
+            l = [scale * math.fsum(q[i, h, t] * k[j, t] for t in range(d)) for j in range(p + 1)]
+            big = max(l)
+            w = [math.exp(x - big) for x in l]
+            z = math.fsum(w)
+            for j in range(p + 1):
+                s_bf[j] += w[j] / z
+            for t in range(d):
+                ref = math.fsum(w[j] * v[j, t] for j in range(p + 1)) / z
+                assert abs(o[i, h, t] - ref) < 1e-12
+            assert abs(lse[i, h] - (big + math.log(z))) < 1e-12
+        np.testing.assert_allclose(scores[i], s_bf, rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# selection
+# ---------------------------------------------------------------------------
+
+def _count_rank_selection(s, p, window, topk):
+    """Independent brute force: a candidate is in the top-k when fewer than
+    topk candidates beat it (higher score, or equal score and lower index)."""
+    n = p + 1
+    n_cand = max(0, n - window)
+    chosen = set(range(n_cand, n))
+    for j in range(n_cand):
+        beaten_by = sum(1 for i in range(n_cand) if s[i] > s[j] or (s[i] == s[j] and i < j))
+        if beaten_by < topk:
+            chosen.add(j)
+    return sorted(chosen)
+
+
+def pin_select_golden(orc):
+    with open(os.path.join(GOLDEN, "select_worked_example.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        idx, count, tau = orc.select_topk_window(np.array(c["scores"]), c["p"], c["window"], c["topk"])
+        assert list(idx) == c["expected"], c["name"]
+        assert count == len(c["expected"]), c["name"]
+        assert tau == c["tau"], c["name"]
+
+
+def pin_select_brute_force(orc):
+    r = _rng(21)
+    for trial in range(200):
+        window = int(r.integers(1, 5))
+        topk = int(r.integers(1, 6))
+        p = int(r.integers(0, 16))
+        s = r.integers(0, 4, size=p + 1).astype(np.float64) / 4.0   # many ties
+        idx, count, _ = orc.select_topk_window(s, p, window, topk)
+        ref = _count_rank_selection(s, p, window, topk)
+        assert list(idx) == ref, (trial, s, p, window, topk)
+        assert count == len(ref)
+
+
+def pin_select_all_ties(orc):
+    """Equal scores: the top-k part is the k lowest candidate indices."""
+    for p in [1151, 1152, 1153, 2000, 4095]:
+        s = np.full(p + 1, 0.5)
+        idx, count, tau = orc.select_topk_window(s, p, 128, 1024)
+        expect = sorted(set(range(min(1024, p + 1))) | set(range(max(0, p - 127), p + 1)))
+        assert list(idx) == expect
+        assert count == min(p + 1, 1152)
+
+
+def pin_select_invariants(orc):
+    """|S| = min(p+1, window+topk), window inside S, strictly ascending, in [0, p]."""
+    r = _rng(22)
+    for p in [0, 1, 126, 127, 128, 129, 1150, 1151, 1152, 1153, 1279, 1280, 1281, 5000]:
+        s = r.random(p + 1)
+        idx, count, tau = orc.select_topk_window(s, p, 128, 1024)
+        assert count == len(idx) == min(p + 1, 1152)
+        assert np.all(np.diff(idx) > 0)
+        assert idx[0] >= 0 and idx[-1] == p
+        assert set(range(max(0, p - 127), p + 1)) <= set(idx.tolist())
+        if tau is not None:
+            cand = np.arange(p - 127)
+            chosen = np.intersect1d(idx, cand)
+            assert len(chosen) == 1024
+            assert s[chosen].min() == tau
+            others = np.setdiff1d(cand, chosen)
+            assert (s[others] <= tau).all()
+
+
+def pin_select_window_scores_ignored(orc):
+    """Scores inside the window never change which candidates are chosen."""
+    r = _rng(23)
+    p = 3000
+    s = r.random(p + 1)
+    a, _, _ = orc.select_topk_window(s, p, 128, 1024)
+    s2 = s.copy()
+    s2[p - 127:] = 1e9
+    b, _, _ = orc.select_topk_window(s2, p, 128, 1024)
+    np.testing.assert_array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# sparse attention over the selected set
+# ---------------------------------------------------------------------------
+
+def pin_sparse_vs_torch_mask(orc):
+    """Sparse attention equals torch SDPA with a boolean mask of the set."""
+    r = _rng(31)
+    H, d, T = 4, 8, 40
+    q = r.standard_normal((H, d))
+    k = r.standard_normal((T, d))
+    v = r.standard_normal((T, d))
+    sel = np.sort(r.choice(T, size=13, replace=False))
+    o, lse = orc.sparse_attn_reuse(q, k, v, sel, 0.45)
+    mask = torch.zeros(T, dtype=torch.bool)
+    mask[torch.from_numpy(sel)] = True
+    qt = torch.from_numpy(q)[:, None, :]
+    o_ref = torch.nn.functional.scaled_dot_product_attention(
+        qt, torch.from_numpy(k)[None].expand(H, T, d), torch.from_numpy(v)[None].expand(H, T, d),
+        attn_mask=mask[None, None, :].expand(H, 1, T), scale=0.45)[:, 0]
+    np.testing.assert_allclose(o, o_ref.numpy(), rtol=1e-12, atol=1e-12)
+    lg = 0.45 * (torch.from_numpy(q) @ torch.from_numpy(k).T)
+    lse_ref = torch.logsumexp(lg.masked_fill(~mask[None], float("-inf")), dim=-1)
+    np.testing.assert_allclose(lse, lse_ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def pin_sparse_equals_full_when_all_selected(orc):
+    """For p+1 <= window+topk the set is [0, p] and the sparse output is full attention."""
+    r = _rng(32)
+    H, d, T = 3, 8, 50
+    q = r.standard_normal((5, H, d))
+    k = r.standard_normal((T, d))
+    v = r.standard_normal((T, d))
+    o_full, lse_full, scores = orc.full_attn_scored(q, k, v, 20, 0.5)
+    for i in range(5):
+        p = 20 + i
+        sel, count, _ = orc.select_topk_window(scores[i], p, 128, 1024)
+        o, lse = orc.sparse_attn_reuse(q[i], k, v, sel, 0.5)
+        np.testing.assert_allclose(o, o_full[i], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse, lse_full[i], rtol=1e-12, atol=1e-13)
+
+
+def pin_sparse_order_invariance(orc):
+    """The order in which the set is listed does not matter."""
+    r = _rng(33)
+    q = r.standard_normal((2, 8))
+    k = r.standard_normal((30, 8))
+    v = r.standard_normal((30, 8))
+    sel = r.choice(30, size=11, replace=False)
+    a = orc.sparse_attn_reuse(q, k, v, np.sort(sel), 0.5)
+    b = orc.sparse_attn_reuse(q, k, v, sel[::-1].copy(), 0.5)
+    np.testing.assert_allclose(a[0], b[0], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(a[1], b[1], rtol=1e-13, atol=1e-14)
+
+
+def pin_sparse_single_and_empty(orc):
+    r = _rng(34)
+    q = r.standard_normal((3, 4))
+    k = r.standard_normal((5, 4))
+    v = r.standard_normal((5, 4))
+    o, lse = orc.sparse_attn_reuse(q, k, v, np.array([2]), 1.0)
+    np.testing.assert_allclose(o, np.tile(v[2], (3, 1)), rtol=0, atol=0)
+    np.testing.assert_allclose(lse, q @ k[2], rtol=1e-13)
+    o, lse = orc.sparse_attn_reuse(q, k, v, np.array([], dtype=np.int64), 1.0)
+    assert (o == 0).all() and np.isneginf(lse).all()
+
+
+# ---------------------------------------------------------------------------
+# KV Bridging projection
+# ---------------------------------------------------------------------------
+
+def pin_bridge_integer_exact(orc):
+    """Integer-valued inputs: the product equals exact int64 matrix products."""
+    r = _rng(41)
+    L, D, d, n = 7, 12, 5, 3
+    x = r.integers(-8, 9, size=(L, D))
+    wk = r.integers(-4, 5, size=(n, D, d))
+    wv = r.integers(-4, 5, size=(n, D, d))
+    k, v = orc.bridge_kv_proj(x.astype(np.float64), wk.astype(np.float64), wv.astype(np.float64))
+    for m in range(n):
+        np.testing.assert_array_equal(k[m], (x @ wk[m]).astype(np.float64))
+        np.testing.assert_array_equal(v[m], (x @ wv[m]).astype(np.float64))
+
+
+def pin_bridge_brute_force(orc):
+    r = _rng(42)
+    L, D, d, n = 3, 4, 2, 2
+    x = r.standard_normal((L, D))
+    wk = r.standard_normal((n, D, d))
+    wv = r.standard_normal((n, D, d))
+    k, v = orc.bridge_kv_proj(x, wk, wv)
+    for m, i, j in itertools.product(range(n), range(L), range(d)):
+        assert abs(k[m, i, j] - math.fsum(x[i, t] * wk[m, t, j] for t in range(D))) < 1e-13
+        assert abs(v[m, i, j] - math.fsum(x[i, t] * wv[m, t, j] for t in range(D))) < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# storage formats
+# ---------------------------------------------------------------------------
+
+def pin_bf16_decode(orc):
+    bits = np.arange(0, 65536, 7, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = orc.bf16_bits_to_f64(bits)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+
+
+def pin_bf16_round(orc):
+    r = _rng(51)
+    x = np.concatenate([r.standard_normal(20000) * 10.0 ** r.integers(-30, 30, 20000),
+                        r.standard_normal(1000)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(orc.f64_to_bf16_bits(x.astype(np.float64)), ref)
+    # hand-checked halfway cases (8 significant bits: the step above 1 is 2**-7)
+    cases = {1.0 + 2.0 ** -8: 0x3F80, 1.0 + 3 * 2.0 ** -8: 0x3F82,
+             -(1.0 + 2.0 ** -8 + 2.0 ** -30): 0xBF81, 2.0 ** -133: 0x0001, 3.0 * 2.0 ** -134: 0x0002,
+             3.4e38: 0x7F80, 3.3e38: 0x7F78}
+    for val, want in cases.items():
+        assert int(orc.f64_to_bf16_bits(np.array([val]))[0]) == want, val
+
+
+def pin_e4m3_table(orc):
+    t = orc.e4m3_decode_table()
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(t), np.isnan(ref))
+    assert np.array_equal(t[~np.isnan(t)], ref[~np.isnan(ref)])
+    assert t[0x7E] == 448.0 and t[0x01] == 2.0 ** -9 and t[0x08] == 2.0 ** -6
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF]) and np.isnan(t).sum() == 2
+
+
+def pin_decode_rows(orc):
+    codes = np.array([[0x38, 0xB8], [0x40, 0x01]], dtype=np.uint8)   # 1, -1 ; 2, 2**-9
+    scale = np.array([0.5, 4.0], dtype=np.float32)
+    np.testing.assert_array_equal(orc.decode_rows(codes, "e4m3", scale), [[0.5, -0.5], [8.0, 2.0 ** -7]])
+    np.testing.assert_array_equal(orc.decode_rows(np.array([0x3F80, 0xC000], dtype=np.uint16), "bf16"), [1.0, -2.0])
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,73 @@
+"""Plant plausible mistakes in copies of the oracle: the pins must catch each one.
+
+Every mutation below is a one-token slip (an off-by-one bound, a wrong sign,
+axis, operand or tie rule).  The mutated source is executed as a throw-away
+module on the CPU; the real oracle is untouched.
+"""
+import os
+import sys
+import types
+
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import oracle_pins  # noqa: E402
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "hs2_oracle.py")
+
+MUTATIONS = [
+    ("causal bound off by one", "keys = k[: p + 1]", "keys = k[: p]"),
+    ("value rows off by one", "vals = v[: p + 1]", "vals = v[1: p + 2]"),
+    ("wrong max sign", "e = np.exp(logits - m)\n        z = e.sum(axis=1, keepdims=True)\n        prob",
+     "e = np.exp(logits + m)\n        z = e.sum(axis=1, keepdims=True)\n        prob"),
+    ("scale dropped", "logits = sm_scale * (q[i] @ keys.T)", "logits = (q[i] @ keys.T)"),
+    ("values used as keys", "logits = sm_scale * (q[i] @ keys.T)", "logits = sm_scale * (q[i] @ vals.T)"),
+    ("lse without max", "lse[i] = m[:, 0] + np.log(z[:, 0])", "lse[i] = np.log(z[:, 0])"),
+    ("score as mean over heads", "scores.append(prob.sum(axis=0))", "scores.append(prob.mean(axis=0))"),
+    ("score from first head only", "scores.append(prob.sum(axis=0))", "scores.append(prob[0])"),
+    ("unnormalised probabilities", "prob = e / z                            # softmax",
+     "prob = e                                # softmax"),
+    ("default scale 1/d", "sm_scale = 1.0 / math.sqrt(d)\n    o = np.zeros", "sm_scale = 1.0 / d\n    o = np.zeros"),
+    ("tie to higher index", "key=lambda j: (-s[j], j)", "key=lambda j: (-s[j], -j)"),
+    ("ascending scores", "key=lambda j: (-s[j], j)", "key=lambda j: (s[j], j)"),
+    ("window one short", "n_cand = max(0, n - window)", "n_cand = max(0, n - window + 1)"),
+    ("window one long", "n_cand = max(0, n - window)", "n_cand = max(0, n - window - 1)"),
+    ("top-k one short", "top = np.array(order[:topk]", "top = np.array(order[:topk - 1]"),
+    ("cut test off by one", "if n_cand <= topk:", "if n_cand < topk:"),
+    ("tau from wrong rank", "tau = float(s[order[topk - 1]])", "tau = float(s[order[topk]])"),
+    ("sparse values unsorted", "vals = np.asarray(v, dtype=np.float64)[sel]",
+     "vals = np.asarray(v, dtype=np.float64)[np.sort(sel)]"),
+    ("sparse scale dropped", "logits = sm_scale * (q @ keys.T)            # [H, |sel|]",
+     "logits = (q @ keys.T)            # [H, |sel|]"),
+    ("sparse lse sign", "lse = m[:, 0] + np.log(z[:, 0])\n    return o, lse",
+     "lse = m[:, 0] - np.log(z[:, 0])\n    return o, lse"),
+    ("bridge V from W_k", "v = np.stack([x @ w_v[m]", "v = np.stack([x @ w_k[m]"),
+    ("bridge weight rows reversed", "k = np.stack([x @ w_k[m]", "k = np.stack([x @ w_k[m][::-1]"),
+    ("bf16 one bit short", "qexp = np.maximum(e - 8, -133)", "qexp = np.maximum(e - 7, -133)"),
+    ("bf16 truncation", "r = np.rint(np.ldexp(xf, -qexp))", "r = np.trunc(np.ldexp(xf, -qexp))"),
+    ("bf16 decode shift", "<< np.uint32(16)).view", "<< np.uint32(15)).view"),
+    ("e4m3 bias 8", "(1.0 + M / 8.0) * 2.0 ** (E - 7)", "(1.0 + M / 8.0) * 2.0 ** (E - 8)"),
+    ("e4m3 subnormal step", "t[code] = s * M * 2.0 ** -9", "t[code] = s * M * 2.0 ** -10"),
+    ("e4m3 scale ignored", "return vals * np.asarray(scale", "return vals + 0 * np.asarray(scale"),
+]
+
+
+def _mutant(old, new):
+    with open(SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation anchor not unique or missing: {old!r}"
+    mod = types.ModuleType("hs2_oracle_mutant")
+    exec(compile(src.replace(old, new), "hs2_oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_mutation(name, old, new):
+    mod = _mutant(old, new)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception:  # noqa: BLE001 - any failure counts as caught
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake: {name}"
