@@ -1,0 +1,194 @@
+/*
+ * hs2.h - C ABI of the MI355X (gfx950) HySparse2 inner-level attention library.
+ *
+ * The method (pages on "HySparse2: Hybrid Sparse Attention with Two-Level KV
+ * Sharing"): a cross-decoder full-attention layer computes exact causal MQA
+ * attention (one K/V head, head dim 256, no positional rotation) and, acting as
+ * a selector, scores every past token; each query then keeps the 128 most
+ * recent tokens plus the 1024 best-scoring older tokens; the sparse layers that
+ * follow attend over those rows of the same K/V cache.  The K/V of the full
+ * layer come from KV Bridging: a re-projection of a self-decoder full layer's
+ * hidden state with the layer's own projection.
+ *
+ * Conventions shared by every entry point
+ *  - Tensor pointers are DEVICE memory owned by the caller.  The library never
+ *    allocates, frees or keeps them beyond the call.  Scratch memory is passed
+ *    in as `workspace` (device memory, `ws_bytes` long, 256-byte aligned);
+ *    query the size with the matching *_workspace_bytes function.
+ *  - Every call enqueues work on `stream` (a hipStream_t passed as void*; NULL
+ *    is the null stream) and returns without synchronising.
+ *  - Return value: HS2_OK (0) or a negative hs2_status.  All argument checks
+ *    are pure host code and run before any HIP call; on an error nothing is
+ *    enqueued and no output is written.  HS2_ERR_HIP reports a failed launch;
+ *    hs2_last_error() then describes it (thread-local string).
+ *  - Layouts are dense, row-major, innermost dimension last.  Pointers must be
+ *    16-byte aligned (scale vectors and index/count arrays: 4-byte aligned).
+ *  - dtypes: HS2_F32 (float32), HS2_BF16 (bfloat16), HS2_FP8E4M3 (OCP e4m3fn
+ *    codes, K/V caches only, each row of 256 codes multiplied by one float32
+ *    scale from k_scale / v_scale).  Supported pairs (q, kv): (F32, F32),
+ *    (BF16, BF16), (BF16, FP8E4M3).
+ *  - Head dim d must be 256; query heads H in {1, 2, 4, 8, 16}.
+ *  - Results are deterministic: no floating-point atomics on any output path.
+ *  - Inputs are not checked for NaN/Inf; finite results need finite inputs.
+ *  - The library is stateless apart from the thread-local error string, and
+ *    calls may be made from several host threads.
+ */
+#ifndef HS2_H_
+#define HS2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum hs2_status {
+  HS2_OK = 0,
+  HS2_ERR_NULL = -1,        /* a required pointer is NULL                       */
+  HS2_ERR_SHAPE = -2,       /* a size is out of range or sizes are inconsistent */
+  HS2_ERR_DTYPE = -3,       /* unknown dtype or unsupported (q, kv) pair        */
+  HS2_ERR_UNSUPPORTED = -4, /* d != 256, H not in {1,2,4,8,16}, ...             */
+  HS2_ERR_ALIGN = -5,       /* a pointer is not aligned as required             */
+  HS2_ERR_WORKSPACE = -6,   /* workspace missing or too small                   */
+  HS2_ERR_HIP = -7          /* a HIP launch failed; see hs2_last_error()        */
+};
+
+enum hs2_dtype { HS2_F32 = 0, HS2_BF16 = 1, HS2_FP8E4M3 = 2 };
+
+#define HS2_HEAD_DIM 256
+#define HS2_MAX_HEADS 16
+#define HS2_MAX_SELECT 4096 /* largest window + topk accepted by the selector */
+
+/*
+ * hs2_full_attn_scored - scored full attention (the selector layer).
+ *
+ * Defines (HySparse2 pages: agihunt.info summary, paragraphs on the inner level
+ * and on model shapes -- exact attention scores of the MQA NoPE full layer pick
+ * the tokens the sparse layers reuse):
+ *   for sequence b, query i at position p = q_pos0 + i, head h:
+ *     l_j   = sm_scale * <q[b,i,h,:], k[b,j,:]>           for j = 0..p
+ *     P_j   = exp(l_j - lse),  lse = log sum_{j<=p} exp(l_j)
+ *     o[b,i,h,:]   = sum_j P_j v[b,j,:]
+ *     lse[b,i,h]   = lse
+ *     scores[b,i,j] = sum_h P_hj   (probabilities summed over the query heads)
+ *
+ *   q       [B, n_q, H, d]   q_dtype (HS2_F32 or HS2_BF16)
+ *   k, v    [B, T, d]        kv_dtype; for HS2_FP8E4M3 k_scale, v_scale [B, T]
+ *                            float32 row scales are required, else they must be NULL
+ *   o       [B, n_q, H, d]   written, dtype q_dtype
+ *   lse     [B, n_q, H]      float32, natural log; may be NULL
+ *   scores  [B, n_q, ld_scores] float32; row i gets columns 0..q_pos0+i, the
+ *                            other columns are left untouched
+ * Requires 1 <= n_q, 0 <= q_pos0, q_pos0 + n_q <= T, ld_scores >= q_pos0 + n_q,
+ * ld_scores a multiple of 4, sm_scale > 0.
+ * FP8 caches are supported when n_q * H <= 16 (decode); larger FP8 calls return
+ * HS2_ERR_UNSUPPORTED.
+ */
+int hs2_full_attn_scored(const void* q, int q_dtype, int B, int n_q, int H, int d,
+                         const void* k, const void* v, int kv_dtype,
+                         const float* k_scale, const float* v_scale, int64_t T,
+                         int64_t q_pos0, float sm_scale,
+                         void* o, float* lse, float* scores, int64_t ld_scores,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+size_t hs2_full_attn_workspace_bytes(int B, int n_q, int H, int64_t T, int kv_dtype);
+
+/*
+ * hs2_select_topk_window - token-level top-k with the forced recent window.
+ *
+ * Defines (HySparse2 pages: agihunt.info summary, paragraph on the inner level
+ * -- the separate sliding-window branch is removed; the most recent 128 tokens
+ * are forced into the selection and the 1024 best-scoring tokens outside that
+ * window are added; arXiv abstract -- a sliding window of recent tokens is
+ * forced into the sparse selection):
+ *   for query i of sequence b at position p = q_pos0 + i:
+ *     W = [max(0, p-window+1), p]        (always selected)
+ *     C = [0, p-window]                  (candidates)
+ *     if |C| <= topk: S = [0, p]
+ *     else S = W + the topk candidates of largest score, ties to lower index
+ *   idx[b,i,:]  the members of S in ascending order, then -1 up to window+topk
+ *   count[b,i]  |S| = min(p+1, window+topk)
+ *
+ *   scores  [B, n_q, ld_scores] float32, non-negative (as written by
+ *           hs2_full_attn_scored); columns 0..p of row i are read
+ *   idx     [B, n_q, window+topk] int32, written
+ *   count   [B, n_q] int32, written
+ * Requires window >= 1, topk >= 1, window + topk <= HS2_MAX_SELECT,
+ * q_pos0 + n_q <= T, ld_scores >= q_pos0 + n_q.  The comparison is exact on
+ * the float32 values (negative zero, NaN and negative scores are outside the
+ * contract).
+ */
+int hs2_select_topk_window(const float* scores, int64_t ld_scores, int B, int n_q, int64_t T,
+                           int64_t q_pos0, int window, int topk,
+                           int32_t* idx, int32_t* count,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+size_t hs2_select_workspace_bytes(int B, int n_q, int64_t T, int64_t q_pos0);
+
+/*
+ * hs2_sparse_attn_reuse - a sparse layer over the reused index set.
+ *
+ * Defines (HySparse2 pages: agihunt.info summary, paragraph on the inner level
+ * -- the sparse layers reuse the K/V of the selected tokens, and local and
+ * global reads use the same full-attention K/V):
+ *   for sequence b, query i, head h, with S = idx[b,i,0..count[b,i]-1]:
+ *     o[b,i,h,:] = sum_{j in S} softmax_{j in S}(sm_scale <q[b,i,h,:], k[b,j,:]>) v[b,j,:]
+ *     lse[b,i,h] = log sum_{j in S} exp(sm_scale <q[b,i,h,:], k[b,j,:]>)
+ *
+ *   q      [B, n_q, H, d]    the sparse layer's own queries (q_dtype)
+ *   k, v   [B, T, d]         the full layer's cache (kv_dtype, scales as above)
+ *   idx    [B, n_q, max_sel] int32 key indices; count [B, n_q] int32
+ *   o      [B, n_q, H, d]    written, dtype q_dtype
+ *   lse    [B, n_q, H]       float32, may be NULL
+ * count is clamped to [0, max_sel]; entries outside [0, T) are skipped (never
+ * read).  An empty set yields o = 0 and lse = -inf.  Requires 1 <= max_sel <=
+ * HS2_MAX_SELECT.
+ */
+int hs2_sparse_attn_reuse(const void* q, int q_dtype, int B, int n_q, int H, int d,
+                          const void* k, const void* v, int kv_dtype,
+                          const float* k_scale, const float* v_scale, int64_t T,
+                          const int32_t* idx, const int32_t* count, int max_sel, float sm_scale,
+                          void* o, float* lse, void* stream);
+
+/*
+ * hs2_bridge_kv_proj - KV Bridging re-projection.
+ *
+ * Defines (HySparse2 pages: agihunt.info summary, paragraph on the outer level
+ * -- a cross-decoder full layer gets its K/V by re-projecting the hidden state
+ * of the matching self-decoder full layer, each layer with its own K/V
+ * projection; arXiv abstract -- the cross-decoder full-layer KV caches are
+ * generated from self-decoder full-layer hidden states):
+ *   k_out[m, i, :] = bf16_rne( sum_t x[i,t] * w_k[m,t,:] )   (float32 accumulation)
+ *   v_out[m, i, :] = bf16_rne( sum_t x[i,t] * w_v[m,t,:] )
+ *
+ *   x            [L, D] bf16
+ *   w_k, w_v     [n_layers, D, d] bf16
+ *   k_out, v_out layer m starts at element m * out_layer_stride; rows of d
+ *                elements follow contiguously ([n_layers][L][d] when
+ *                out_layer_stride == L*d; a larger stride writes into caches
+ *                of T >= L rows, e.g. appending decode rows)
+ * Requires L >= 1, D a positive multiple of 32, d == 256, 1 <= n_layers <= 64,
+ * out_layer_stride >= L * d.
+ */
+int hs2_bridge_kv_proj(const void* x, int64_t L, int D,
+                       const void* w_k, const void* w_v, int n_layers, int d,
+                       void* k_out, void* v_out, int64_t out_layer_stride,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+size_t hs2_bridge_workspace_bytes(int n_layers, int D, int d);
+
+/* Human-readable name of a status code (static string). */
+const char* hs2_status_str(int status);
+
+/* Detail of the last error on this thread ("" if none). */
+const char* hs2_last_error(void);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int hs2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HS2_H_ */

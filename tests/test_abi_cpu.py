@@ -1,0 +1,158 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+of include/hs2.h, and rejects invalid arguments in host code before any HIP
+call (fake device addresses are never dereferenced on these paths)."""
+import ctypes
+
+import pytest
+
+from token_level_sparse_full_amd import hs2
+
+A = 0x7F0000000000          # 256-byte aligned fake device address
+MIS = A + 8                 # misaligned for 16-byte checks
+F32, BF16, FP8 = hs2.HS2_F32, hs2.HS2_BF16, hs2.HS2_FP8E4M3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return hs2.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = hs2.header_symbols()
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.hs2_version() == 10000
+    for code in range(0, -8, -1):
+        assert lib.hs2_status_str(code).decode().startswith("HS2_")
+    assert b"unknown" in lib.hs2_status_str(-99)
+
+
+def full(lib, **kw):
+    a = dict(q=A, qd=BF16, B=1, n_q=1, H=16, d=256, k=A, v=A, kvd=BF16, ks=None, vs=None, T=100, q0=99, sc=0.0625,
+             o=A, lse=A, scores=A, ld=100, ws=A, wsb=1 << 40)
+    a.update(kw)
+    return lib.hs2_full_attn_scored(a["q"], a["qd"], a["B"], a["n_q"], a["H"], a["d"], a["k"], a["v"], a["kvd"],
+                                    a["ks"], a["vs"], a["T"], a["q0"], a["sc"], a["o"], a["lse"], a["scores"],
+                                    a["ld"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), hs2.HS2_ERR_NULL),
+    (dict(scores=None), hs2.HS2_ERR_NULL),
+    (dict(d=128), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(H=3), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(H=32), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(qd=F32), hs2.HS2_ERR_DTYPE),
+    (dict(qd=7), hs2.HS2_ERR_DTYPE),
+    (dict(kvd=FP8), hs2.HS2_ERR_NULL),
+    (dict(ks=A, vs=A), hs2.HS2_ERR_DTYPE),
+    (dict(q=MIS), hs2.HS2_ERR_ALIGN),
+    (dict(scores=MIS), hs2.HS2_ERR_ALIGN),
+    (dict(q0=100), hs2.HS2_ERR_SHAPE),
+    (dict(q0=-1), hs2.HS2_ERR_SHAPE),
+    (dict(n_q=0), hs2.HS2_ERR_SHAPE),
+    (dict(ld=96), hs2.HS2_ERR_SHAPE),
+    (dict(ld=102), hs2.HS2_ERR_SHAPE),
+    (dict(sc=0.0), hs2.HS2_ERR_SHAPE),
+    (dict(sc=float("nan")), hs2.HS2_ERR_SHAPE),
+    (dict(ws=None), hs2.HS2_ERR_WORKSPACE),
+    (dict(wsb=16), hs2.HS2_ERR_WORKSPACE),
+    (dict(ws=A + 16), hs2.HS2_ERR_ALIGN),
+    (dict(kvd=FP8, ks=A, vs=A, n_q=4, q0=96, H=16), hs2.HS2_ERR_UNSUPPORTED),
+])
+def test_full_attn_rejects(lib, kw, code):
+    assert full(lib, **kw) == code
+    assert lib.hs2_last_error().decode() != ""
+
+
+def test_workspace_sizes(lib):
+    # decode rows (n_q * H <= 16) need logits and partial states; prefill needs none
+    big = lib.hs2_full_attn_workspace_bytes(1, 1, 16, 1 << 20, FP8)
+    assert big >= (1 << 20) * 16 * 4
+    assert lib.hs2_full_attn_workspace_bytes(1, 2048, 4, 2048, F32) == 0
+    assert lib.hs2_full_attn_workspace_bytes(16, 1, 16, 32768, BF16) >= 16 * 32768 * 16 * 4
+    assert lib.hs2_bridge_workspace_bytes(4, 2048, 256) == 0
+    assert lib.hs2_select_workspace_bytes(1, 1, 1 << 20, (1 << 20) - 1) == 0
+
+
+def sel(lib, **kw):
+    a = dict(scores=A, ld=1152, B=1, n_q=1, T=1152, q0=1151, w=128, k=1024, idx=A, count=A, ws=None, wsb=0)
+    a.update(kw)
+    return lib.hs2_select_topk_window(a["scores"], a["ld"], a["B"], a["n_q"], a["T"], a["q0"], a["w"], a["k"],
+                                      a["idx"], a["count"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(scores=None), hs2.HS2_ERR_NULL),
+    (dict(idx=None), hs2.HS2_ERR_NULL),
+    (dict(w=0), hs2.HS2_ERR_SHAPE),
+    (dict(k=0), hs2.HS2_ERR_SHAPE),
+    (dict(w=2048, k=2049), hs2.HS2_ERR_SHAPE),
+    (dict(q0=1152), hs2.HS2_ERR_SHAPE),
+    (dict(ld=1150), hs2.HS2_ERR_SHAPE),
+    (dict(ld=1153), hs2.HS2_ERR_SHAPE),
+    (dict(scores=MIS), hs2.HS2_ERR_ALIGN),
+    (dict(idx=A + 2), hs2.HS2_ERR_ALIGN),
+    (dict(B=0), hs2.HS2_ERR_SHAPE),
+])
+def test_select_rejects(lib, kw, code):
+    assert sel(lib, **kw) == code
+
+
+def sparse(lib, **kw):
+    a = dict(q=A, qd=BF16, B=1, n_q=1, H=16, d=256, k=A, v=A, kvd=BF16, ks=None, vs=None, T=100, idx=A, count=A,
+             ms=1152, sc=0.0625, o=A, lse=None)
+    a.update(kw)
+    return lib.hs2_sparse_attn_reuse(a["q"], a["qd"], a["B"], a["n_q"], a["H"], a["d"], a["k"], a["v"], a["kvd"],
+                                     a["ks"], a["vs"], a["T"], a["idx"], a["count"], a["ms"], a["sc"], a["o"],
+                                     a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(idx=None), hs2.HS2_ERR_NULL),
+    (dict(count=None), hs2.HS2_ERR_NULL),
+    (dict(ms=0), hs2.HS2_ERR_SHAPE),
+    (dict(ms=5000), hs2.HS2_ERR_SHAPE),
+    (dict(d=64), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(kvd=FP8), hs2.HS2_ERR_NULL),
+    (dict(qd=F32), hs2.HS2_ERR_DTYPE),
+    (dict(o=MIS), hs2.HS2_ERR_ALIGN),
+    (dict(lse=A + 2), hs2.HS2_ERR_ALIGN),
+    (dict(T=0), hs2.HS2_ERR_SHAPE),
+])
+def test_sparse_rejects(lib, kw, code):
+    assert sparse(lib, **kw) == code
+
+
+def bridge(lib, **kw):
+    a = dict(x=A, L=4096, D=2048, wk=A, wv=A, n=4, d=256, ko=A, vo=A, st=4096 * 256, ws=None, wsb=0)
+    a.update(kw)
+    return lib.hs2_bridge_kv_proj(a["x"], a["L"], a["D"], a["wk"], a["wv"], a["n"], a["d"], a["ko"], a["vo"],
+                                  a["st"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), hs2.HS2_ERR_NULL),
+    (dict(vo=None), hs2.HS2_ERR_NULL),
+    (dict(d=128), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(D=2047), hs2.HS2_ERR_SHAPE),
+    (dict(D=16), hs2.HS2_ERR_SHAPE),
+    (dict(L=0), hs2.HS2_ERR_SHAPE),
+    (dict(n=0), hs2.HS2_ERR_SHAPE),
+    (dict(n=65), hs2.HS2_ERR_SHAPE),
+    (dict(st=4096 * 256 - 1), hs2.HS2_ERR_SHAPE),
+    (dict(wk=MIS), hs2.HS2_ERR_ALIGN),
+])
+def test_bridge_rejects(lib, kw, code):
+    assert bridge(lib, **kw) == code
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(hs2, "_lib", None)
+    monkeypatch.setattr(hs2, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        hs2.lib()

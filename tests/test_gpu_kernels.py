@@ -1,0 +1,226 @@
+"""GPU parity of each C-ABI entry point against the float64 oracle.
+
+Sizes are small enough for the oracle to finish in seconds while spanning
+several key tiles, several workgroups and ragged tails.  The acceptance rules
+are stated in parity.py.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import parity  # noqa: E402
+
+import oracle  # noqa: E402
+from token_level_sparse_full_amd import hs2, inputs  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SCALE = 1.0 / 16.0
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+# --------------------------------------------------------------------------- sparse reuse
+def _random_sets(rng, B, n_q, T, sizes, max_sel, with_invalid):
+    idx = np.full((B, n_q, max_sel), -1, dtype=np.int32)
+    cnt = np.zeros((B, n_q), dtype=np.int32)
+    for b in range(B):
+        for i in range(n_q):
+            n = sizes[(b * n_q + i) % len(sizes)]
+            sel = rng.choice(T, size=n, replace=False).astype(np.int32)
+            if with_invalid and n > 3 and i % 3 == 0:
+                sel[rng.integers(0, n)] = -1
+                sel[rng.integers(0, n)] = T + int(rng.integers(0, 5))
+            idx[b, i, :n] = sel
+            cnt[b, i] = n
+    return idx, cnt
+
+
+@pytest.mark.parametrize("kv,H", [("bf16", 16), ("bf16", 4), ("e4m3", 16), ("f32", 4), ("f32", 16), ("bf16", 1)])
+def test_sparse_reuse_parity(kv, H):
+    say("sparse", kv, H)
+    B, n_q, T, max_sel = 2, 24, 3000, 1152
+    inp = inputs.attention_inputs(B=B, n_q=n_q, T=T, H=H, d=256, kv=kv, n_sparse=0, seed=11, device=DEV)
+    rng = np.random.default_rng(5)
+    idx, cnt = _random_sets(rng, B, n_q, T, [0, 1, 5, 31, 32, 33, 100, 1152, 700, 17], max_sel, True)
+    o, lse = hs2.hs2_sparse_attn_reuse(inp["q"], inp["k"], inp["v"], torch.from_numpy(idx).to(DEV),
+                                       torch.from_numpy(cnt).to(DEV), sm_scale=SCALE,
+                                       k_scale=inp["k_scale"], v_scale=inp["v_scale"])
+    torch.cuda.synchronize()
+    q64 = parity.decode(inp["q"])
+    o_ref = np.zeros((B, n_q, H, 256))
+    lse_ref = np.zeros((B, n_q, H))
+    for b in range(B):
+        k64, v64 = parity.kv_f64(inp, b)
+        for i in range(n_q):
+            sel = idx[b, i, : cnt[b, i]]
+            sel = sel[(sel >= 0) & (sel < T)]
+            o_ref[b, i], lse_ref[b, i] = oracle.sparse_attn_reuse(q64[b, i], k64, v64, sel, SCALE)
+    parity.check_out(o, o_ref, kv)
+    lg = lse.cpu().numpy()
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lg), empty)
+    parity.check_lse(torch.from_numpy(lg[~empty]), lse_ref[~empty])
+
+
+# --------------------------------------------------------------------------- selection
+def _select_case(scores_np, q_pos0, T, window, topk):
+    B, n_q, ld = scores_np.shape
+    s = torch.from_numpy(scores_np).to(DEV)
+    idx, cnt = hs2.hs2_select_topk_window(s, q_pos0=q_pos0, T=T, window=window, topk=topk)
+    torch.cuda.synchronize()
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(B):
+        for i in range(n_q):
+            p = q_pos0 + i
+            parity.check_selection(idx[b, i], int(cnt[b, i]), scores_np[b, i, : p + 1].astype(np.float64), p,
+                                   window, topk, exact=True)
+
+
+@pytest.mark.parametrize("q_pos0,n_q,T", [(0, 140, 200), (1100, 200, 1400), (9000, 40, 9100), (40000, 3, 40004)])
+def test_select_parity(q_pos0, n_q, T):
+    say("select", q_pos0, n_q, T)
+    rng = np.random.default_rng(q_pos0 + 7)
+    ld = (q_pos0 + n_q + 3) // 4 * 4
+    B = 2
+    sc = np.zeros((B, n_q, ld), dtype=np.float32)
+    for b in range(B):
+        for i in range(n_q):
+            n = q_pos0 + i + 1
+            mode = (b * n_q + i) % 5
+            if mode == 0:      # smooth random
+                row = rng.random(n, dtype=np.float32) / n
+            elif mode == 1:    # heavy ties
+                row = (rng.integers(0, 7, n) / 64.0).astype(np.float32)
+            elif mode == 2:    # all equal
+                row = np.full(n, 1.0 / n, dtype=np.float32)
+            elif mode == 3:    # zeros with a few spikes
+                row = np.zeros(n, dtype=np.float32)
+                row[rng.integers(0, n, size=min(n, 50))] = 1.0
+            else:              # near-uniform: differences only in low mantissa bits
+                row = (np.float32(1.0 / 4096) * (1 + rng.integers(0, 16, n) * np.float32(2 ** -20))).astype(np.float32)
+            sc[b, i, :n] = row
+    _select_case(sc, q_pos0, T, 128, 1024)
+
+
+def test_select_small_window_topk():
+    say("select small")
+    rng = np.random.default_rng(3)
+    q_pos0, n_q, T = 0, 64, 64
+    sc = (rng.integers(0, 5, size=(1, n_q, 64)) / 8.0).astype(np.float32)
+    _select_case(sc, q_pos0, T, 2, 3)
+
+
+# --------------------------------------------------------------------------- scored full attention
+def _oracle_full(inp, b, q_pos0):
+    k64, v64 = parity.kv_f64(inp, b)
+    q64 = parity.decode(inp["q"][b])
+    return oracle.full_attn_scored(q64, k64, v64, q_pos0, SCALE)
+
+
+def _check_full(inp, o, lse, scores, q_pos0, kv):
+    B, n_q = inp["q"].shape[:2]
+    s_np = scores.cpu().numpy()
+    for b in range(B):
+        o_ref, lse_ref, s_ref = _oracle_full(inp, b, q_pos0)
+        parity.check_out(o[b], o_ref, kv)
+        parity.check_lse(lse[b], lse_ref)
+        for i in range(n_q):
+            p = q_pos0 + i
+            parity.check_scores(s_np[b, i, : p + 1], s_ref[i], f"scores b={b} i={i}")
+
+
+@pytest.mark.parametrize("kv,H,q_pos0,n_q,T", [
+    ("bf16", 16, 300, 333, 700),
+    ("bf16", 16, 0, 70, 70),
+    ("bf16", 8, 130, 77, 300),
+    ("bf16", 4, 5, 100, 110),
+    ("f32", 4, 0, 200, 200),
+    ("f32", 16, 64, 40, 104),
+    ("bf16", 2, 0, 50, 50),
+    ("bf16", 1, 10, 90, 100),
+])
+def test_full_attn_prefill_parity(kv, H, q_pos0, n_q, T):
+    say("prefill", kv, H, q_pos0, n_q, T)
+    inp = inputs.attention_inputs(B=2, n_q=n_q, T=T, H=H, d=256, kv=kv, n_sparse=0, seed=21, device=DEV)
+    o, lse, scores = hs2.hs2_full_attn_scored(inp["q"], inp["k"], inp["v"], q_pos0=q_pos0, sm_scale=SCALE)
+    torch.cuda.synchronize()
+    _check_full(inp, o, lse, scores, q_pos0, kv)
+
+
+@pytest.mark.parametrize("kv,H,n_q,T,q_pos0", [
+    ("bf16", 16, 1, 5000, 4999),
+    ("bf16", 16, 1, 5000, 3000),
+    ("e4m3", 16, 1, 5000, 4999),
+    ("f32", 16, 1, 700, 699),
+    ("bf16", 8, 2, 2100, 2098),
+    ("bf16", 4, 4, 300, 200),
+    ("e4m3", 4, 2, 3000, 2998),
+])
+def test_full_attn_decode_parity(kv, H, n_q, T, q_pos0):
+    say("decode", kv, H, n_q, T, q_pos0)
+    inp = inputs.attention_inputs(B=3, n_q=n_q, T=T, H=H, d=256, kv=kv, n_sparse=0, seed=31, device=DEV)
+    o, lse, scores = hs2.hs2_full_attn_scored(inp["q"], inp["k"], inp["v"], q_pos0=q_pos0, sm_scale=SCALE,
+                                              k_scale=inp["k_scale"], v_scale=inp["v_scale"])
+    torch.cuda.synchronize()
+    _check_full(inp, o, lse, scores, q_pos0, kv)
+
+
+def test_full_attn_leaves_other_columns_untouched():
+    say("untouched columns")
+    inp = inputs.attention_inputs(B=1, n_q=20, T=64, H=16, d=256, kv="bf16", n_sparse=0, seed=3, device=DEV)
+    scores = torch.full((1, 20, 64), -7.0, device=DEV)
+    hs2.hs2_full_attn_scored(inp["q"], inp["k"], inp["v"], q_pos0=40, sm_scale=SCALE, scores=scores, ld_scores=64)
+    torch.cuda.synchronize()
+    s = scores.cpu().numpy()[0]
+    for i in range(20):
+        assert (s[i, 41 + i:] == -7.0).all()
+        assert (s[i, : 41 + i] >= 0).all()
+
+
+# --------------------------------------------------------------------------- bridge
+def _bf16_from_f32(x):
+    return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("L,D,n_layers", [(300, 256, 2), (1, 2048, 4), (513, 512, 1)])
+def test_bridge_integer_exact(L, D, n_layers):
+    say("bridge int", L, D, n_layers)
+    rng = np.random.default_rng(L + D)
+    x = rng.integers(-8, 9, size=(L, D))
+    wk = rng.integers(-4, 5, size=(n_layers, D, 256))
+    wv = rng.integers(-4, 5, size=(n_layers, D, 256))
+    k, v = hs2.hs2_bridge_kv_proj(_bf16_from_f32(x).to(DEV), _bf16_from_f32(wk).to(DEV), _bf16_from_f32(wv).to(DEV))
+    torch.cuda.synchronize()
+    k_ref, v_ref = oracle.bridge_kv_proj(x.astype(np.float64), wk.astype(np.float64), wv.astype(np.float64))
+    assert np.array_equal(inputs.raw_numpy(k), oracle.f64_to_bf16_bits(k_ref))
+    assert np.array_equal(inputs.raw_numpy(v), oracle.f64_to_bf16_bits(v_ref))
+
+
+def test_bridge_normal_within_one_ulp_and_strided_output():
+    say("bridge normal")
+    L, D, n_layers, T = 700, 2048, 2, 1024
+    inp = inputs.bridge_inputs(L=L, D=D, n_layers=n_layers, d=256, seed=4, device=DEV)
+    k_cache = torch.zeros((n_layers, T, 256), dtype=torch.bfloat16, device=DEV)
+    v_cache = torch.zeros((n_layers, T, 256), dtype=torch.bfloat16, device=DEV)
+    hs2.hs2_bridge_kv_proj(inp["x"], inp["w_k"], inp["w_v"], k_out=k_cache, v_out=v_cache, out_layer_stride=T * 256)
+    torch.cuda.synchronize()
+    x64, wk64, wv64 = parity.decode(inp["x"]), parity.decode(inp["w_k"]), parity.decode(inp["w_v"])
+    k_ref, v_ref = oracle.bridge_kv_proj(x64, wk64, wv64)
+    # |sum| of |x w| bounds the float32 accumulation error: allow 64 roundings of
+    # 2**-24 on that scale, plus one bf16 step of the result (the float32 sum may
+    # sit on the other side of a rounding boundary).
+    k_abs, v_abs = oracle.bridge_kv_proj(np.abs(x64), np.abs(wk64), np.abs(wv64))
+    for got, ref, mag in ((k_cache[:, :L], k_ref, k_abs), (v_cache[:, :L], v_ref, v_abs)):
+        g = parity.decode(got.contiguous())
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+        assert (np.abs(g - ref) <= ulp + 64 * 2.0 ** -24 * mag).all()
+        assert (np.abs(g - ref) <= ulp).mean() > 0.999
+    assert (k_cache[:, L:] == 0).all() and (v_cache[:, L:] == 0).all()

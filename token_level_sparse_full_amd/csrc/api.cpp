@@ -1,0 +1,198 @@
+// C ABI of libhs2 (declarations and contracts: include/hs2.h).
+//
+// Every entry point validates its arguments in plain host code first; only
+// when all checks pass does it touch HIP (kernel launches on the caller's
+// stream).  Errors never enqueue work or write outputs.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/hs2.h"
+#include "hs2_internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return HS2_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(HS2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool heads_ok(int H) { return H == 1 || H == 2 || H == 4 || H == 8 || H == 16; }
+
+// (q, kv) dtype pair check shared by the attention entry points.
+int check_dtypes(int q_dtype, int kv_dtype, const float* k_scale, const float* v_scale) {
+  const bool known = (q_dtype == HS2_F32 || q_dtype == HS2_BF16) &&
+                     (kv_dtype == HS2_F32 || kv_dtype == HS2_BF16 || kv_dtype == HS2_FP8E4M3);
+  if (!known) return fail(HS2_ERR_DTYPE, "unknown dtype (q=%d, kv=%d)", q_dtype, kv_dtype);
+  const bool pair = (q_dtype == HS2_F32 && kv_dtype == HS2_F32) || (q_dtype == HS2_BF16 && kv_dtype == HS2_BF16) ||
+                    (q_dtype == HS2_BF16 && kv_dtype == HS2_FP8E4M3);
+  if (!pair) return fail(HS2_ERR_DTYPE, "unsupported (q, kv) dtype pair (%d, %d)", q_dtype, kv_dtype);
+  if (kv_dtype == HS2_FP8E4M3) {
+    if (!k_scale || !v_scale) return fail(HS2_ERR_NULL, "FP8 caches need k_scale and v_scale");
+    if (!aligned(k_scale, 4) || !aligned(v_scale, 4)) return fail(HS2_ERR_ALIGN, "scale vectors must be 4-byte aligned");
+  } else if (k_scale || v_scale) {
+    return fail(HS2_ERR_DTYPE, "k_scale/v_scale are only used with FP8 caches; pass NULL");
+  }
+  return HS2_OK;
+}
+
+int check_attn_common(const void* q, int q_dtype, int B, int n_q, int H, int d, const void* k, const void* v,
+                      int kv_dtype, const float* k_scale, const float* v_scale, int64_t T, float sm_scale,
+                      const void* o, const float* lse) {
+  if (!q || !k || !v || !o) return fail(HS2_ERR_NULL, "q, k, v and o are required");
+  if (d != HS2_HEAD_DIM) return fail(HS2_ERR_UNSUPPORTED, "head dim %d unsupported (only %d)", d, HS2_HEAD_DIM);
+  if (!heads_ok(H)) return fail(HS2_ERR_UNSUPPORTED, "H=%d unsupported (1, 2, 4, 8 or 16)", H);
+  if (B < 1 || n_q < 1 || T < 1) return fail(HS2_ERR_SHAPE, "B, n_q and T must be >= 1 (B=%d n_q=%d T=%lld)", B, n_q, (long long)T);
+  if ((int64_t)B * n_q > 0x7FFFFFFF || T > 0x7FFFFFFF) return fail(HS2_ERR_SHAPE, "B*n_q and T must fit in int32");
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(HS2_ERR_SHAPE, "sm_scale must be finite and > 0");
+  const int rc = check_dtypes(q_dtype, kv_dtype, k_scale, v_scale);
+  if (rc != HS2_OK) return rc;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(HS2_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(HS2_ERR_ALIGN, "lse must be 4-byte aligned");
+  return HS2_OK;
+}
+
+int kv_kind(int dtype) { return dtype == HS2_F32 ? hs2::KV_F32 : (dtype == HS2_BF16 ? hs2::KV_BF16 : hs2::KV_E4M3); }
+
+}  // namespace
+
+extern "C" {
+
+int hs2_version(void) { return 10000; }
+
+const char* hs2_last_error(void) { return g_last_error; }
+
+const char* hs2_status_str(int status) {
+  switch (status) {
+    case HS2_OK: return "HS2_OK";
+    case HS2_ERR_NULL: return "HS2_ERR_NULL: a required pointer is NULL";
+    case HS2_ERR_SHAPE: return "HS2_ERR_SHAPE: size out of range or inconsistent";
+    case HS2_ERR_DTYPE: return "HS2_ERR_DTYPE: unknown or unsupported dtype";
+    case HS2_ERR_UNSUPPORTED: return "HS2_ERR_UNSUPPORTED: configuration not supported";
+    case HS2_ERR_ALIGN: return "HS2_ERR_ALIGN: pointer misaligned";
+    case HS2_ERR_WORKSPACE: return "HS2_ERR_WORKSPACE: workspace missing or too small";
+    case HS2_ERR_HIP: return "HS2_ERR_HIP: HIP launch failed";
+    default: return "unknown hs2 status";
+  }
+}
+
+size_t hs2_full_attn_workspace_bytes(int B, int n_q, int H, int64_t T, int kv_dtype) {
+  if (B < 1 || n_q < 1 || T < 1 || !heads_ok(H)) return 0;
+  return hs2::attn_workspace_bytes(B, n_q, H, T, kv_kind(kv_dtype));
+}
+
+int hs2_full_attn_scored(const void* q, int q_dtype, int B, int n_q, int H, int d, const void* k, const void* v,
+                         int kv_dtype, const float* k_scale, const float* v_scale, int64_t T, int64_t q_pos0,
+                         float sm_scale, void* o, float* lse, float* scores, int64_t ld_scores, void* workspace,
+                         size_t ws_bytes, void* stream) {
+  int rc = check_attn_common(q, q_dtype, B, n_q, H, d, k, v, kv_dtype, k_scale, v_scale, T, sm_scale, o, lse);
+  if (rc != HS2_OK) return rc;
+  if (!scores) return fail(HS2_ERR_NULL, "scores is required");
+  if (!aligned(scores, 16)) return fail(HS2_ERR_ALIGN, "scores must be 16-byte aligned");
+  if (q_pos0 < 0 || q_pos0 + n_q > T) return fail(HS2_ERR_SHAPE, "need 0 <= q_pos0 and q_pos0 + n_q <= T");
+  if (ld_scores < q_pos0 + n_q || ld_scores % 4 != 0)
+    return fail(HS2_ERR_SHAPE, "ld_scores must be >= q_pos0 + n_q and a multiple of 4");
+  const bool decode = hs2::attn_uses_decode(n_q, H);
+  if (kv_dtype == HS2_FP8E4M3 && !decode)
+    return fail(HS2_ERR_UNSUPPORTED, "FP8 caches are supported for n_q * H <= 16 only");
+  const size_t need = hs2::attn_workspace_bytes(B, n_q, H, T, kv_kind(kv_dtype));
+  if (need > 0) {
+    if (!workspace) return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if (!aligned(workspace, 256)) return fail(HS2_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (ws_bytes < need) return fail(HS2_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  }
+  hs2::AttnParams p;
+  p.q = q; p.k = k; p.v = v; p.k_scale = k_scale; p.v_scale = v_scale;
+  p.o = o; p.lse = lse; p.scores = scores; p.ld_scores = ld_scores;
+  p.B = B; p.n_q = n_q; p.H = H; p.T = T; p.q_pos0 = q_pos0;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  return hip_status(hs2::launch_full_attn(p, kv_kind(q_dtype), kv_kind(kv_dtype), workspace, ws_bytes,
+                                          (hipStream_t)stream),
+                    "hs2_full_attn_scored");
+}
+
+size_t hs2_select_workspace_bytes(int B, int n_q, int64_t T, int64_t q_pos0) {
+  return hs2::select_workspace_bytes(B, n_q, T, q_pos0);
+}
+
+int hs2_select_topk_window(const float* scores, int64_t ld_scores, int B, int n_q, int64_t T, int64_t q_pos0,
+                           int window, int topk, int32_t* idx, int32_t* count, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  if (!scores || !idx || !count) return fail(HS2_ERR_NULL, "scores, idx and count are required");
+  if (B < 1 || n_q < 1 || T < 1) return fail(HS2_ERR_SHAPE, "B, n_q and T must be >= 1");
+  if ((int64_t)B * n_q > 0x7FFFFFFF || T > 0x7FFFFFFF) return fail(HS2_ERR_SHAPE, "B*n_q and T must fit in int32");
+  if (window < 1 || topk < 1 || window + topk > HS2_MAX_SELECT)
+    return fail(HS2_ERR_SHAPE, "need window >= 1, topk >= 1, window + topk <= %d", HS2_MAX_SELECT);
+  if (q_pos0 < 0 || q_pos0 + n_q > T) return fail(HS2_ERR_SHAPE, "need 0 <= q_pos0 and q_pos0 + n_q <= T");
+  if (ld_scores < q_pos0 + n_q || ld_scores % 4 != 0)
+    return fail(HS2_ERR_SHAPE, "ld_scores must be >= q_pos0 + n_q and a multiple of 4");
+  if (!aligned(scores, 16)) return fail(HS2_ERR_ALIGN, "scores must be 16-byte aligned");
+  if (!aligned(idx, 4) || !aligned(count, 4)) return fail(HS2_ERR_ALIGN, "idx and count must be 4-byte aligned");
+  const size_t need = hs2::select_workspace_bytes(B, n_q, T, q_pos0);
+  if (need > 0 && (!workspace || ws_bytes < need)) return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+  hs2::SelectParams p;
+  p.scores = scores; p.ld_scores = ld_scores; p.B = B; p.n_q = n_q; p.q_pos0 = q_pos0;
+  p.window = window; p.topk = topk; p.idx = idx; p.count = count;
+  return hip_status(hs2::launch_select(p, workspace, ws_bytes, (hipStream_t)stream), "hs2_select_topk_window");
+}
+
+int hs2_sparse_attn_reuse(const void* q, int q_dtype, int B, int n_q, int H, int d, const void* k, const void* v,
+                          int kv_dtype, const float* k_scale, const float* v_scale, int64_t T, const int32_t* idx,
+                          const int32_t* count, int max_sel, float sm_scale, void* o, float* lse, void* stream) {
+  int rc = check_attn_common(q, q_dtype, B, n_q, H, d, k, v, kv_dtype, k_scale, v_scale, T, sm_scale, o, lse);
+  if (rc != HS2_OK) return rc;
+  if (!idx || !count) return fail(HS2_ERR_NULL, "idx and count are required");
+  if (!aligned(idx, 4) || !aligned(count, 4)) return fail(HS2_ERR_ALIGN, "idx and count must be 4-byte aligned");
+  if (max_sel < 1 || max_sel > HS2_MAX_SELECT) return fail(HS2_ERR_SHAPE, "max_sel must be in [1, %d]", HS2_MAX_SELECT);
+  hs2::SparseParams p;
+  p.q = q; p.k = k; p.v = v; p.k_scale = k_scale; p.v_scale = v_scale;
+  p.idx = idx; p.count = count; p.o = o; p.lse = lse;
+  p.B = B; p.n_q = n_q; p.H = H; p.T = T; p.max_sel = max_sel;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  return hip_status(hs2::launch_sparse_attn(p, kv_kind(q_dtype), kv_kind(kv_dtype), (hipStream_t)stream),
+                    "hs2_sparse_attn_reuse");
+}
+
+size_t hs2_bridge_workspace_bytes(int n_layers, int D, int d) { return hs2::bridge_workspace_bytes(n_layers, D, d); }
+
+int hs2_bridge_kv_proj(const void* x, int64_t L, int D, const void* w_k, const void* w_v, int n_layers, int d,
+                       void* k_out, void* v_out, int64_t out_layer_stride, void* workspace, size_t ws_bytes,
+                       void* stream) {
+  if (!x || !w_k || !w_v || !k_out || !v_out) return fail(HS2_ERR_NULL, "x, w_k, w_v, k_out and v_out are required");
+  if (d != HS2_HEAD_DIM) return fail(HS2_ERR_UNSUPPORTED, "projection width %d unsupported (only %d)", d, HS2_HEAD_DIM);
+  if (L < 1 || D < 32 || D % 32 != 0) return fail(HS2_ERR_SHAPE, "need L >= 1 and D a positive multiple of 32");
+  if (n_layers < 1 || n_layers > 64) return fail(HS2_ERR_SHAPE, "n_layers must be in [1, 64]");
+  if (out_layer_stride < L * (int64_t)d) return fail(HS2_ERR_SHAPE, "out_layer_stride must be >= L * d");
+  if ((L + 255) / 256 * (int64_t)(2 * n_layers) > 0x7FFFFFFF) return fail(HS2_ERR_SHAPE, "L too large");
+  if (!aligned(x, 16) || !aligned(w_k, 16) || !aligned(w_v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16))
+    return fail(HS2_ERR_ALIGN, "x, w_k, w_v, k_out and v_out must be 16-byte aligned");
+  const size_t need = hs2::bridge_workspace_bytes(n_layers, D, d);
+  if (need > 0 && (!workspace || ws_bytes < need)) return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+  hs2::BridgeParams p;
+  p.x = x; p.w_k = w_k; p.w_v = w_v; p.k_out = k_out; p.v_out = v_out;
+  p.L = L; p.D = D; p.n_layers = n_layers; p.out_layer_stride = out_layer_stride;
+  return hip_status(hs2::launch_bridge(p, workspace, ws_bytes, (hipStream_t)stream), "hs2_bridge_kv_proj");
+}
+
+}  // extern "C"

@@ -1,0 +1,292 @@
+// Scored full attention, few-query path (decode: n_q * H <= 16 rows).
+//
+// Same definition as the prefill path (HySparse2 pages, agihunt.info summary:
+// the full layer's exact attention probabilities score the tokens for the
+// sparse layers), computed as a split over keys because one decode row has
+// little work per key and the K/V stream (512 MiB at 1M FP8 tokens) must run
+// at HBM speed:
+//   split   : grid (key chunks, sequences); each workgroup computes the
+//             float32 logits of its keys (kept in the workspace, log2 units),
+//             and a partial softmax state (max, sum, unnormalised O) per row;
+//   combine : one workgroup per (row, sequence) merges the partial states into
+//             O, lse (and lse in log2 units for the next kernel);
+//   score   : one thread per key, s_j = sum_h exp2(x_hj - lse2_h) per query.
+// No atomics: every partial has its own slot, so results are deterministic.
+#include "attn_tile.hpp"
+#include "hs2_internal.hpp"
+
+namespace hs2 {
+namespace {
+
+constexpr int DC_WAVES = 4;
+constexpr int DC_THREADS = DC_WAVES * kWave;
+constexpr int kRedPitch = 260;
+constexpr int kDcSmem = (DC_WAVES * kTileStageBytes > (DC_WAVES * 16 * kRedPitch + 2 * DC_WAVES * 16) * 4)
+                            ? DC_WAVES * kTileStageBytes
+                            : (DC_WAVES * 16 * kRedPitch + 2 * DC_WAVES * 16) * 4;
+
+struct DecodeWs {
+  float* logits;  // [B][T][16]  log2-domain logits of each row
+  float* part_m;  // [B][nch][16]
+  float* part_z;  // [B][nch][16]
+  float* part_o;  // [B][nch][16][256]
+  float* lse2;    // [B][16]
+  int chunk, nch;
+};
+
+int decode_chunk(int B, int64_t T) {
+  const int64_t total = (int64_t)B * T;
+  int ch = 256;
+  while (ch < 4096 && total / ch > 1024) ch *= 2;
+  return ch;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t decode_ws_layout(int B, int64_t T, char* base, DecodeWs* ws) {
+  const int ch = decode_chunk(B, T);
+  const int64_t nch = (T + ch - 1) / ch;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* ptr = base ? base + off : nullptr;
+    off += align256(bytes);
+    return (float*)ptr;
+  };
+  DecodeWs w;
+  w.logits = take((size_t)B * T * 16 * 4);
+  w.part_m = take((size_t)B * nch * 16 * 4);
+  w.part_z = take((size_t)B * nch * 16 * 4);
+  w.part_o = take((size_t)B * nch * 16 * 256 * 4);
+  w.lse2 = take((size_t)B * 16 * 4);
+  w.chunk = ch;
+  w.nch = (int)nch;
+  if (ws) *ws = w;
+  return off;
+}
+
+template <int KV, int H>
+__global__ __launch_bounds__(DC_THREADS) void decode_split_kernel(const AttnParams p, const DecodeWs ws) {
+  constexpr int STEP = TileCfg<KV>::STEP;
+  constexpr int NMT = STEP / 16;
+  constexpr int ROWB = (KV == KV_F32) ? 1024 : (KV == KV_BF16 ? 512 : 256);
+  constexpr int QB = (KV == KV_F32) ? 4 : 2;
+  __shared__ __attribute__((aligned(16))) char smem[kDcSmem];
+
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int g = l >> 4, c16 = l & 15;
+  const int chunk = blockIdx.x, b = blockIdx.y;
+  const int R = p.n_q * H;
+  const bool row_ok = c16 < R;
+  const int64_t row_pos = row_ok ? p.q_pos0 + c16 / H : -1;
+  const int64_t n_keys = p.q_pos0 + p.n_q;
+  const int64_t key0 = (int64_t)chunk * ws.chunk;
+  const int64_t key1 = min(n_keys, key0 + ws.chunk);
+  const int64_t kv_row0 = (int64_t)b * p.T;
+  const char* kseq = (const char*)p.k + kv_row0 * ROWB;
+  const char* vseq = (const char*)p.v + kv_row0 * ROWB;
+  float* lg = ws.logits + kv_row0 * 16;
+  char* stage = smem + wave * kTileStageBytes;
+
+  QFrag qf;
+  load_qfrag<KV>((const char*)p.q + ((int64_t)b * R + c16) * kHeadDim * QB, row_ok, g, qf);
+
+  float m_run = kNegInf, z_run = 0.f;
+  f32x4 oacc[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nst = (int)((key1 - key0 + STEP - 1) / STEP);
+  for (int st = wave; st < nst; st += DC_WAVES) {
+    const int64_t kb = key0 + (int64_t)st * STEP;
+    f32x4 sacc[NMT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const int64_t key = kb + 16 * mt + c16;
+      sacc[mt] = s_tile<KV>(key < key1 ? kseq + key * ROWB : nullptr, g, qf);
+    }
+    stage_v<KV>(stage, l, [&](int slot) -> const char* {
+      const int64_t key = kb + slot;
+      return key < key1 ? vseq + key * ROWB : nullptr;
+    });
+    float x[NMT][4];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t key = kb + 16 * mt + 4 * g + r;
+        float v = sacc[mt][r] * p.scale_log2;
+        if constexpr (KV == KV_E4M3) v *= (key < key1) ? p.k_scale[kv_row0 + key] : 0.f;
+        v = (key < key1 && key <= row_pos) ? v : kNegInf;
+        if (row_ok && key < key1) lg[key * 16 + c16] = v;
+        x[mt][r] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+    float pr[NMT][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = (x[mt][r] == kNegInf) ? 0.f : fast_exp2(x[mt][r] - m_new);
+        psum += e;
+        pr[mt][r] = e;
+        if constexpr (KV == KV_E4M3) {
+          const int64_t key = kb + 16 * mt + 4 * g + r;
+          pr[mt][r] = (key < key1) ? e * p.v_scale[kv_row0 + key] : 0.f;
+        }
+      }
+    z_run = z_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) oacc[t] *= alpha;
+    wave_lds_order();
+    pv_step<KV>(stage, pr, g, c16, oacc);
+    wave_lds_order();
+  }
+
+  // ---- merge the 4 lane groups and 4 waves into this chunk's partial state
+  z_run += shfl_xor(z_run, 16);
+  z_run += shfl_xor(z_run, 32);
+  __syncthreads();
+  float* red_o = (float*)smem;
+  float* red_m = red_o + DC_WAVES * 16 * kRedPitch;
+  float* red_z = red_m + DC_WAVES * 16;
+  if (l < 16) {
+    red_m[wave * 16 + l] = m_run;
+    red_z[wave * 16 + l] = z_run;
+  }
+#pragma unroll
+  for (int t = 0; t < 16; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red_o[(wave * 16 + c16) * kRedPitch + 16 * t + 4 * g + r] = oacc[t][r];
+  __syncthreads();
+  const int64_t pbase = ((int64_t)b * ws.nch + chunk) * 16;
+  for (int e = tid; e < R * kHeadDim; e += DC_THREADS) {
+    const int row = e / kHeadDim, d = e % kHeadDim;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < DC_WAVES; ++w) M = fmaxf(M, red_m[w * 16 + row]);
+    float Z = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < DC_WAVES; ++w) {
+      const float mw = red_m[w * 16 + row];
+      if (mw != kNegInf) {
+        const float f = fast_exp2(mw - M);
+        Z += red_z[w * 16 + row] * f;
+        acc += red_o[(w * 16 + row) * kRedPitch + d] * f;
+      }
+    }
+    ws.part_o[(pbase + row) * kHeadDim + d] = acc;
+    if (d == 0) {
+      ws.part_m[pbase + row] = M;
+      ws.part_z[pbase + row] = Z;
+    }
+  }
+}
+
+template <int QKIND>
+__global__ __launch_bounds__(256) void decode_combine_kernel(const AttnParams p, const DecodeWs ws) {
+  const int row = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int64_t n_keys = p.q_pos0 + p.n_q;
+  const int nch = (int)((n_keys + ws.chunk - 1) / ws.chunk);
+  const int64_t pb = (int64_t)b * ws.nch * 16;
+  float M = kNegInf;
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, ws.part_m[pb + c * 16 + row]);
+  float Z = 0.f, acc = 0.f;
+  for (int c = 0; c < nch; ++c) {
+    const float mc = ws.part_m[pb + c * 16 + row];
+    if (mc != kNegInf) {
+      const float f = fast_exp2(mc - M);
+      Z += ws.part_z[pb + c * 16 + row] * f;
+      acc += ws.part_o[((pb + c * 16 + row)) * kHeadDim + d] * f;
+    }
+  }
+  const int R = gridDim.x;
+  const int64_t oi = ((int64_t)b * R + row) * kHeadDim + d;
+  const float out = acc / Z;
+  if constexpr (QKIND == KV_F32)
+    ((float*)p.o)[oi] = out;
+  else
+    ((bf16*)p.o)[oi] = to_bf16(out);
+  if (d == 0) {
+    const float l2 = M + fast_log2(Z);
+    ws.lse2[b * 16 + row] = l2;
+    if (p.lse) p.lse[(int64_t)b * R + row] = l2 * kLn2;
+  }
+}
+
+template <int H>
+__global__ __launch_bounds__(256) void decode_score_kernel(const AttnParams p, const DecodeWs ws) {
+  const int b = blockIdx.y;
+  const int64_t key = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n_keys = p.q_pos0 + p.n_q;
+  if (key >= n_keys) return;
+  const float* x = ws.logits + ((int64_t)b * p.T + key) * 16;
+  const f32x4 x0 = *(const f32x4*)x, x1 = *(const f32x4*)(x + 4), x2 = *(const f32x4*)(x + 8), x3 = *(const f32x4*)(x + 12);
+  const float xs[16] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3],
+                        x2[0], x2[1], x2[2], x2[3], x3[0], x3[1], x3[2], x3[3]};
+  const float* l2 = ws.lse2 + b * 16;
+  for (int i = 0; i < p.n_q; ++i) {
+    if (key > p.q_pos0 + i) continue;
+    float s = 0.f;
+#pragma unroll
+    for (int h = 0; h < H; ++h) s += fast_exp2(xs[(i * H + h) & 15] - l2[(i * H + h) & 15]);
+    p.scores[((int64_t)b * p.n_q + i) * p.ld_scores + key] = s;
+  }
+}
+
+template <int KV, int H>
+hipError_t launch_decode_h(const AttnParams& p, const DecodeWs& ws, hipStream_t stream) {
+  const int64_t n_keys = p.q_pos0 + p.n_q;
+  const unsigned nch = (unsigned)((n_keys + ws.chunk - 1) / ws.chunk);
+  hipLaunchKernelGGL((decode_split_kernel<KV, H>), dim3(nch, p.B), dim3(DC_THREADS), 0, stream, p, ws);
+  const int R = p.n_q * p.H;
+  if (KV == KV_F32)
+    hipLaunchKernelGGL((decode_combine_kernel<KV_F32>), dim3(R, p.B), dim3(256), 0, stream, p, ws);
+  else
+    hipLaunchKernelGGL((decode_combine_kernel<KV_BF16>), dim3(R, p.B), dim3(256), 0, stream, p, ws);
+  hipLaunchKernelGGL((decode_score_kernel<H>), dim3((unsigned)((n_keys + 255) / 256), p.B), dim3(256), 0, stream, p, ws);
+  return hipGetLastError();
+}
+
+template <int KV>
+hipError_t launch_decode_kv(const AttnParams& p, const DecodeWs& ws, hipStream_t stream) {
+  switch (p.H) {
+    case 1: return launch_decode_h<KV, 1>(p, ws, stream);
+    case 2: return launch_decode_h<KV, 2>(p, ws, stream);
+    case 4: return launch_decode_h<KV, 4>(p, ws, stream);
+    case 8: return launch_decode_h<KV, 8>(p, ws, stream);
+    default: return launch_decode_h<KV, 16>(p, ws, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const AttnParams& p, int kv_kind, hipStream_t stream);  // attn_prefill.hip
+
+bool attn_uses_decode(int n_q, int H) { return n_q * H <= 16; }
+
+size_t attn_workspace_bytes(int B, int n_q, int H, int64_t T, int /*kv_kind*/) {
+  if (!attn_uses_decode(n_q, H)) return 0;
+  return decode_ws_layout(B, T, nullptr, nullptr);
+}
+
+hipError_t launch_full_attn(const AttnParams& p, int /*q_kind*/, int kv_kind, void* ws_ptr, size_t /*ws_bytes*/,
+                            hipStream_t stream) {
+  if (p.B * p.n_q == 0) return hipSuccess;
+  if (!attn_uses_decode(p.n_q, p.H)) return launch_prefill(p, kv_kind, stream);
+  DecodeWs ws;
+  decode_ws_layout(p.B, p.T, (char*)ws_ptr, &ws);
+  switch (kv_kind) {
+    case KV_F32: return launch_decode_kv<KV_F32>(p, ws, stream);
+    case KV_BF16: return launch_decode_kv<KV_BF16>(p, ws, stream);
+    default: return launch_decode_kv<KV_E4M3>(p, ws, stream);
+  }
+}
+
+}  // namespace hs2

@@ -1,0 +1,77 @@
+// Host-side declarations shared between the C-ABI layer (api.cpp) and the
+// kernel translation units.  Each launcher enqueues its kernels on `stream`
+// and returns the hipError_t of the launch; all arguments have already been
+// validated by api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hs2 {
+
+// storage kinds of K/V (and of Q/O: KV_F32 or KV_BF16)
+enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_E4M3 = 2 };
+
+struct SparseParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* idx;
+  const int32_t* count;
+  void* o;
+  float* lse;
+  int B, n_q, H;
+  int64_t T;
+  int max_sel;
+  float scale_log2;  // sm_scale * log2(e)
+};
+hipError_t launch_sparse_attn(const SparseParams& p, int q_kind, int kv_kind, hipStream_t stream);
+
+struct SelectParams {
+  const float* scores;
+  int64_t ld_scores;
+  int B, n_q;
+  int64_t q_pos0;
+  int window, topk;
+  int32_t* idx;
+  int32_t* count;
+};
+size_t select_workspace_bytes(int B, int n_q, int64_t T, int64_t q_pos0);
+hipError_t launch_select(const SelectParams& p, void* ws, size_t ws_bytes, hipStream_t stream);
+
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* k_scale;
+  const float* v_scale;
+  void* o;
+  float* lse;
+  float* scores;
+  int64_t ld_scores;
+  int B, n_q, H;
+  int64_t T, q_pos0;
+  float scale_log2;
+};
+bool attn_uses_decode(int n_q, int H);
+size_t attn_workspace_bytes(int B, int n_q, int H, int64_t T, int kv_kind);
+hipError_t launch_full_attn(const AttnParams& p, int q_kind, int kv_kind, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+struct BridgeParams {
+  const void* x;
+  const void* w_k;
+  const void* w_v;
+  void* k_out;
+  void* v_out;
+  int64_t L;
+  int D, n_layers;
+  int64_t out_layer_stride;
+};
+size_t bridge_workspace_bytes(int n_layers, int D, int d);
+hipError_t launch_bridge(const BridgeParams& p, void* ws, size_t ws_bytes, hipStream_t stream);
+
+}  // namespace hs2
