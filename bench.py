@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the HySparse2 inner-level attention hot path on one MI355X.
+
+Workload (default): the 128k-token long prefill -- 1 sequence, L = T = 131072,
+16 query heads over one shared K/V head (MQA), head dim 256, bf16, causal,
+inputs N(0,1)/16 with 64 planted needle keys.  One step is the whole path on
+that batch:
+  scored full attention (queries processed in chunks; each chunk writes its
+  float32 score rows) -> token top-k with the forced 128-token window (1024
+  picks per query) -> 2 sparse layers reusing the indices (own queries each).
+
+Printed: one JSON line with the whole-step prefill rate (tokens/s), the
+roofline of the dominant kernel (the MFMA-bound full-attention kernel), the
+stage breakdown, and the float64 CPU oracle timed on a bounded sample of the
+same workload (rows of the same sequence, incl. the needle targets), whose
+outputs are also compared with the GPU's for those rows.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk C]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+D = 256
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--chunk", type=int, default=32768, help="queries per full-attention call")
+    ap.add_argument("--workload", default="prefill_128k")
+    ap.add_argument("--cpu-rows", type=int, default=74, help="oracle sample size (rows)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from token_level_sparse_full_amd import hs2, inputs
+
+    wl = inputs.WORKLOADS[args.workload]
+    assert wl.kind == "prefill" and wl.kv == "bf16"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L, H, n_sparse = wl.L, wl.H, wl.n_sparse
+    scale = 1.0 / math.sqrt(D)
+    window, topk = 128, 1024
+    max_sel = window + topk
+
+    # ---------------------------------------------------------------- inputs (resident in HBM)
+    inp = inputs.attention_inputs(B=1, n_q=L, T=L, H=H, d=D, kv=wl.kv, n_sparse=n_sparse, seed=wl.seed, device=dev)
+    needles = inputs.plant_needles(inp["q"][0], inp["k"][0], wl.needles, wl.seed) if wl.needles else []
+    q, k, v, qs = inp["q"], inp["k"], inp["v"], inp["q_sparse"]
+    C = min(args.chunk, L)
+    chunks = [(c0, min(L, c0 + C)) for c0 in range(0, L, C)]
+    ld = (L + 3) // 4 * 4
+    scores = torch.empty((1, C, ld), dtype=torch.float32, device=dev)
+    idx = torch.empty((1, L, max_sel), dtype=torch.int32, device=dev)
+    cnt = torch.empty((1, L), dtype=torch.int32, device=dev)
+    o_full = torch.empty_like(q)
+    lse_full = torch.empty((1, L, H), dtype=torch.float32, device=dev)
+    o_sp = [torch.empty_like(q) for _ in range(n_sparse)]
+    lse_sp = [torch.empty((1, L, H), dtype=torch.float32, device=dev) for _ in range(n_sparse)]
+    torch.cuda.synchronize()
+
+    n_ev = len(chunks) * 2 + n_sparse + 1
+    keep_rows = {}
+
+    def step(events=None, sample_rows=None):
+        ev = iter(events) if events else None
+        mark = (lambda: next(ev).record()) if ev else (lambda: None)
+        mark()
+        for c0, c1 in chunks:
+            hs2.hs2_full_attn_scored(q[:, c0:c1], k, v, q_pos0=c0, sm_scale=scale, o=o_full[:, c0:c1],
+                                     lse=lse_full[:, c0:c1], scores=scores[:, : c1 - c0], ld_scores=ld)
+            mark()
+            if sample_rows:
+                for p in sample_rows:
+                    if c0 <= p < c1:
+                        keep_rows[p] = scores[0, p - c0, : p + 1].clone()
+            hs2.hs2_select_topk_window(scores[:, : c1 - c0], q_pos0=c0, T=L, n_q=c1 - c0, window=window, topk=topk,
+                                       idx=idx[:, c0:c1], count=cnt[:, c0:c1])
+            mark()
+        for s in range(n_sparse):
+            hs2.hs2_sparse_attn_reuse(qs[s], k, v, idx, cnt, sm_scale=scale, o=o_sp[s], lse=lse_sp[s])
+            mark()
+
+    # ---------------------------------------------------------------- warmup + timed steps
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total, ms_fa, ms_sel, ms_sp = [], [], [], []
+    for e in evs:
+        ms_total.append(e[0].elapsed_time(e[-1]))
+        j = 0
+        fa = sel = 0.0
+        for _ in chunks:
+            fa += e[j].elapsed_time(e[j + 1])
+            sel += e[j + 1].elapsed_time(e[j + 2])
+            j += 2
+        ms_fa.append(fa)
+        ms_sel.append(sel)
+        ms_sp.append([e[j + i].elapsed_time(e[j + i + 1]) for i in range(n_sparse)])
+    ms_step = float(np.mean(ms_total))
+    fa_ms = float(np.mean(ms_fa))
+    sel_ms = float(np.mean(ms_sel))
+    sp_ms = float(np.mean([np.mean(x) for x in ms_sp]))
+
+    # ---------------------------------------------------------------- algorithmic work
+    npos = np.arange(L, dtype=np.float64) + 1.0                     # keys seen by each query
+    fa_flop = 4.0 * H * D * npos.sum()                               # QK^T + PV, causal
+    fa_tflops = fa_flop / (fa_ms * 1e-3) / 1e12
+    counts = np.minimum(npos, max_sel)
+    sp_bytes = counts.sum() * 2 * D * 2 + L * (2 * H * D * 2 + max_sel * 4 + 4 + H * 4)
+    sp_gbs = sp_bytes / (sp_ms * 1e-3) / 1e9
+    cand = np.maximum(npos - window, 0)
+    sel_bytes = np.where(cand > topk, cand, 0).sum() * 4 + L * max_sel * 4
+    sel_gbs = sel_bytes / (sel_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "sparse-reuse attn queries/s at 128k ctx + prefill tokens/s; % HBM/MFMA peak",
+        "value": L / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/16 Q/K/V, 64 planted needle keys)",
+        "config": {"workload": "prefill_128k", "seq_len": L, "query_heads": H, "kv_heads": 1, "head_dim": D,
+                   "window": window, "topk": topk, "sparse_layers": n_sparse, "query_chunk": C,
+                   "global_batch": 1, "parallelism": "single GPU"},
+        "roofline": {"kernel": "prefill_kernel (scored full attention)", "bound": "mfma",
+                     "achieved": fa_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": fa_tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                     "algorithmic_flop_per_step": fa_flop, "launches_per_step": len(chunks)},
+        "stages": {
+            "full_attn_ms": fa_ms, "select_ms": sel_ms, "sparse_ms_per_layer": sp_ms,
+            "sparse_reuse_queries_per_s": L / (sp_ms * 1e-3),
+            "sparse_reuse_gbs_algorithmic": sp_gbs, "sparse_reuse_hbm_frac": sp_gbs / HBM_PEAK_GBS,
+            "select_gbs_algorithmic": sel_gbs,
+            "wall_s_timed": wall,
+        },
+    }
+
+    # ---------------------------------------------------------------- oracle sample (host cores)
+    if not args.no_cpu:
+        result["cpu_baseline"], result["sample_parity"] = cpu_baseline(
+            args, inp, needles, step, keep_rows, idx, cnt, o_full, o_sp, L, H, scale, window, topk)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, inp, needles, step, keep_rows, idx, cnt, o_full, o_sp, L, H, scale, window, topk):
+    """Time the float64 oracle on sampled query rows of the same sequence and
+    compare the GPU results of those rows with it."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from token_level_sparse_full_amd import inputs
+
+    edge = [0, 1, 127, 128, 129, 1151, 1152, 1153, L // 2, L - 1]
+    rows = sorted(set(edge + [i for _, i in needles]))[: max(args.cpu_rows, len(edge))]
+    # one more pass that also keeps the score rows of the sampled queries
+    step(sample_rows=rows)
+    torch.cuda.synchronize()
+    k64 = oracle.decode_rows(inputs.raw_numpy(inp["k"][0]), "bf16")
+    v64 = oracle.decode_rows(inputs.raw_numpy(inp["v"][0]), "bf16")
+    q_np = inputs.raw_numpy(inp["q"][0])
+    qs_np = [inputs.raw_numpy(t[0]) for t in inp["q_sparse"]]
+    idx_np, cnt_np = idx[0].cpu().numpy(), cnt[0].cpu().numpy()
+    o_np = o_full[0].float().cpu().numpy()
+    osp_np = [t[0].float().cpu().numpy() for t in o_sp]
+    worst = {"full_o": 0.0, "scores_rel": 0.0, "sparse_o": 0.0, "sel_swaps": 0, "needles_found": 0}
+    t0 = time.perf_counter()
+    for p in rows:
+        qrow = oracle.decode_rows(q_np[p:p + 1], "bf16")
+        o_ref, _, s_ref = oracle.full_attn_scored(qrow, k64, v64, p, scale)
+        sel, n, tau = oracle.select_topk_window(s_ref[0], p, window, topk)
+        o2_refs = [oracle.sparse_attn_reuse(oracle.decode_rows(qs_np[s][p], "bf16"), k64, v64, sel, scale)[0]
+                   for s in range(len(qs_np))]
+        # comparisons (not part of the timed oracle work: cheap)
+        worst["full_o"] = max(worst["full_o"], float(np.abs(o_np[p] - o_ref[0]).max()))
+        g = keep_rows[p].cpu().numpy().astype(np.float64)
+        worst["scores_rel"] = max(worst["scores_rel"], float((np.abs(g - s_ref[0]) / s_ref[0]).max()))
+        got = idx_np[p, : cnt_np[p]]
+        diff = np.setxor1d(got, sel)
+        if tau is not None and diff.size:
+            assert (np.abs(s_ref[0][diff] - tau) <= 1e-5 * tau).all(), f"selection outside tolerance at row {p}"
+        worst["sel_swaps"] += int(diff.size)
+        # the sparse layers are compared on the GPU's own index set (stage-wise inputs)
+        for s in range(len(qs_np)):
+            o2_on_gpu_set, _ = oracle.sparse_attn_reuse(oracle.decode_rows(qs_np[s][p], "bf16"), k64, v64, got, scale)
+            worst["sparse_o"] = max(worst["sparse_o"], float(np.abs(osp_np[s][p] - o2_on_gpu_set).max()))
+        del o2_refs
+    t_cpu = time.perf_counter() - t0
+    for j, i in needles:
+        worst["needles_found"] += int(np.isin(j, idx_np[i, : cnt_np[i]]))
+    worst["needles"] = len(needles)
+    worst["rows"] = len(rows)
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = 1
+    cores = min(len(os.sched_getaffinity(0)), blas_threads)
+    base = {"value": len(rows) / t_cpu, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(rows)} query rows of the same 128k sequence (64 needle targets + edge positions), "
+                      f"each through full attention + select + {len(qs_np)} sparse layers in float64",
+            "seconds": t_cpu}
+    return base, worst
+
+
+if __name__ == "__main__":
+    main()
