@@ -371,9 +371,11 @@ hipError_t launch_prefill_kv(const AttnParams& p, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t stream);  // attn_prefill_bf16.hip
+
 hipError_t launch_prefill(const AttnParams& p, int kv_kind, hipStream_t stream) {
   if (p.B * p.n_q == 0) return hipSuccess;
-  return kv_kind == KV_F32 ? launch_prefill_kv<KV_F32>(p, stream) : launch_prefill_kv<KV_BF16>(p, stream);
+  return kv_kind == KV_F32 ? launch_prefill_kv<KV_F32>(p, stream) : launch_prefill_bf16(p, stream);
 }
 
 }  // namespace hs2

@@ -1,0 +1,383 @@
+// Scored full attention, many-query path, bf16 caches.
+//
+// Same definition and the same two sweeps as attn_prefill.hip (HySparse2
+// pages, agihunt.info summary: the full layer's exact attention probabilities
+// score the tokens for the sparse layers; per head P_hj = exp(l_hj - lse_h),
+// score_j = sum_h P_hj), laid out for MI355X's LDS bandwidth:
+//
+//  * 64 query rows per wave (64/H tokens x H heads), 4 waves = 256 rows per
+//    workgroup.  Every K or V fragment read from LDS feeds two 32-row MFMA
+//    tiles, which halves the LDS bytes per MFMA flop against 32-row waves;
+//    the 64 x 256 float32 O accumulator of a wave lives in the AGPR file.
+//  * K/V tiles of 32 keys are double-buffered in LDS and filled with
+//    global_load_lds_dwordx4 (no register staging): the DMA of tile t+1 runs
+//    while tile t is computed, one barrier per tile.  Lanes fetch permuted
+//    16-byte chunks so that the LDS image is XOR-swizzled (K: chunk ^ (key &
+//    15), V: chunk ^ 2 (key & 3)), which keeps the MFMA operand reads and the
+//    ds_read_b64_tr_b16 reads free of bank conflicts.
+//  * sweep 1: S^T = K Q^T (a lane owns a row, online max/sum in registers);
+//    sweep 2: S = Q K^T (a lane owns a key: float32 P, in-lane head sums for
+//    the scores), P -> LDS [key][row] -> transposed reads -> O += P V.
+#include "hs2_device.hpp"
+#include "hs2_internal.hpp"
+
+namespace hs2 {
+namespace {
+
+constexpr int PB_WAVES = 4;
+constexpr int PB_THREADS = PB_WAVES * kWave;
+constexpr int PB_KT = 32;                       // keys per tile
+constexpr int PB_RW = 64;                       // rows per wave
+// LDS rows are padded rather than swizzled, so that every operand read of a
+// lane is one base register plus an immediate offset:
+//   K rows: 33 chunks of 16 B (528 B): 16 consecutive rows read at the same
+//           chunk hit 16 distinct 4-bank groups;
+//   V rows: 34 chunks (544 B): the 4 rows x 32 B of one transposed read hit
+//           32 distinct banks.
+constexpr int PB_KC = 33, PB_VC = 34;           // chunks per padded K / V row
+constexpr int PB_KTILE = 17 * 1024;             // 32 x 33 chunks (16.5 KB) rounded to 17 DMA instructions
+constexpr int PB_VTILE = 17 * 1024;             // 32 x 34 chunks = 17 DMA instructions
+constexpr int PB_PP = 144;                      // P buffer pitch (bytes per key)
+constexpr int PB_SMEM = 2 * PB_KTILE + 2 * PB_VTILE + PB_WAVES * PB_KT * PB_PP + PB_WAVES * PB_RW * 4;
+
+template <int H>
+__global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnParams p) {
+  constexpr int TPW = PB_RW / H;       // tokens per wave
+  constexpr int TPB = PB_WAVES * TPW;  // tokens per workgroup
+  __shared__ __attribute__((aligned(1024))) char smem[PB_SMEM];
+
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int hb = l >> 5, l32 = l & 31;
+  const int G = l >> 4, s16 = l & 15;
+
+  const int nblk_tok = (p.n_q + TPB - 1) / TPB;
+  const int b = blockIdx.x / nblk_tok;
+  const int tb = nblk_tok - 1 - (blockIdx.x % nblk_tok);  // latest (heaviest) token blocks first
+  const int tok_blk0 = tb * TPB;
+  const int tok_w0 = tok_blk0 + wave * TPW;
+  const int n_valid_blk = min(TPB, p.n_q - tok_blk0);
+  const int64_t pos_first = p.q_pos0 + tok_blk0;
+  const int64_t n_keys = pos_first + n_valid_blk;
+  const int ntiles = (int)((n_keys + PB_KT - 1) / PB_KT);
+  const char* kg = (const char*)p.k + (int64_t)b * p.T * 512;
+  const char* vg = (const char*)p.v + (int64_t)b * p.T * 512;
+  auto kbuf = [&](int i) { return smem + i * PB_KTILE; };
+  auto vbuf = [&](int i) { return smem + 2 * PB_KTILE + i * PB_VTILE; };
+  auto pbuf = [&](int i) { return smem + 2 * PB_KTILE + 2 * PB_VTILE + (wave + i) * PB_KT * PB_PP; };
+  float* lse_lds = (float*)(smem + 2 * PB_KTILE + 2 * PB_VTILE + PB_WAVES * PB_KT * PB_PP) + wave * PB_RW;
+
+  auto tok_of_row = [&](int row) { return tok_w0 + row / H; };
+  auto pos_of_row = [&](int row) -> int64_t {
+    const int t = tok_of_row(row);
+    return p.q_pos0 + (t < p.n_q ? t : p.n_q - 1);
+  };
+
+  // ---- queries: rows 32*mt + l32 of this wave, K-step s covers dims 16s..16s+15
+  const int64_t q_row0 = ((int64_t)b * p.n_q + tok_w0) * H;
+  bf16x8 qf[2][16];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const bool ok = tok_of_row(32 * mt + l32) < p.n_q;
+    const bf16* qp = (const bf16*)p.q + (q_row0 + 32 * mt + l32) * kHeadDim + 8 * hb;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) qf[mt][s] = ok ? as_bf16x8(*(const u32x4*)(qp + 16 * s)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  }
+
+  // ---- LDS DMA of one 32-key tile into its padded image: the image is cut into
+  // 17 wave-instructions of 64 x 16 B (lane l of instruction i fills chunk
+  // 64 i + l); instructions are dealt round-robin to the waves.  Pad chunks
+  // and the slack after the last row load a valid row and are never read.
+  auto dma = [&](const char* g, int kt, char* buf, int pc) {
+    for (int ins = wave; ins < 17; ins += PB_WAVES) {
+      const int c = 64 * ins + l;
+      const int row = c / pc, ch = c - row * pc;
+      int64_t key = (int64_t)kt * PB_KT + (row < PB_KT ? row : PB_KT - 1);
+      key = key < n_keys ? key : n_keys - 1;   // rows past the last key: any valid row (masked later)
+      const int chv = ch < 32 ? ch : 0;
+      __builtin_amdgcn_global_load_lds((const void*)(g + key * 512 + chv * 16),
+                                       (void HS2_LDS*)(buf + ins * 1024), 16, 0, 0);
+    }
+  };
+  auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+  // K fragment for K-step s: key l32 of the tile, dims 16s + 8hb .. +7
+  const int kofs = l32 * (PB_KC * 16) + 16 * hb;
+  auto kfrag = [&](const char* buf, int s) -> bf16x8 { return as_bf16x8(*(const u32x4*)(buf + kofs + 32 * s)); };
+
+  // Both sweeps are software-pipelined one tile deep: while the VALU works on
+  // the logits of tile t (exp2, max/sum or probabilities, scores, P -> LDS),
+  // the MFMA unit already computes the logits of tile t+1.  K therefore runs
+  // one tile ahead of V; with double buffers the DMA of K(t+2) and V(t+1) is
+  // issued right after the barrier of iteration t.  The logits of the tile
+  // after the last are computed from a stale buffer and never used, which
+  // keeps the loop body straight-line.
+  struct Pair {
+    f32x16 v[2];
+  };
+  auto s_keys_rows = [&](const char* kb) {   // S^T: lane = row l32 (+32), regs = keys
+    Pair st = {{f32x16{}, f32x16{}}};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const bf16x8 kf = kfrag(kb, s);
+      st.v[0] = mfma32(kf, qf[0][s], st.v[0]);
+      st.v[1] = mfma32(kf, qf[1][s], st.v[1]);
+    }
+    return st;
+  };
+
+  // =============================== sweep 1: lse per row ===============================
+  float m_run[2] = {kNegInf, kNegInf}, z_run[2] = {0.f, 0.f};
+  const int my_pos[2] = {(int)pos_of_row(l32), (int)pos_of_row(32 + l32)};
+  dma(kg, 0, kbuf(0), PB_KC);
+  wait_dma();
+  __syncthreads();
+  if (ntiles > 1) dma(kg, 1, kbuf(1), PB_KC);
+  f32x16 st_cur[2];
+  {
+    auto t = s_keys_rows(kbuf(0));
+    st_cur[0] = t.v[0];
+    st_cur[1] = t.v[1];
+  }
+  // Online max / sum of one tile (lane: rows l32 and 32 + l32, keys kt*32 +
+  // 8(r/4) + 4hb + r%4).  Tiles left of the diagonal need no causal mask:
+  // that path is the bulk of the work, so it is kept free of selects.
+  auto lse_update = [&](Pair& st, int kt, bool masked) {
+    const int kbase = kt * PB_KT;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      if (!masked) {
+        float tmax = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st.v[n][r]);
+        const float m_new = fmaxf(m_run[n], tmax * p.scale_log2);  // scale > 0: max commutes
+        float acc = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc += fast_exp2(st.v[n][r] * p.scale_log2 - m_new);
+        z_run[n] = z_run[n] * fast_exp2(m_run[n] - m_new) + acc;  // exp2(-inf) = 0 on the first tile
+        m_run[n] = m_new;
+      } else {
+        float tmax = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = st.v[n][r] * p.scale_log2;
+          x = (kbase + 8 * (r >> 2) + 4 * hb + (r & 3) <= my_pos[n]) ? x : kNegInf;
+          st.v[n][r] = x;
+          tmax = fmaxf(tmax, x);
+        }
+        const float m_new = fmaxf(m_run[n], tmax);
+        const float m_use = m_new == kNegInf ? 0.f : m_new;  // all masked so far: every term is 0
+        float acc = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc += fast_exp2(st.v[n][r] - m_use);
+        z_run[n] = z_run[n] * fast_exp2(m_run[n] - m_use) + acc;
+        m_run[n] = m_new;
+      }
+    }
+  };
+  Pair st_c = {{st_cur[0], st_cur[1]}};
+  for (int kt = 0; kt < ntiles; ++kt) {
+    wait_dma();
+    __syncthreads();
+    if (kt + 2 < ntiles) dma(kg, kt + 2, kbuf(kt & 1), PB_KC);
+    // the next tile's logits go to the MFMA unit while this tile's max / sum run
+    // on the VALU; both branches carry the MFMAs so that they interleave
+    const bool need_mask = (int64_t)kt * PB_KT + PB_KT - 1 > pos_first;
+    Pair st_n;
+    if (!need_mask) {
+      st_n = s_keys_rows(kbuf((kt + 1) & 1));
+      lse_update(st_c, kt, false);
+      // issue order: MFMA, K-fragment read, VALU, MFMA, VALU, ... so that the
+      // matrix unit never waits for the softmax arithmetic of the other tile
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+    } else {
+      st_n = s_keys_rows(kbuf((kt + 1) & 1));
+      lse_update(st_c, kt, true);
+    }
+    st_c = st_n;
+  }
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const float mo = shfl_xor(m_run[n], 32), zo = shfl_xor(z_run[n], 32);
+    const float m = fmaxf(m_run[n], mo);
+    const float z = (m_run[n] == kNegInf ? 0.f : z_run[n] * fast_exp2(m_run[n] - m)) +
+                    (mo == kNegInf ? 0.f : zo * fast_exp2(mo - m));
+    if (hb == 0) lse_lds[32 * n + l32] = m + fast_log2(z);
+  }
+  __syncthreads();
+
+  // =============================== sweep 2: P, scores, O ===============================
+  f32x16 oacc[2][8];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int n = 0; n < 8; ++n) oacc[mt][n] = f32x16{};
+  float* srow_base = p.scores + (int64_t)b * p.n_q * p.ld_scores;
+  auto s_rows_keys = [&](const char* kb) {   // S: lane = key l32, regs = rows
+    Pair sa = {{f32x16{}, f32x16{}}};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const bf16x8 kf = kfrag(kb, s);
+      sa.v[0] = mfma32(qf[0][s], kf, sa.v[0]);
+      sa.v[1] = mfma32(qf[1][s], kf, sa.v[1]);
+    }
+    return sa;
+  };
+
+  // probabilities of tile kt (lane: key kbase + l32, rows 32mt + 8(r/4) + 4hb + r%4),
+  // the score of each token of the lane's key, and P (bf16) -> LDS [key][row]
+  auto probs = [&](Pair& sa, int kt, char* pb, float (&sc)[2][2]) {
+    const int64_t kbase = (int64_t)kt * PB_KT;
+    const int64_t key = kbase + l32;
+    const bool need_mask = kbase + PB_KT - 1 > pos_first;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 l4 = *(const f32x4*)(lse_lds + 32 * mt + 8 * q + 4 * hb);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * q + j;
+          const float e = fast_exp2(sa.v[mt][r] * p.scale_log2 - l4[j]);
+          if (need_mask)
+            sa.v[mt][r] = key <= pos_of_row(32 * mt + 8 * q + 4 * hb + j) ? e : 0.f;
+          else
+            sa.v[mt][r] = e;
+        }
+      }
+      if constexpr (H == 16) {
+        float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          t0 += sa.v[mt][r];
+          t1 += sa.v[mt][8 + r];
+        }
+        sc[mt][0] = halfwave_pair_sum(t0, t1);
+      } else if constexpr (H == 8) {
+        float t[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) t[q] = sa.v[mt][4 * q] + sa.v[mt][4 * q + 1] + sa.v[mt][4 * q + 2] + sa.v[mt][4 * q + 3];
+        sc[mt][0] = halfwave_pair_sum(t[0], t[1]);
+        sc[mt][1] = halfwave_pair_sum(t[2], t[3]);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 v4;
+        v4[0] = to_bf16(sa.v[mt][4 * q]);
+        v4[1] = to_bf16(sa.v[mt][4 * q + 1]);
+        v4[2] = to_bf16(sa.v[mt][4 * q + 2]);
+        v4[3] = to_bf16(sa.v[mt][4 * q + 3]);
+        *(bf16x4*)(pb + l32 * PB_PP + (32 * mt + 8 * q + 4 * hb) * 2) = v4;
+      }
+    }
+  };
+  // scores of tile kt to global memory (token sums of 32/H tokens per 32-row tile)
+  auto store_scores = [&](const Pair& sa, int kt, const float (&sc)[2][2]) {
+    const int64_t key = (int64_t)kt * PB_KT + l32;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      auto put = [&](int row_in_tile0, float val) {
+        const int tok = tok_of_row(32 * mt + row_in_tile0);
+        if (tok < p.n_q && key <= p.q_pos0 + tok) srow_base[(int64_t)tok * p.ld_scores + key] = val;
+      };
+      if constexpr (H == 16) {
+        put(16 * hb, sc[mt][0]);
+      } else if constexpr (H == 8) {
+        put(8 * hb, sc[mt][0]);
+        put(16 + 8 * hb, sc[mt][1]);
+      } else if constexpr (H == 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          put(8 * q + 4 * hb, sa.v[mt][4 * q] + sa.v[mt][4 * q + 1] + sa.v[mt][4 * q + 2] + sa.v[mt][4 * q + 3]);
+      } else if constexpr (H == 2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+            put(8 * q + 4 * hb + 2 * jj, sa.v[mt][4 * q + 2 * jj] + sa.v[mt][4 * q + 2 * jj + 1]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) put(8 * (r >> 2) + 4 * hb + (r & 3), sa.v[mt][r]);
+      }
+    }
+  };
+  // O += P V for one tile (A = P rows x keys, B = V keys x dims, both via transposed reads)
+  auto pv = [&](const char* pb, const char* vb) {
+#pragma unroll
+    for (int ks = 0; ks < PB_KT / 16; ++ks) {
+      const int krow = 16 * ks + 8 * (G >> 1) + (s16 >> 2);
+      const int off = 16 * (G & 1) + 4 * (s16 & 3);
+      bf16x8 a[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16* pa = (const bf16*)(pb + krow * PB_PP) + 32 * mt + off;
+        a[mt] = cat8(lds_tr16(pa), lds_tr16(pa + 4 * (PB_PP / 2)));
+      }
+      const bf16* vrow = (const bf16*)(vb + krow * (PB_VC * 16)) + off;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const bf16x8 bv = cat8(lds_tr16(vrow + 32 * n), lds_tr16(vrow + 4 * (PB_VC * 8) + 32 * n));
+        oacc[0][n] = mfma32(a[0], bv, oacc[0][n]);
+        oacc[1][n] = mfma32(a[1], bv, oacc[1][n]);
+      }
+    }
+  };
+
+  // Sweep 2: per tile, S -> P (float32 -> scores, bf16 -> LDS) -> O += P V.
+  // K and V of the next tile are fetched while this one is computed.
+  dma(kg, 0, kbuf(0), PB_KC);
+  dma(vg, 0, vbuf(0), PB_VC);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    wait_dma();
+    __syncthreads();
+    if (kt + 1 < ntiles) {
+      dma(kg, kt + 1, kbuf((kt + 1) & 1), PB_KC);
+      dma(vg, kt + 1, vbuf((kt + 1) & 1), PB_VC);
+    }
+    Pair sa = s_rows_keys(kbuf(kt & 1));
+    float sc[2][2];
+    probs(sa, kt, pbuf(0), sc);
+    store_scores(sa, kt, sc);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    pv(pbuf(0), vbuf(kt & 1));
+  }
+
+  // ---- outputs: lane holds O[32mt + 8(r/4) + 4hb + r%4][32n + l32]
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 32 * mt + 8 * (r >> 2) + 4 * hb + (r & 3);
+      if (tok_of_row(row) >= p.n_q) continue;
+      bf16* orow = (bf16*)p.o + (q_row0 + row) * kHeadDim;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) orow[32 * n + l32] = to_bf16(oacc[mt][n][r]);
+    }
+  if (p.lse && hb == 0) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+      if (tok_of_row(32 * n + l32) < p.n_q) p.lse[q_row0 + 32 * n + l32] = lse_lds[32 * n + l32] * kLn2;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t stream) {
+  const int tpb = PB_WAVES * PB_RW / p.H;
+  const unsigned nblk = (unsigned)(p.B * ((p.n_q + tpb - 1) / tpb));
+  switch (p.H) {
+    case 1: hipLaunchKernelGGL(prefill_bf16_kernel<1>, dim3(nblk), dim3(PB_THREADS), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL(prefill_bf16_kernel<2>, dim3(nblk), dim3(PB_THREADS), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL(prefill_bf16_kernel<4>, dim3(nblk), dim3(PB_THREADS), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL(prefill_bf16_kernel<8>, dim3(nblk), dim3(PB_THREADS), 0, stream, p); break;
+    default: hipLaunchKernelGGL(prefill_bf16_kernel<16>, dim3(nblk), dim3(PB_THREADS), 0, stream, p); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hs2
