@@ -85,17 +85,32 @@ __global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnP
 
   // ---- LDS DMA of one 32-key tile into its padded image: the image is cut into
   // 17 wave-instructions of 64 x 16 B (lane l of instruction i fills chunk
-  // 64 i + l); instructions are dealt round-robin to the waves.  Pad chunks
-  // and the slack after the last row load a valid row and are never read.
-  auto dma = [&](const char* g, int kt, char* buf, int pc) {
-    for (int ins = wave; ins < 17; ins += PB_WAVES) {
-      const int c = 64 * ins + l;
-      const int row = c / pc, ch = c - row * pc;
-      int64_t key = (int64_t)kt * PB_KT + (row < PB_KT ? row : PB_KT - 1);
-      key = key < n_keys ? key : n_keys - 1;   // rows past the last key: any valid row (masked later)
-      const int chv = ch < 32 ? ch : 0;
-      __builtin_amdgcn_global_load_lds((const void*)(g + key * 512 + chv * 16),
-                                       (void HS2_LDS*)(buf + ins * 1024), 16, 0, 0);
+  // 64 i + l); instruction i is issued by wave i % 4.  Pad chunks and the slack
+  // after the last row load a valid row and are never read.  The per-lane
+  // source offsets inside a tile are loop invariant; a tile that ends past the
+  // last key clamps its rows to that key (masked later).
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t koff[5], voff[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int c = 64 * (wv + 4 * i) + l;
+    const int kr = c / PB_KC, kc = c - kr * PB_KC;
+    const int vr = c / PB_VC, vc = c - vr * PB_VC;
+    koff[i] = (uint32_t)(min(kr, PB_KT - 1) * 512 + (kc < 32 ? kc : 0) * 16);
+    voff[i] = (uint32_t)(min(vr, PB_KT - 1) * 512 + (vc < 32 ? vc : 0) * 16);
+  }
+  auto dma = [&](const char* g, int kt, char* buf, const uint32_t (&off)[5]) {
+    const int64_t last = n_keys - 1 - (int64_t)kt * PB_KT;   // last valid row of the tile
+    const bool partial = last < PB_KT - 1;
+    const char* gt = g + (int64_t)kt * (PB_KT * 512);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int ins = wv + 4 * i;
+      if (i < 4 || wv == 0) {   // 17 instructions: wave 0 issues the last one
+        uint32_t o = off[i];
+        if (partial) o = min(o, (o & 511u) | ((uint32_t)last << 9));
+        __builtin_amdgcn_global_load_lds((const void*)(gt + o), (void HS2_LDS*)(buf + ins * 1024), 16, 0, 0);
+      }
     }
   };
   auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
@@ -127,10 +142,10 @@ __global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnP
   // =============================== sweep 1: lse per row ===============================
   float m_run[2] = {kNegInf, kNegInf}, z_run[2] = {0.f, 0.f};
   const int my_pos[2] = {(int)pos_of_row(l32), (int)pos_of_row(32 + l32)};
-  dma(kg, 0, kbuf(0), PB_KC);
+  dma(kg, 0, kbuf(0), koff);
   wait_dma();
   __syncthreads();
-  if (ntiles > 1) dma(kg, 1, kbuf(1), PB_KC);
+  if (ntiles > 1) dma(kg, 1, kbuf(1), koff);
   f32x16 st_cur[2];
   {
     auto t = s_keys_rows(kbuf(0));
@@ -177,7 +192,7 @@ __global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnP
   for (int kt = 0; kt < ntiles; ++kt) {
     wait_dma();
     __syncthreads();
-    if (kt + 2 < ntiles) dma(kg, kt + 2, kbuf(kt & 1), PB_KC);
+    if (kt + 2 < ntiles) dma(kg, kt + 2, kbuf(kt & 1), koff);
     // the next tile's logits go to the MFMA unit while this tile's max / sum run
     // on the VALU; both branches carry the MFMAs so that they interleave
     const bool need_mask = (int64_t)kt * PB_KT + PB_KT - 1 > pos_first;
@@ -330,14 +345,14 @@ __global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnP
 
   // Sweep 2: per tile, S -> P (float32 -> scores, bf16 -> LDS) -> O += P V.
   // K and V of the next tile are fetched while this one is computed.
-  dma(kg, 0, kbuf(0), PB_KC);
-  dma(vg, 0, vbuf(0), PB_VC);
+  dma(kg, 0, kbuf(0), koff);
+  dma(vg, 0, vbuf(0), voff);
   for (int kt = 0; kt < ntiles; ++kt) {
     wait_dma();
     __syncthreads();
     if (kt + 1 < ntiles) {
-      dma(kg, kt + 1, kbuf((kt + 1) & 1), PB_KC);
-      dma(vg, kt + 1, vbuf((kt + 1) & 1), PB_VC);
+      dma(kg, kt + 1, kbuf((kt + 1) & 1), koff);
+      dma(vg, kt + 1, vbuf((kt + 1) & 1), voff);
     }
     Pair sa = s_rows_keys(kbuf(kt & 1));
     float sc[2][2];
