@@ -3,21 +3,26 @@
 // Same definition and the same two sweeps as attn_prefill.hip (HySparse2
 // pages, agihunt.info summary: the full layer's exact attention probabilities
 // score the tokens for the sparse layers; per head P_hj = exp(l_hj - lse_h),
-// score_j = sum_h P_hj), laid out for MI355X's LDS bandwidth:
+// score_j = sum_h P_hj), laid out for MI355X:
 //
 //  * 64 query rows per wave (64/H tokens x H heads), 4 waves = 256 rows per
-//    workgroup.  Every K or V fragment read from LDS feeds two 32-row MFMA
-//    tiles, which halves the LDS bytes per MFMA flop against 32-row waves;
-//    the 64 x 256 float32 O accumulator of a wave lives in the AGPR file.
+//    workgroup, one wave per SIMD.  Every K or V fragment read from LDS feeds
+//    two 32-row MFMA tiles, which halves the LDS bytes per MFMA flop against
+//    32-row waves; the 64 x 256 float32 O accumulator of a wave fills the AGPR
+//    file.  Rows 0..31 of the wave's queries stay in VGPRs, rows 32..63 are
+//    parked in LDS: the freed registers hold operands fetched three MFMA steps
+//    ahead, which is what hides the LDS latency with a single wave per SIMD.
 //  * K/V tiles of 32 keys are double-buffered in LDS and filled with
 //    global_load_lds_dwordx4 (no register staging): the DMA of tile t+1 runs
-//    while tile t is computed, one barrier per tile.  Lanes fetch permuted
-//    16-byte chunks so that the LDS image is XOR-swizzled (K: chunk ^ (key &
-//    15), V: chunk ^ 2 (key & 3)), which keeps the MFMA operand reads and the
-//    ds_read_b64_tr_b16 reads free of bank conflicts.
-//  * sweep 1: S^T = K Q^T (a lane owns a row, online max/sum in registers);
+//    while tile t is computed, one barrier per tile.  Every buffer is its own
+//    LDS object and the loops are unrolled twice, so that the compiler sees
+//    that reads of one buffer do not depend on the DMA into the other.
+//  * sweep 1: S^T = K Q^T (a lane owns a row, online max/sum in registers,
+//    interleaved with the MFMAs of the next tile);
 //    sweep 2: S = Q K^T (a lane owns a key: float32 P, in-lane head sums for
 //    the scores), P -> LDS [key][row] -> transposed reads -> O += P V.
+#include <type_traits>
+
 #include "hs2_device.hpp"
 #include "hs2_internal.hpp"
 
@@ -38,13 +43,17 @@ constexpr int PB_KC = 33, PB_VC = 34;           // chunks per padded K / V row
 constexpr int PB_KTILE = 17 * 1024;             // 32 x 33 chunks (16.5 KB) rounded to 17 DMA instructions
 constexpr int PB_VTILE = 17 * 1024;             // 32 x 34 chunks = 17 DMA instructions
 constexpr int PB_PP = 144;                      // P buffer pitch (bytes per key)
-constexpr int PB_SMEM = 2 * PB_KTILE + 2 * PB_VTILE + PB_WAVES * PB_KT * PB_PP + PB_WAVES * PB_RW * 4;
+constexpr int PB_AHEAD = 3;                     // operand prefetch distance (MFMA steps)
 
 template <int H>
 __global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnParams p) {
   constexpr int TPW = PB_RW / H;       // tokens per wave
   constexpr int TPB = PB_WAVES * TPW;  // tokens per workgroup
-  __shared__ __attribute__((aligned(1024))) char smem[PB_SMEM];
+  __shared__ __attribute__((aligned(1024))) char lds_k0[PB_KTILE], lds_k1[PB_KTILE];
+  __shared__ __attribute__((aligned(1024))) char lds_v0[PB_VTILE], lds_v1[PB_VTILE];
+  __shared__ __attribute__((aligned(1024))) char lds_q[PB_WAVES * 16 * 1024];
+  __shared__ __attribute__((aligned(16))) char lds_p[PB_WAVES * PB_KT * PB_PP];
+  __shared__ __attribute__((aligned(16))) float lds_lse[PB_WAVES * PB_RW];
 
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int hb = l >> 5, l32 = l & 31;
@@ -61,10 +70,8 @@ __global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnP
   const int ntiles = (int)((n_keys + PB_KT - 1) / PB_KT);
   const char* kg = (const char*)p.k + (int64_t)b * p.T * 512;
   const char* vg = (const char*)p.v + (int64_t)b * p.T * 512;
-  auto kbuf = [&](int i) { return smem + i * PB_KTILE; };
-  auto vbuf = [&](int i) { return smem + 2 * PB_KTILE + i * PB_VTILE; };
-  auto pbuf = [&](int i) { return smem + 2 * PB_KTILE + 2 * PB_VTILE + (wave + i) * PB_KT * PB_PP; };
-  float* lse_lds = (float*)(smem + 2 * PB_KTILE + 2 * PB_VTILE + PB_WAVES * PB_KT * PB_PP) + wave * PB_RW;
+  char* const pbuf = lds_p + wave * PB_KT * PB_PP;
+  float* const lse_lds = lds_lse + wave * PB_RW;
 
   auto tok_of_row = [&](int row) { return tok_w0 + row / H; };
   auto pos_of_row = [&](int row) -> int64_t {
@@ -72,16 +79,24 @@ __global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnP
     return p.q_pos0 + (t < p.n_q ? t : p.n_q - 1);
   };
 
-  // ---- queries: rows 32*mt + l32 of this wave, K-step s covers dims 16s..16s+15
+  // ---- queries: rows 32*mt + l32 of this wave, K-step s covers dims 16s..16s+15.
+  // Rows 0..31 stay in registers; rows 32..63 go to LDS as [s][lane] (16 KB per
+  // wave), so that each fragment read is one conflict-free ds_read_b128.
   const int64_t q_row0 = ((int64_t)b * p.n_q + tok_w0) * H;
-  bf16x8 qf[2][16];
+  bf16x8 qf[16];
+  char* const qlds = lds_q + wave * (16 * 1024) + l * 16;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     const bool ok = tok_of_row(32 * mt + l32) < p.n_q;
     const bf16* qp = (const bf16*)p.q + (q_row0 + 32 * mt + l32) * kHeadDim + 8 * hb;
 #pragma unroll
-    for (int s = 0; s < 16; ++s) qf[mt][s] = ok ? as_bf16x8(*(const u32x4*)(qp + 16 * s)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    for (int s = 0; s < 16; ++s) {
+      const u32x4 v = ok ? *(const u32x4*)(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+      if (mt == 0) qf[s] = as_bf16x8(v);
+      else *(u32x4*)(qlds + s * 1024) = v;
+    }
   }
+  auto q1frag = [&](int s) -> bf16x8 { return as_bf16x8(*(const u32x4*)(qlds + s * 1024)); };
 
   // ---- LDS DMA of one 32-key tile into its padded image: the image is cut into
   // 17 wave-instructions of 64 x 16 B (lane l of instruction i fills chunk
@@ -99,7 +114,7 @@ __global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnP
     koff[i] = (uint32_t)(min(kr, PB_KT - 1) * 512 + (kc < 32 ? kc : 0) * 16);
     voff[i] = (uint32_t)(min(vr, PB_KT - 1) * 512 + (vc < 32 ? vc : 0) * 16);
   }
-  auto dma = [&](const char* g, int kt, char* buf, const uint32_t (&off)[5]) {
+  auto dma = [&](const char* g, int kt, char* buf, const uint32_t (&off)[5]) __attribute__((always_inline)) {
     const int64_t last = n_keys - 1 - (int64_t)kt * PB_KT;   // last valid row of the tile
     const bool partial = last < PB_KT - 1;
     const char* gt = g + (int64_t)kt * (PB_KT * 512);
@@ -109,7 +124,7 @@ __global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnP
       if (i < 4 || wv == 0) {   // 17 instructions: wave 0 issues the last one
         uint32_t o = off[i];
         if (partial) o = min(o, (o & 511u) | ((uint32_t)last << 9));
-        __builtin_amdgcn_global_load_lds((const void*)(gt + o), (void HS2_LDS*)(buf + ins * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(gt + o), (void HS2_LDS*)((char HS2_LDS*)buf + ins * 1024), 16, 0, 0);
       }
     }
   };
@@ -118,23 +133,17 @@ __global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnP
   const int kofs = l32 * (PB_KC * 16) + 16 * hb;
   auto kfrag = [&](const char* buf, int s) -> bf16x8 { return as_bf16x8(*(const u32x4*)(buf + kofs + 32 * s)); };
 
-  // Both sweeps are software-pipelined one tile deep: while the VALU works on
-  // the logits of tile t (exp2, max/sum or probabilities, scores, P -> LDS),
-  // the MFMA unit already computes the logits of tile t+1.  K therefore runs
-  // one tile ahead of V; with double buffers the DMA of K(t+2) and V(t+1) is
-  // issued right after the barrier of iteration t.  The logits of the tile
-  // after the last are computed from a stale buffer and never used, which
-  // keeps the loop body straight-line.
   struct Pair {
     f32x16 v[2];
   };
-  auto s_keys_rows = [&](const char* kb) {   // S^T: lane = row l32 (+32), regs = keys
+  // S^T = K Q^T of one tile (lane = row l32 (+32), regs = keys)
+  auto s_keys_rows = [&](const char* kb) __attribute__((always_inline)) {
     Pair st = {{f32x16{}, f32x16{}}};
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       const bf16x8 kf = kfrag(kb, s);
-      st.v[0] = mfma32(kf, qf[0][s], st.v[0]);
-      st.v[1] = mfma32(kf, qf[1][s], st.v[1]);
+      st.v[0] = mfma32(kf, qf[s], st.v[0]);
+      st.v[1] = mfma32(kf, q1frag(s), st.v[1]);
     }
     return st;
   };
@@ -142,20 +151,15 @@ __global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnP
   // =============================== sweep 1: lse per row ===============================
   float m_run[2] = {kNegInf, kNegInf}, z_run[2] = {0.f, 0.f};
   const int my_pos[2] = {(int)pos_of_row(l32), (int)pos_of_row(32 + l32)};
-  dma(kg, 0, kbuf(0), koff);
+  dma(kg, 0, lds_k0, koff);
   wait_dma();
   __syncthreads();
-  if (ntiles > 1) dma(kg, 1, kbuf(1), koff);
-  f32x16 st_cur[2];
-  {
-    auto t = s_keys_rows(kbuf(0));
-    st_cur[0] = t.v[0];
-    st_cur[1] = t.v[1];
-  }
+  if (ntiles > 1) dma(kg, 1, lds_k1, koff);
+  Pair st_c = s_keys_rows(lds_k0);
   // Online max / sum of one tile (lane: rows l32 and 32 + l32, keys kt*32 +
   // 8(r/4) + 4hb + r%4).  Tiles left of the diagonal need no causal mask:
   // that path is the bulk of the work, so it is kept free of selects.
-  auto lse_update = [&](Pair& st, int kt, bool masked) {
+  auto lse_update = [&](Pair& st, int kt, bool masked) __attribute__((always_inline)) {
     const int kbase = kt * PB_KT;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
@@ -188,33 +192,43 @@ __global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnP
       }
     }
   };
-  Pair st_c = {{st_cur[0], st_cur[1]}};
-  for (int kt = 0; kt < ntiles; ++kt) {
+  // kd: buffer of tile kt (refilled with tile kt+2), kn: buffer of tile kt+1.
+  // While the VALU works on the max / sum of tile kt, the MFMA unit computes
+  // the logits of tile kt+1; the logits of the tile after the last are
+  // computed from a stale buffer and never used, which keeps the loop body
+  // straight-line.
+  auto step1 = [&](int kt, char* kd, const char* kn) __attribute__((always_inline)) {
     wait_dma();
     __syncthreads();
-    if (kt + 2 < ntiles) dma(kg, kt + 2, kbuf(kt & 1), koff);
-    // the next tile's logits go to the MFMA unit while this tile's max / sum run
-    // on the VALU; both branches carry the MFMAs so that they interleave
+    if (kt + 2 < ntiles) dma(kg, kt + 2, kd, koff);
     const bool need_mask = (int64_t)kt * PB_KT + PB_KT - 1 > pos_first;
     Pair st_n;
     if (!need_mask) {
-      st_n = s_keys_rows(kbuf((kt + 1) & 1));
+      st_n = s_keys_rows(kn);
       lse_update(st_c, kt, false);
-      // issue order: MFMA, K-fragment read, VALU, MFMA, VALU, ... so that the
-      // matrix unit never waits for the softmax arithmetic of the other tile
+      // issue order: MFMA, operand read, VALU, MFMA, operand read, VALU, ...
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);
       }
     } else {
-      st_n = s_keys_rows(kbuf((kt + 1) & 1));
+      st_n = s_keys_rows(kn);
       lse_update(st_c, kt, true);
     }
     st_c = st_n;
+  };
+  {
+    int kt = 0;
+    for (; kt + 1 < ntiles; kt += 2) {
+      step1(kt, lds_k0, lds_k1);
+      step1(kt + 1, lds_k1, lds_k0);
+    }
+    if (kt < ntiles) step1(kt, lds_k0, lds_k1);
   }
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
@@ -233,23 +247,33 @@ __global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnP
 #pragma unroll
     for (int n = 0; n < 8; ++n) oacc[mt][n] = f32x16{};
   float* srow_base = p.scores + (int64_t)b * p.n_q * p.ld_scores;
-  auto s_rows_keys = [&](const char* kb) {   // S: lane = key l32, regs = rows
+  // S = Q K^T (lane = key l32, regs = rows), operands PB_AHEAD steps ahead.
+  auto s_rows_keys = [&](const char* kb) __attribute__((always_inline)) {
     Pair sa = {{f32x16{}, f32x16{}}};
+    bf16x8 kf[16], q1[16];
+#pragma unroll
+    for (int s = 0; s < PB_AHEAD; ++s) {
+      kf[s] = kfrag(kb, s);
+      q1[s] = q1frag(s);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
-      const bf16x8 kf = kfrag(kb, s);
-      sa.v[0] = mfma32(qf[0][s], kf, sa.v[0]);
-      sa.v[1] = mfma32(qf[1][s], kf, sa.v[1]);
+      sa.v[0] = mfma32(qf[s], kf[s], sa.v[0]);
+      if (s + PB_AHEAD < 16) kf[s + PB_AHEAD] = kfrag(kb, s + PB_AHEAD);
+      sa.v[1] = mfma32(q1[s], kf[s], sa.v[1]);
+      if (s + PB_AHEAD < 16) q1[s + PB_AHEAD] = q1frag(s + PB_AHEAD);
+      __builtin_amdgcn_sched_barrier(0);
     }
     return sa;
   };
 
   // probabilities of tile kt (lane: key kbase + l32, rows 32mt + 8(r/4) + 4hb + r%4),
   // the score of each token of the lane's key, and P (bf16) -> LDS [key][row]
-  auto probs = [&](Pair& sa, int kt, char* pb, float (&sc)[2][2]) {
+  auto probs = [&](Pair& sa, int kt, char* pb, float (&sc)[2][2], auto masked) __attribute__((always_inline)) {
+    constexpr bool need_mask = decltype(masked)::value;
     const int64_t kbase = (int64_t)kt * PB_KT;
     const int64_t key = kbase + l32;
-    const bool need_mask = kbase + PB_KT - 1 > pos_first;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -259,7 +283,7 @@ __global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnP
         for (int j = 0; j < 4; ++j) {
           const int r = 4 * q + j;
           const float e = fast_exp2(sa.v[mt][r] * p.scale_log2 - l4[j]);
-          if (need_mask)
+          if constexpr (need_mask)
             sa.v[mt][r] = key <= pos_of_row(32 * mt + 8 * q + 4 * hb + j) ? e : 0.f;
           else
             sa.v[mt][r] = e;
@@ -292,7 +316,7 @@ __global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnP
     }
   };
   // scores of tile kt to global memory (token sums of 32/H tokens per 32-row tile)
-  auto store_scores = [&](const Pair& sa, int kt, const float (&sc)[2][2]) {
+  auto store_scores = [&](const Pair& sa, int kt, const float (&sc)[2][2]) __attribute__((always_inline)) {
     const int64_t key = (int64_t)kt * PB_KT + l32;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -321,46 +345,86 @@ __global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnP
       }
     }
   };
-  // O += P V for one tile (A = P rows x keys, B = V keys x dims, both via transposed reads)
-  auto pv = [&](const char* pb, const char* vb) {
-#pragma unroll
-    for (int ks = 0; ks < PB_KT / 16; ++ks) {
+  // O += P V for one tile (A = P rows x keys, B = V keys x dims, both via
+  // transposed reads).  Step j = (ks, n) = (j / 8, j % 8); the V fragment of
+  // step j is read PB_AHEAD steps before it is used, P of K-step 1 at step 4.
+  auto pv = [&](const char* pb, const char* vb) __attribute__((always_inline)) {
+    bf16x8 a[2][2], bv[16];
+    auto read_a = [&](int ks) {
       const int krow = 16 * ks + 8 * (G >> 1) + (s16 >> 2);
       const int off = 16 * (G & 1) + 4 * (s16 & 3);
-      bf16x8 a[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         const bf16* pa = (const bf16*)(pb + krow * PB_PP) + 32 * mt + off;
-        a[mt] = cat8(lds_tr16(pa), lds_tr16(pa + 4 * (PB_PP / 2)));
+        a[ks][mt] = cat8(lds_tr16(pa), lds_tr16(pa + 4 * (PB_PP / 2)));
       }
+    };
+    auto read_b = [&](int j) {
+      const int ks = j >> 3, n = j & 7;
+      const int krow = 16 * ks + 8 * (G >> 1) + (s16 >> 2);
+      const int off = 16 * (G & 1) + 4 * (s16 & 3);
       const bf16* vrow = (const bf16*)(vb + krow * (PB_VC * 16)) + off;
+      bv[j] = cat8(lds_tr16(vrow + 32 * n), lds_tr16(vrow + 4 * (PB_VC * 8) + 32 * n));
+    };
+    read_a(0);
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const bf16x8 bv = cat8(lds_tr16(vrow + 32 * n), lds_tr16(vrow + 4 * (PB_VC * 8) + 32 * n));
-        oacc[0][n] = mfma32(a[0], bv, oacc[0][n]);
-        oacc[1][n] = mfma32(a[1], bv, oacc[1][n]);
-      }
+    for (int j = 0; j < PB_AHEAD; ++j) read_b(j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int ks = j >> 3, n = j & 7;
+      oacc[0][n] = mfma32(a[ks][0], bv[j], oacc[0][n]);
+      if (j + PB_AHEAD < 16) read_b(j + PB_AHEAD);
+      oacc[1][n] = mfma32(a[ks][1], bv[j], oacc[1][n]);
+      if (j == 4) read_a(1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // Sweep 2: per tile, S -> P (float32 -> scores, bf16 -> LDS) -> O += P V.
-  // K and V of the next tile are fetched while this one is computed.
-  dma(kg, 0, kbuf(0), koff);
-  dma(vg, 0, vbuf(0), voff);
-  for (int kt = 0; kt < ntiles; ++kt) {
+  // K and V of the next tile are fetched while this one is computed.  With
+  // H >= 8 the scores of a tile are two (four) floats per lane; they are
+  // written one tile late, right after the DMA issue, so that the stores have
+  // long completed when the next wait on the vector-memory counter comes.
+  float sc_prev[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  auto step2 = [&](int kt, const char* kc, const char* vc, char* kn, char* vn) __attribute__((always_inline)) {
     wait_dma();
     __syncthreads();
     if (kt + 1 < ntiles) {
-      dma(kg, kt + 1, kbuf((kt + 1) & 1), koff);
-      dma(vg, kt + 1, vbuf((kt + 1) & 1), voff);
+      dma(kg, kt + 1, kn, koff);
+      dma(vg, kt + 1, vn, voff);
     }
-    Pair sa = s_rows_keys(kbuf(kt & 1));
+    if constexpr (H >= 8) {
+      if (kt > 0) store_scores(Pair{}, kt - 1, sc_prev);
+    }
+    Pair sa = s_rows_keys(kc);
     float sc[2][2];
-    probs(sa, kt, pbuf(0), sc);
-    store_scores(sa, kt, sc);
+    // tiles left of the diagonal need no causal mask (uniform branch)
+    if ((int64_t)kt * PB_KT + PB_KT - 1 > pos_first)
+      probs(sa, kt, pbuf, sc, std::true_type{});
+    else
+      probs(sa, kt, pbuf, sc, std::false_type{});
+    if constexpr (H >= 8) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) sc_prev[mt][0] = sc[mt][0], sc_prev[mt][1] = sc[mt][1];
+    } else {
+      store_scores(sa, kt, sc);
+    }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    pv(pbuf(0), vbuf(kt & 1));
+    __builtin_amdgcn_sched_barrier(0);
+    pv(pbuf, vc);
+  };
+  dma(kg, 0, lds_k0, koff);
+  dma(vg, 0, lds_v0, voff);
+  {
+    int kt = 0;
+    for (; kt + 1 < ntiles; kt += 2) {
+      step2(kt, lds_k0, lds_v0, lds_k1, lds_v1);
+      step2(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+    }
+    if (kt < ntiles) step2(kt, lds_k0, lds_v0, lds_k1, lds_v1);
   }
+  if constexpr (H >= 8) store_scores(Pair{}, ntiles - 1, sc_prev);
 
   // ---- outputs: lane holds O[32mt + 8(r/4) + 4hb + r%4][32n + l32]
 #pragma unroll
