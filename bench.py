@@ -43,7 +43,147 @@ def parse():
     ap.add_argument("--workload", default="prefill_128k")
     ap.add_argument("--cpu-rows", type=int, default=74, help="oracle sample size (rows)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="run one warm-up step and one step of the full-attention launches, then a 1 GiB "
+                         "copy-calibration kernel (the target of the traffic counter runs)")
+    ap.add_argument("--collect-traffic", action="store_true",
+                    help="run rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE over --pmc-probe and record the "
+                         "per-launch HBM traffic of the full-attention kernel under profiles/")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_128k_traffic.txt")
+KERNEL_SOURCES = ["attn_prefill_bf16.hip", "hs2_device.hpp", "hs2_internal.hpp"]
+CALIB_BYTES = 1 << 30          # the calibration kernel reads and writes exactly this many bytes
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the sources the full-attention kernel is compiled from."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "token_level_sparse_full_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """Per-launch HBM bytes of the full-attention kernel recorded by --collect-traffic,
+    or None when there is no record or the kernel sources changed since it was taken."""
+    try:
+        rec = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if "=" in line and not line.startswith("#"):
+                    key, val = line.split("=", 1)
+                    rec[key.strip()] = val.strip()
+        if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+            return None
+        return float(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def collect_traffic(args):
+    """Two counter passes (FETCH_SIZE, then WRITE_SIZE) over `bench.py --pmc-probe`, each
+    scaled by what the same counter reads for a copy kernel that moves exactly CALIB_BYTES."""
+    import csv
+    import glob
+    import subprocess
+
+    out_root = os.path.join(ROOT, "gpurun_out", "traffic")
+    res = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        d = os.path.join(out_root, ctr.lower())
+        cmd = ["rocprofv3", "--pmc", ctr, "--output-format", "csv", "-d", d, "-o", "p", "--",
+               sys.executable, os.path.join(ROOT, "bench.py"), "--pmc-probe", "--workload", args.workload,
+               "--chunk", str(args.chunk)]
+        print("[traffic] " + " ".join(cmd), flush=True)
+        env = dict(os.environ, TMPDIR="/tmp")
+        r = subprocess.run(cmd, cwd="/tmp", env=env, timeout=300)
+        if r.returncode != 0:
+            raise SystemExit(f"rocprofv3 {ctr} pass failed with status {r.returncode}")
+        rows = []
+        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows += list(csv.DictReader(open(fn)))
+        per = {}
+        for row in rows:
+            if row["Counter_Name"] != ctr:
+                continue
+            key = (int(row["Dispatch_Id"]), row["Kernel_Name"])
+            per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+        disp = sorted(per.items())
+        attn = [v for (i, n), v in disp if "prefill_bf16_kernel" in n]
+        calib = [v for (i, n), v in disp if "elementwise" in n]
+        n_launch = len(range(0, inputs_L(args), min(args.chunk, inputs_L(args))))
+        attn = attn[-n_launch:]                       # the measured step (the warm-up step comes first)
+        res[ctr] = {"attn_kib_per_launch": sum(attn) / len(attn), "calib_kib": calib[-1], "launches": len(attn)}
+    # one more pass: MFMA busy cycles of the same launches (utilisation of the matrix cores)
+    d = os.path.join(out_root, "sq")
+    sq_ctrs = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"]
+    cmd = ["rocprofv3", "--pmc", *sq_ctrs, "--output-format", "csv", "-d", d, "-o", "p", "--",
+           sys.executable, os.path.join(ROOT, "bench.py"), "--pmc-probe", "--workload", args.workload,
+           "--chunk", str(args.chunk)]
+    print("[traffic] " + " ".join(cmd), flush=True)
+    r = subprocess.run(cmd, cwd="/tmp", env=dict(os.environ, TMPDIR="/tmp"), timeout=300)
+    if r.returncode != 0:
+        raise SystemExit(f"rocprofv3 SQ pass failed with status {r.returncode}")
+    rows = []
+    for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        rows += list(csv.DictReader(open(fn)))
+    sq, dur = {}, {}
+    for row in rows:
+        if "prefill_bf16_kernel" not in row["Kernel_Name"]:
+            continue
+        i = int(row["Dispatch_Id"])
+        sq.setdefault(i, {}).setdefault(row["Counter_Name"], 0.0)
+        sq[i][row["Counter_Name"]] += float(row["Counter_Value"])
+        dur[i] = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-9
+    last = sorted(sq)[-res["FETCH_SIZE"]["launches"]:]
+    sq_avg = {c: sum(sq[i].get(c, 0.0) for i in last) / len(last) for c in sq_ctrs}
+    dur_avg = sum(dur[i] for i in last) / len(last)
+    # busy cycles of all 1024 SIMDs over the launch at the 2.4 GHz peak clock (a lower bound
+    # on the utilisation when the clock runs below peak)
+    mfma_util = sq_avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * dur_avg * 2.4e9)
+    f_fetch = CALIB_BYTES / (res["FETCH_SIZE"]["calib_kib"] * 1024.0)
+    f_write = CALIB_BYTES / (res["WRITE_SIZE"]["calib_kib"] * 1024.0)
+    fetch_b = res["FETCH_SIZE"]["attn_kib_per_launch"] * 1024.0 * f_fetch
+    write_b = res["WRITE_SIZE"]["attn_kib_per_launch"] * 1024.0 * f_write
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("# HBM traffic of the scored full-attention kernel (prefill_bf16_kernel), one launch of the\n")
+        f.write(f"# {args.workload} step ({res['FETCH_SIZE']['launches']} launches of {args.chunk} queries,"
+                " averaged), from rocprofv3 counter passes.\n")
+        f.write("# command: python bench.py --collect-traffic   (runs, one pass per counter set:)\n")
+        f.write(f"#   rocprofv3 --pmc <FETCH_SIZE | WRITE_SIZE | {' '.join(sq_ctrs)}> --output-format csv -d <dir> -o p"
+                f" -- python bench.py --pmc-probe --workload {args.workload} --chunk {args.chunk}\n")
+        f.write("# calibration: a float32 copy kernel (torch.mul by 1.0) that reads and writes exactly 1 GiB;\n")
+        f.write("# each counter is scaled by (1 GiB / what it reads for that kernel).\n")
+        f.write(f"fetch_kib_per_launch_raw = {res['FETCH_SIZE']['attn_kib_per_launch']:.1f}\n")
+        f.write(f"write_kib_per_launch_raw = {res['WRITE_SIZE']['attn_kib_per_launch']:.1f}\n")
+        f.write(f"calib_fetch_kib = {res['FETCH_SIZE']['calib_kib']:.1f}\n")
+        f.write(f"calib_write_kib = {res['WRITE_SIZE']['calib_kib']:.1f}\n")
+        f.write(f"scale_fetch = {f_fetch:.4f}\n")
+        f.write(f"scale_write = {f_write:.4f}\n")
+        f.write(f"fetch_bytes_per_launch = {fetch_b:.4e}\n")
+        f.write(f"write_bytes_per_launch = {write_b:.4e}\n")
+        f.write(f"traffic_bytes_per_launch = {fetch_b + write_b:.4e}\n")
+        f.write("# MFMA utilisation of the same launches (third pass, SQ counters, per launch):\n")
+        for c in sq_ctrs:
+            f.write(f"{c.lower()} = {sq_avg[c]:.4e}\n")
+        f.write(f"launch_seconds_under_counters = {dur_avg:.4f}\n")
+        f.write(f"mfma_busy_frac_at_2p4ghz = {mfma_util:.4f}\n")
+        f.write(f"kernel_source_sha256_16 = {kernel_source_hash()}\n")
+    text = open(TRAFFIC_FILE).read()
+    os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
+    with open(os.path.join(ROOT, "gpurun_out", os.path.basename(TRAFFIC_FILE)), "w") as f:
+        f.write(text)
+    print(text, flush=True)
+
+
+def inputs_L(args) -> int:
+    from token_level_sparse_full_amd import inputs
+    return inputs.WORKLOADS[args.workload].L
 
 
 def main():
@@ -51,6 +191,9 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
         sys.exit(2)
+    if args.collect_traffic:      # orchestration only: this process never touches the GPU
+        collect_traffic(args)
+        return
 
     import numpy as np
     import torch
@@ -103,6 +246,20 @@ def main():
         for s in range(n_sparse):
             hs2.hs2_sparse_attn_reuse(qs[s], k, v, idx, cnt, sm_scale=scale, o=o_sp[s], lse=lse_sp[s])
             mark()
+
+    if args.pmc_probe:
+        step()                                   # warm-up step
+        torch.cuda.synchronize()
+        for c0, c1 in chunks:                    # the measured full-attention launches
+            hs2.hs2_full_attn_scored(q[:, c0:c1], k, v, q_pos0=c0, sm_scale=scale, o=o_full[:, c0:c1],
+                                     lse=lse_full[:, c0:c1], scores=scores[:, : c1 - c0], ld_scores=ld)
+        torch.cuda.synchronize()
+        a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.mul(a, 1.0, out=b)                 # copy calibration: reads and writes 1 GiB
+        torch.cuda.synchronize()
+        print("pmc probe done", flush=True)
+        return
 
     # ---------------------------------------------------------------- warmup + timed steps
     for _ in range(args.warmup):
@@ -161,7 +318,8 @@ def main():
                    "global_batch": 1, "parallelism": "single GPU"},
         "roofline": {"kernel": "prefill_kernel (scored full attention)", "bound": "mfma",
                      "achieved": fa_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": fa_tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                     "frac": fa_tflops / BF16_PEAK_TFLOPS, "traffic": read_traffic(),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "algorithmic_flop_per_step": fa_flop, "launches_per_step": len(chunks)},
         "stages": {
             "full_attn_ms": fa_ms, "select_ms": sel_ms, "sparse_ms_per_layer": sp_ms,
