@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--workload", default="prefill_128k")
     ap.add_argument("--cpu-rows", type=int, default=74, help="oracle sample size (rows)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the decode (16 x 32k, 1M FP8) and bridge (64k) workload lines")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run one warm-up step and one step of the full-attention launches, then a 1 GiB "
                          "copy-calibration kernel (the target of the traffic counter runs)")
@@ -330,11 +332,141 @@ def main():
         },
     }
 
+    if not args.no_others:
+        result["other_workloads"] = other_workloads(dev)
+
     # ---------------------------------------------------------------- oracle sample (host cores)
     if not args.no_cpu:
         result["cpu_baseline"], result["sample_parity"] = cpu_baseline(
             args, inp, needles, step, keep_rows, idx, cnt, o_full, o_sp, L, H, scale, window, topk)
     print(json.dumps(result), flush=True)
+
+
+def _timed(run, stages: int, reps: int = 10, warm: int = 3, flush=None):
+    """Median over reps of the HIP-event times between stage marks (run(mark) calls mark()
+    after each stage).  flush() runs between reps, outside the timed region."""
+    import numpy as np
+    import torch
+
+    for _ in range(warm):
+        run(lambda: None)
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(stages + 1)]
+        it = iter(ev)
+        next(it).record()
+        run(lambda: next(it).record())
+        torch.cuda.synchronize()
+        per.append([ev[i].elapsed_time(ev[i + 1]) for i in range(stages)])
+    return np.median(np.array(per), axis=0)
+
+
+def other_workloads(dev):
+    """The decode and bridge workloads at their own sizes: HIP-event times of each stage
+    (median of 10 after 3 warm-ups; a 512 MiB buffer write between reps pushes K/V out of
+    L2 and MALL) against the HBM (decode stages) or bf16 MFMA (bridge) roofline."""
+    import torch
+
+    from token_level_sparse_full_amd import hs2, inputs
+
+    out = {}
+    junk = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = lambda: junk.fill_(1)  # noqa: E731
+    win, topk, ms = 128, 1024, 128 + 1024
+    scale = 1.0 / 16
+
+    def decode_step(q, qs, k, v, T, p, ks=None, vs=None):
+        B, _, H, _ = q.shape
+        kvd = hs2._dtype_code(k)
+        ws = hs2.workspace(hs2.full_attn_workspace_bytes(B, 1, H, T, kvd), dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, 1, H), dtype=torch.float32, device=dev)
+        ld = (p + 1 + 3) // 4 * 4
+        sc = torch.empty((B, 1, ld), dtype=torch.float32, device=dev)
+        idx = torch.empty((B, 1, ms), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B, 1), dtype=torch.int32, device=dev)
+        o2 = [torch.empty_like(x) for x in qs]
+        l2 = [torch.empty((B, 1, H), dtype=torch.float32, device=dev) for _ in qs]
+
+        def run(mark):
+            hs2.hs2_full_attn_scored(q, k, v, q_pos0=p, sm_scale=scale, k_scale=ks, v_scale=vs, o=o, lse=lse,
+                                     scores=sc, ld_scores=ld, ws=ws)
+            mark()
+            hs2.hs2_select_topk_window(sc, q_pos0=p, T=T, idx=idx, count=cnt)
+            mark()
+            for i, x in enumerate(qs):
+                hs2.hs2_sparse_attn_reuse(x, k, v, idx, cnt, sm_scale=scale, k_scale=ks, v_scale=vs, o=o2[i],
+                                          lse=l2[i])
+            mark()
+        return _timed(run, 3, flush=flush)
+
+    # batched decode: 16 sequences x 32k keys, 3 sparse layers
+    wl = inputs.WORKLOADS["decode_b16_32k"]
+    inp = inputs.attention_inputs(B=wl.B, n_q=1, T=wl.T, H=wl.H, d=D, kv="bf16", n_sparse=wl.n_sparse, seed=wl.seed,
+                                  device=dev)
+    t_fa, t_sel, t_sp = decode_step(inp["q"], inp["q_sparse"], inp["k"], inp["v"], wl.T, wl.T - 1)
+    kv_bytes = 2.0 * wl.B * wl.T * 512
+    sp_bytes = wl.B * (ms * 2 * 512 + 2 * wl.H * D * 2 + ms * 4)
+    out[wl.name] = {
+        "ms_per_step": float(t_fa + t_sel + t_sp), "queries_per_s": wl.B / ((t_fa + t_sel + t_sp) * 1e-3),
+        "full_attn_ms": float(t_fa), "full_attn_hbm_frac": kv_bytes / (t_fa * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "select_ms": float(t_sel), "sparse_ms_all_layers": float(t_sp),
+        "sparse_hbm_frac": wl.n_sparse * sp_bytes / (t_sp * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "note": "cold: a 512 MiB write between reps; K/V 512 MiB per step"}
+    del inp
+    torch.cuda.empty_cache()
+
+    # one 1M-token sequence, FP8 e4m3 K/V with per-row scales, 4 decode steps, 4 sparse layers each
+    wl = inputs.WORKLOADS["decode_1m_fp8"]
+    k, v, ks, vs = inputs.kv_cache((1, wl.T, 256), "e4m3", wl.seed, dev)
+    steps = []
+    for st in range(wl.steps):
+        p = wl.T - wl.steps + st
+        q = inputs.cast(inputs.normal((1, 1, wl.H, 256), inputs.STD_QKV, wl.seed, inputs.S_Q + 10 * st, dev), "bf16")
+        qs = [inputs.cast(inputs.normal((1, 1, wl.H, 256), inputs.STD_QKV, wl.seed, inputs.S_QSPARSE + 10 * st + i,
+                                        dev), "bf16") for i in range(wl.n_sparse)]
+        steps.append(decode_step(q, qs, k, v, wl.T, p, ks, vs))
+    t_fa = sum(x[0] for x in steps) / len(steps)
+    t_sel = sum(x[1] for x in steps) / len(steps)
+    t_sp = sum(x[2] for x in steps) / len(steps)
+    kv_bytes = 2.0 * wl.T * (256 + 4)
+    out[wl.name] = {
+        "ms_per_step": float(t_fa + t_sel + t_sp), "queries_per_s": 1.0 / ((t_fa + t_sel + t_sp) * 1e-3),
+        "full_attn_ms": float(t_fa), "full_attn_hbm_frac": kv_bytes / (t_fa * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "select_ms": float(t_sel), "sparse_ms_all_layers": float(t_sp),
+        "note": "mean of the 4 steps (p = T-4 .. T-1); cold between reps"}
+    del k, v, ks, vs
+    torch.cuda.empty_cache()
+
+    # KV bridging: 4 projections of a 64k-token hidden state, then 4 bridged decode steps
+    wl = inputs.WORKLOADS["bridge_64k"]
+    br = inputs.bridge_inputs(L=wl.L, D=wl.D, n_layers=wl.n_full, d=256, seed=wl.seed, device=dev)
+    k_all = torch.empty((wl.n_full, wl.L, 256), dtype=torch.bfloat16, device=dev)
+    v_all = torch.empty_like(k_all)
+
+    def run_bridge(mark):
+        hs2.hs2_bridge_kv_proj(br["x"], br["w_k"], br["w_v"], k_out=k_all, v_out=v_all)
+        mark()
+    (t_br,) = _timed(run_bridge, 1)
+    br_flop = 2.0 * wl.L * wl.D * (2 * wl.n_full * 256)
+    t_layers = []
+    for m in range(wl.n_full):
+        q = inputs.cast(inputs.normal((1, 1, wl.H, 256), inputs.STD_QKV, wl.seed, inputs.S_QFULL_LAYER + m, dev),
+                        "bf16")
+        qs = [inputs.cast(inputs.normal((1, 1, wl.H, 256), inputs.STD_QKV, wl.seed, inputs.S_QSPARSE + 8 * m + i, dev),
+                          "bf16") for i in range(wl.n_sparse)]
+        t_layers.append(decode_step(q, qs, k_all[m:m + 1], v_all[m:m + 1], wl.L, wl.L - 1))
+    t_cross = float(sum(sum(x) for x in t_layers))
+    out[wl.name] = {
+        "bridge_ms": float(t_br), "bridge_tflops": br_flop / (t_br * 1e-3) / 1e12,
+        "bridge_mfma_frac": br_flop / (t_br * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+        "cross_decoder_step_ms": t_cross, "prefill_tokens_per_s": wl.L / ((t_br + t_cross) * 1e-3),
+        "note": "bridge warm (inputs resident); the 4 bridged decode steps cold"}
+    del junk
+    return out
 
 
 def cpu_baseline(args, inp, needles, step, keep_rows, idx, cnt, o_full, o_sp, L, H, scale, window, topk):

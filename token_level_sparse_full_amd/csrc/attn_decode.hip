@@ -8,8 +8,9 @@
 //   split   : grid (key chunks, sequences); each workgroup computes the
 //             float32 logits of its keys (kept in the workspace, log2 units),
 //             and a partial softmax state (max, sum, unnormalised O) per row;
-//   combine : one workgroup per (row, sequence) merges the partial states into
-//             O, lse (and lse in log2 units for the next kernel);
+//   merge   : a tree of workgroups merges the partial states (32 per
+//             workgroup and level) into O, lse (and lse in log2 units for the
+//             next kernel);
 //   score   : one thread per key, s_j = sum_h exp2(x_hj - lse2_h) per query.
 // No atomics: every partial has its own slot, so results are deterministic.
 #include "attn_tile.hpp"
@@ -30,9 +31,13 @@ struct DecodeWs {
   float* part_m;  // [B][nch][16]
   float* part_z;  // [B][nch][16]
   float* part_o;  // [B][nch][16][256]
+  float* mid_m;   // [B][nmid][16]       partial states after one merge level
+  float* mid_z;   // [B][nmid][16]
+  float* mid_o;   // [B][nmid][16][256]
   float* lse2;    // [B][16]
-  int chunk, nch;
+  int chunk, nch, nmid;
 };
+constexpr int kMergeFan = 32;   // partial states merged per workgroup and level
 
 int decode_chunk(int B, int64_t T) {
   const int64_t total = (int64_t)B * T;
@@ -57,9 +62,14 @@ size_t decode_ws_layout(int B, int64_t T, char* base, DecodeWs* ws) {
   w.part_m = take((size_t)B * nch * 16 * 4);
   w.part_z = take((size_t)B * nch * 16 * 4);
   w.part_o = take((size_t)B * nch * 16 * 256 * 4);
+  const int64_t nmid = (nch + kMergeFan - 1) / kMergeFan;
+  w.mid_m = take((size_t)B * nmid * 16 * 4);
+  w.mid_z = take((size_t)B * nmid * 16 * 4);
+  w.mid_o = take((size_t)B * nmid * 16 * 256 * 4);
   w.lse2 = take((size_t)B * 16 * 4);
   w.chunk = ch;
   w.nch = (int)nch;
+  w.nmid = (int)nmid;
   if (ws) *ws = w;
   return off;
 }
@@ -189,34 +199,62 @@ __global__ __launch_bounds__(DC_THREADS) void decode_split_kernel(const AttnPara
   }
 }
 
-template <int QKIND>
-__global__ __launch_bounds__(256) void decode_combine_kernel(const AttnParams p, const DecodeWs ws) {
-  const int row = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const int64_t n_keys = p.q_pos0 + p.n_q;
-  const int nch = (int)((n_keys + ws.chunk - 1) / ws.chunk);
-  const int64_t pb = (int64_t)b * ws.nch * 16;
+// Merge of partial softmax states (m, z, unnormalised O) over key chunks, as
+// a tree: workgroup (g, row, b) merges the states g*F .. g*F+F-1 of one row
+// (thread = head dim).  Intermediate levels write merged states; the last
+// level (one output state) writes O, lse and lse2.  The order of the sums is
+// fixed, so results are deterministic.
+struct MergeIO {
+  const float* in_m;
+  const float* in_z;
+  const float* in_o;
+  float* out_m;
+  float* out_z;
+  float* out_o;
+  int in_stride, nin, out_stride;   // states per sequence in the layouts; valid inputs
+};
+
+template <int QKIND, bool FINAL>
+__global__ __launch_bounds__(256) void decode_merge_kernel(const AttnParams p, const DecodeWs ws, const MergeIO io) {
+  const int g = blockIdx.x, row = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
+  const int c0 = g * kMergeFan, c1 = min(io.nin, c0 + kMergeFan);
+  const int64_t ib = (int64_t)b * io.in_stride;
+  float mc[kMergeFan];
   float M = kNegInf;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, ws.part_m[pb + c * 16 + row]);
+#pragma unroll
+  for (int i = 0; i < kMergeFan; ++i) {
+    mc[i] = (c0 + i < c1) ? io.in_m[(ib + c0 + i) * 16 + row] : kNegInf;
+    M = fmaxf(M, mc[i]);
+  }
   float Z = 0.f, acc = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const float mc = ws.part_m[pb + c * 16 + row];
-    if (mc != kNegInf) {
-      const float f = fast_exp2(mc - M);
-      Z += ws.part_z[pb + c * 16 + row] * f;
-      acc += ws.part_o[((pb + c * 16 + row)) * kHeadDim + d] * f;
+#pragma unroll
+  for (int i = 0; i < kMergeFan; ++i) {
+    if (mc[i] != kNegInf) {
+      const float f = fast_exp2(mc[i] - M);
+      Z += io.in_z[(ib + c0 + i) * 16 + row] * f;
+      acc += io.in_o[((ib + c0 + i) * 16 + row) * kHeadDim + d] * f;
     }
   }
-  const int R = gridDim.x;
-  const int64_t oi = ((int64_t)b * R + row) * kHeadDim + d;
-  const float out = acc / Z;
-  if constexpr (QKIND == KV_F32)
-    ((float*)p.o)[oi] = out;
-  else
-    ((bf16*)p.o)[oi] = to_bf16(out);
-  if (d == 0) {
-    const float l2 = M + fast_log2(Z);
-    ws.lse2[b * 16 + row] = l2;
-    if (p.lse) p.lse[(int64_t)b * R + row] = l2 * kLn2;
+  if constexpr (FINAL) {
+    const int R = gridDim.y;
+    const int64_t oi = ((int64_t)b * R + row) * kHeadDim + d;
+    const float out = acc / Z;
+    if constexpr (QKIND == KV_F32)
+      ((float*)p.o)[oi] = out;
+    else
+      ((bf16*)p.o)[oi] = to_bf16(out);
+    if (d == 0) {
+      const float l2 = M + fast_log2(Z);
+      ws.lse2[b * 16 + row] = l2;
+      if (p.lse) p.lse[(int64_t)b * R + row] = l2 * kLn2;
+    }
+  } else {
+    const int64_t ob = ((int64_t)b * io.out_stride + g) * 16 + row;
+    io.out_o[ob * kHeadDim + d] = acc;
+    if (d == 0) {
+      io.out_m[ob] = M;
+      io.out_z[ob] = Z;
+    }
   }
 }
 
@@ -246,10 +284,26 @@ hipError_t launch_decode_h(const AttnParams& p, const DecodeWs& ws, hipStream_t 
   const unsigned nch = (unsigned)((n_keys + ws.chunk - 1) / ws.chunk);
   hipLaunchKernelGGL((decode_split_kernel<KV, H>), dim3(nch, p.B), dim3(DC_THREADS), 0, stream, p, ws);
   const int R = p.n_q * p.H;
+  // merge tree over the chunk states: part -> mid -> part -> ... -> final
+  MergeIO io{ws.part_m, ws.part_z, ws.part_o, ws.mid_m, ws.mid_z, ws.mid_o, ws.nch, (int)nch, ws.nmid};
+  while (io.nin > kMergeFan) {
+    const int nout = (io.nin + kMergeFan - 1) / kMergeFan;
+    hipLaunchKernelGGL((decode_merge_kernel<KV_BF16, false>), dim3(nout, R, p.B), dim3(256), 0, stream, p, ws, io);
+    const bool to_mid = io.out_m == ws.mid_m;
+    io.in_m = io.out_m;
+    io.in_z = io.out_z;
+    io.in_o = io.out_o;
+    io.in_stride = io.out_stride;
+    io.nin = nout;
+    io.out_m = to_mid ? ws.part_m : ws.mid_m;   // the inputs of the previous level are free again
+    io.out_z = to_mid ? ws.part_z : ws.mid_z;
+    io.out_o = to_mid ? ws.part_o : ws.mid_o;
+    io.out_stride = to_mid ? ws.nch : ws.nmid;
+  }
   if (KV == KV_F32)
-    hipLaunchKernelGGL((decode_combine_kernel<KV_F32>), dim3(R, p.B), dim3(256), 0, stream, p, ws);
+    hipLaunchKernelGGL((decode_merge_kernel<KV_F32, true>), dim3(1, R, p.B), dim3(256), 0, stream, p, ws, io);
   else
-    hipLaunchKernelGGL((decode_combine_kernel<KV_BF16>), dim3(R, p.B), dim3(256), 0, stream, p, ws);
+    hipLaunchKernelGGL((decode_merge_kernel<KV_BF16, true>), dim3(1, R, p.B), dim3(256), 0, stream, p, ws, io);
   hipLaunchKernelGGL((decode_score_kernel<H>), dim3((unsigned)((n_keys + 255) / 256), p.B), dim3(256), 0, stream, p, ws);
   return hipGetLastError();
 }
