@@ -76,7 +76,10 @@ def test_workspace_sizes(lib):
     assert lib.hs2_full_attn_workspace_bytes(1, 2048, 4, 2048, F32) == 0
     assert lib.hs2_full_attn_workspace_bytes(16, 1, 16, 32768, BF16) >= 16 * 32768 * 16 * 4
     assert lib.hs2_bridge_workspace_bytes(4, 2048, 256) == 0
-    assert lib.hs2_select_workspace_bytes(1, 1, 1 << 20, (1 << 20) - 1) == 0
+    # few long rows (decode) use the multi-workgroup selector: histograms + per-segment counts
+    assert lib.hs2_select_workspace_bytes(1, 1, 1 << 20, (1 << 20) - 1) >= 3 * 2048 * 4 + (1 << 20) // 4096 * 8
+    assert lib.hs2_select_workspace_bytes(1, 32768, 131072, 98304) == 0     # many rows: one workgroup per row
+    assert lib.hs2_select_workspace_bytes(16, 1, 32768, 32767) == 0         # 16 rows below 32768 candidates
 
 
 def sel(lib, **kw):

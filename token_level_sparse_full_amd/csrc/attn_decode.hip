@@ -75,7 +75,7 @@ size_t decode_ws_layout(int B, int64_t T, char* base, DecodeWs* ws) {
 }
 
 template <int KV, int H>
-__global__ __launch_bounds__(DC_THREADS) void decode_split_kernel(const AttnParams p, const DecodeWs ws) {
+__global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(const AttnParams p, const DecodeWs ws) {
   constexpr int STEP = TileCfg<KV>::STEP;
   constexpr int NMT = STEP / 16;
   constexpr int ROWB = (KV == KV_F32) ? 1024 : (KV == KV_BF16 ? 512 : 256);

@@ -18,6 +18,8 @@
 // LDS histograms) start right below them and split the actual value range
 // instead of the (nearly constant) exponent.  The compaction pass is a
 // block-wide ordered scan that stops as soon as topk candidates are out.
+// Few long rows (at most 64 rows, at least 32768 candidates, the decode case)
+// go to a multi-workgroup version of the same selection (below).
 #include "hs2_device.hpp"
 #include "hs2_internal.hpp"
 
@@ -59,6 +61,24 @@ __device__ __forceinline__ int block_excl_scan(int v, int tid, SelShared& sh, in
   total = 0;
 #pragma unroll
   for (int w = 0; w < SEL_WAVES; ++w) {
+    const int t = sh.wave_tot[w];
+    before += (w < wave) ? t : 0;
+    total += t;
+  }
+  __syncthreads();
+  return before + inc - v;
+}
+
+template <int NT>
+__device__ __forceinline__ int block_excl_scan_n(int v, int tid, SelShared& sh, int& total) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int inc = wave_incl_scan(v, lane);
+  if (lane == 63) sh.wave_tot[wave] = inc;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < NT / kWave; ++w) {
     const int t = sh.wave_tot[w];
     before += (w < wave) ? t : 0;
     total += t;
@@ -216,13 +236,281 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const SelectParams 
   if (tid == 0) p.count[qid] = max_sel;
 }
 
+// ---------------------------------------------------------------------------
+// Few long rows (decode): the same selection, spread over many workgroups per
+// row.  The radix digits are fixed (bits 30-20, 19-9, 8-0 of the non-negative
+// float32 pattern); each pass is one launch that histograms its segment of
+// the row (LDS, then integer atomics into the row's global histogram, so the
+// counts do not depend on the order).  Every workgroup of a later launch
+// derives the digits picked so far from those histograms itself.  Then one
+// launch counts, per segment, the candidates above tau and equal to tau, and
+// the last one writes each segment's picks at their ascending positions.
+constexpr int MB_THREADS = 256;
+constexpr int MB_PER_THREAD = 16;
+constexpr int MB_SEG = MB_THREADS * MB_PER_THREAD;  // candidates per workgroup
+constexpr int MB_MAX_ROWS = 64;
+constexpr int MB_MIN_CAND = 32768;
+constexpr int MB_BINS = 2048;
+
+struct MbWs {
+  int* hist;     // [rows][3][MB_BINS]
+  int* bcount;   // [rows][nblk][2]: candidates above tau, equal to tau
+  int nblk;
+};
+
+__device__ __forceinline__ int mb_shift(int pass) { return pass == 0 ? 20 : (pass == 1 ? 9 : 0); }
+__device__ __forceinline__ int mb_width(int pass) { return pass == 2 ? 9 : 11; }
+
+struct MbShared {
+  int part[MB_THREADS];
+  int digit, above;
+  int cnt[2 * MB_THREADS / kWave];
+  int lh[MB_BINS];
+};
+
+// Digits of passes 0..npass-1 from the row's histograms: returns the common
+// prefix (bits above the next digit) and how many picks remain inside it.
+__device__ void mb_prefix(const int* hist_row, int npass, int topk, MbShared& sh, uint32_t& prefix, int& krem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  prefix = 0u;
+  krem = topk;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int nb = 1 << mb_width(pass);
+    const int per = nb / MB_THREADS;             // 8 (11-bit digits) or 2 (9-bit)
+    const int* h = hist_row + pass * MB_BINS;
+    // thread t owns digits nb-1-per*t down to nb-per*(t+1): the scan runs from
+    // the top digit down
+    int c = 0;
+    for (int i = 0; i < per; ++i) c += h[nb - 1 - per * tid - i];
+    const int inc = wave_incl_scan(c, lane);
+    if (lane == 63) sh.cnt[wave] = inc;
+    __syncthreads();
+    int before = inc - c;
+    for (int w = 0; w < wave; ++w) before += sh.cnt[w];
+    if (before < krem && krem <= before + c) {   // exactly one thread: the total is >= krem
+      int cum = before, d = nb - 1 - per * tid;
+      for (int i = 0; i < per - 1; ++i, --d) {
+        const int hv = h[d];
+        if (cum + hv >= krem) break;
+        cum += hv;
+      }
+      sh.digit = d;
+      sh.above = cum;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sh.digit << mb_shift(pass);
+    krem -= sh.above;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void mb_zero_kernel(int* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
+}
+
+template <int PASS>
+__global__ __launch_bounds__(MB_THREADS) void mb_hist_kernel(const SelectParams p, const MbWs ws) {
+  __shared__ MbShared sh;
+  const int tid = threadIdx.x, row = blockIdx.y;
+  const int64_t n_cand = p.q_pos0 + row % p.n_q + 1 - p.window;
+  const int64_t s0 = (int64_t)blockIdx.x * MB_SEG;
+  if (n_cand <= p.topk || s0 >= n_cand) return;
+  int* hist_row = ws.hist + (int64_t)row * 3 * MB_BINS;
+  uint32_t prefix;
+  int krem;
+  mb_prefix(hist_row, PASS, p.topk, sh, prefix, krem);
+  for (int b = tid; b < MB_BINS; b += MB_THREADS) sh.lh[b] = 0;
+  __syncthreads();
+  const int sh_lo = mb_shift(PASS), w = mb_width(PASS);
+  const uint32_t want = PASS == 0 ? 0u : prefix >> (sh_lo + w);
+  const float* rowp = p.scores + (int64_t)row * p.ld_scores;
+#pragma unroll
+  for (int r = 0; r < MB_PER_THREAD / 4; ++r) {
+    const int64_t j = s0 + 1024 * r + 4 * tid;
+    uint32_t u[4];
+    if (j + 3 < n_cand) {
+      const f32x4 v = *(const f32x4*)(rowp + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = fbits(v[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = (j + e < n_cand) ? fbits(rowp[j + e]) : 0xFFFFFFFFu;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (u[e] != 0xFFFFFFFFu && (u[e] >> (sh_lo + w)) == want) atomicAdd(&sh.lh[(u[e] >> sh_lo) & ((1 << w) - 1)], 1);
+  }
+  __syncthreads();
+  int* gh = hist_row + PASS * MB_BINS;
+  for (int b = tid; b < (1 << w); b += MB_THREADS)
+    if (sh.lh[b]) atomicAdd(&gh[b], sh.lh[b]);
+}
+
+// Candidates above tau and equal to tau in each segment.
+__global__ __launch_bounds__(MB_THREADS) void mb_count_kernel(const SelectParams p, const MbWs ws) {
+  __shared__ MbShared sh;
+  const int tid = threadIdx.x, row = blockIdx.y;
+  const int64_t n_cand = p.q_pos0 + row % p.n_q + 1 - p.window;
+  const int64_t s0 = (int64_t)blockIdx.x * MB_SEG;
+  if (n_cand <= p.topk || s0 >= n_cand) return;
+  uint32_t tau;
+  int need_eq;
+  mb_prefix(ws.hist + (int64_t)row * 3 * MB_BINS, 3, p.topk, sh, tau, need_eq);
+  const float* rowp = p.scores + (int64_t)row * p.ld_scores;
+  int above = 0, eq = 0;
+#pragma unroll
+  for (int r = 0; r < MB_PER_THREAD / 4; ++r) {
+    const int64_t j = s0 + 1024 * r + 4 * tid;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (j + e < n_cand) {
+        const uint32_t u = fbits(rowp[j + e]);
+        above += u > tau;
+        eq += u == tau;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    above += __shfl_xor(above, o, kWave);
+    eq += __shfl_xor(eq, o, kWave);
+  }
+  if ((tid & 63) == 0) {
+    sh.cnt[2 * (tid >> 6)] = above;
+    sh.cnt[2 * (tid >> 6) + 1] = eq;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int a = 0, q = 0;
+    for (int wv = 0; wv < MB_THREADS / kWave; ++wv) {
+      a += sh.cnt[2 * wv];
+      q += sh.cnt[2 * wv + 1];
+    }
+    int* bc = ws.bcount + ((int64_t)row * ws.nblk + blockIdx.x) * 2;
+    bc[0] = a;
+    bc[1] = q;
+  }
+}
+
+// Each segment writes its picks at their ascending positions; segment 0 also
+// writes the window, the count, and the rows that keep every key.
+__global__ __launch_bounds__(MB_THREADS) void mb_write_kernel(const SelectParams p, const MbWs ws) {
+  __shared__ MbShared sh;
+  __shared__ SelShared ssh;
+  const int tid = threadIdx.x, row = blockIdx.y;
+  const int64_t pos = p.q_pos0 + row % p.n_q;
+  const int64_t n = pos + 1;
+  const int64_t n_cand = n - p.window;
+  const int max_sel = p.window + p.topk;
+  int32_t* out = p.idx + (int64_t)row * max_sel;
+  const int64_t s0 = (int64_t)blockIdx.x * MB_SEG;
+  if (n_cand <= p.topk) {
+    if (blockIdx.x == 0) {
+      for (int j = tid; j < max_sel; j += MB_THREADS) out[j] = j < n ? j : -1;
+      if (tid == 0) p.count[row] = (int32_t)n;
+    }
+    return;
+  }
+  if (blockIdx.x == 0) {
+    for (int w = tid; w < p.window; w += MB_THREADS) out[p.topk + w] = (int32_t)(n_cand + w);
+    if (tid == 0) p.count[row] = max_sel;
+  }
+  if (s0 >= n_cand) return;
+  uint32_t tau;
+  int need_eq;
+  mb_prefix(ws.hist + (int64_t)row * 3 * MB_BINS, 3, p.topk, sh, tau, need_eq);
+  // picks and ties in the segments before this one
+  int sel_before = 0, eq_before = 0;
+  const int* bc = ws.bcount + (int64_t)row * ws.nblk * 2;
+  for (int b = tid; b < (int)blockIdx.x; b += MB_THREADS) {
+    sel_before += bc[2 * b];
+    eq_before += bc[2 * b + 1];
+  }
+  int tot;
+  (void)block_excl_scan_n<MB_THREADS>(sel_before, tid, ssh, tot);
+  sel_before = tot;
+  (void)block_excl_scan_n<MB_THREADS>(eq_before, tid, ssh, tot);
+  eq_before = tot;
+  // ties taken before this segment: the first need_eq ties in index order
+  sel_before += min(eq_before, need_eq);
+  const float* rowp = p.scores + (int64_t)row * p.ld_scores;
+  int eq_seen = eq_before, sel_seen = sel_before;
+#pragma unroll
+  for (int r = 0; r < MB_PER_THREAD / 4; ++r) {
+    const int64_t j0 = s0 + 1024 * r + 4 * tid;
+    uint32_t u[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = (j0 + e < n_cand) ? fbits(rowp[j0 + e]) : 0u;
+    int eq_cnt = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) eq_cnt += (j0 + e < n_cand && u[e] == tau) ? 1 : 0;
+    int eq_total;
+    int eq_rank = eq_seen + block_excl_scan_n<MB_THREADS>(eq_cnt, tid, ssh, eq_total);
+    bool sel[4];
+    int sel_cnt = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool valid = j0 + e < n_cand;
+      const bool gt = valid && u[e] > tau;
+      const bool eq = valid && u[e] == tau;
+      sel[e] = gt || (eq && eq_rank < need_eq);
+      eq_rank += eq ? 1 : 0;
+      sel_cnt += sel[e] ? 1 : 0;
+    }
+    int sel_total;
+    int opos = sel_seen + block_excl_scan_n<MB_THREADS>(sel_cnt, tid, ssh, sel_total);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (sel[e] && opos < p.topk) out[opos++] = (int32_t)(j0 + e);
+    eq_seen += eq_total;
+    sel_seen += sel_total;
+  }
+}
+
+bool select_multi_block(int B, int n_q, int64_t q_pos0, int window) {
+  const int64_t max_cand = q_pos0 + n_q - window;
+  return (int64_t)B * n_q <= MB_MAX_ROWS && max_cand >= MB_MIN_CAND;
+}
+
+size_t mb_layout(int rows, int64_t max_cand, char* base, MbWs* ws) {
+  const int nblk = (int)((max_cand + MB_SEG - 1) / MB_SEG);
+  const size_t hist_bytes = ((size_t)rows * 3 * MB_BINS * 4 + 255) & ~(size_t)255;
+  const size_t cnt_bytes = ((size_t)rows * nblk * 2 * 4 + 255) & ~(size_t)255;
+  if (ws) {
+    ws->hist = (int*)base;
+    ws->bcount = (int*)(base + hist_bytes);
+    ws->nblk = nblk;
+  }
+  return hist_bytes + cnt_bytes;
+}
+
 }  // namespace
 
-size_t select_workspace_bytes(int, int, int64_t, int64_t) { return 0; }
+// Sized for the smallest window (1), which has the most candidates: the launch
+// with the caller's window needs at most this much, or none.
+size_t select_workspace_bytes(int B, int n_q, int64_t /*T*/, int64_t q_pos0) {
+  if (!select_multi_block(B, n_q, q_pos0, 1)) return 0;
+  return mb_layout(B * n_q, q_pos0 + n_q - 1, nullptr, nullptr);
+}
 
-hipError_t launch_select(const SelectParams& p, void*, size_t, hipStream_t stream) {
+hipError_t launch_select(const SelectParams& p, void* ws_ptr, size_t /*ws_bytes*/, hipStream_t stream) {
   if (p.B * p.n_q == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)(p.B * p.n_q)), dim3(SEL_THREADS), 0, stream, p);
+  if (!select_multi_block(p.B, p.n_q, p.q_pos0, p.window)) {
+    hipLaunchKernelGGL(select_kernel, dim3((unsigned)(p.B * p.n_q)), dim3(SEL_THREADS), 0, stream, p);
+    return hipGetLastError();
+  }
+  const int rows = p.B * p.n_q;
+  MbWs ws;
+  mb_layout(rows, p.q_pos0 + p.n_q - p.window, (char*)ws_ptr, &ws);
+  const int64_t nh = (int64_t)rows * 3 * MB_BINS;
+  hipLaunchKernelGGL(mb_zero_kernel, dim3((unsigned)((nh + 255) / 256 < 1024 ? (nh + 255) / 256 : 1024)), dim3(256), 0,
+                     stream, ws.hist, nh);
+  const dim3 grid((unsigned)ws.nblk, (unsigned)rows);
+  hipLaunchKernelGGL(mb_hist_kernel<0>, grid, dim3(MB_THREADS), 0, stream, p, ws);
+  hipLaunchKernelGGL(mb_hist_kernel<1>, grid, dim3(MB_THREADS), 0, stream, p, ws);
+  hipLaunchKernelGGL(mb_hist_kernel<2>, grid, dim3(MB_THREADS), 0, stream, p, ws);
+  hipLaunchKernelGGL(mb_count_kernel, grid, dim3(MB_THREADS), 0, stream, p, ws);
+  hipLaunchKernelGGL(mb_write_kernel, grid, dim3(MB_THREADS), 0, stream, p, ws);
   return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@ constexpr int kRedBytes = (SP_WAVES * 16 * kRedPitch + 2 * SP_WAVES * 16) * 4;
 constexpr int kSmemBytes = (SP_WAVES * kWaveBytes > kRedBytes) ? SP_WAVES * kWaveBytes : kRedBytes;
 
 template <int KV, int H>
-__global__ __launch_bounds__(SP_THREADS) void sparse_attn_kernel(const SparseParams p) {
+__global__ __launch_bounds__(SP_THREADS, 2) void sparse_attn_kernel(const SparseParams p) {
   constexpr int STEP = TileCfg<KV>::STEP;
   constexpr int NMT = STEP / 16;
   constexpr int ROWB = (KV == KV_F32) ? 1024 : (KV == KV_BF16 ? 512 : 256);
