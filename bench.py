@@ -118,8 +118,10 @@ def collect_traffic(args):
         attn = [v for (i, n), v in disp if "prefill_bf16_kernel" in n]
         calib = [v for (i, n), v in disp if "elementwise" in n]
         n_launch = len(range(0, inputs_L(args), min(args.chunk, inputs_L(args))))
-        attn = attn[-n_launch:]                       # the measured step (the warm-up step comes first)
-        res[ctr] = {"attn_kib_per_launch": sum(attn) / len(attn), "calib_kib": calib[-1], "launches": len(attn)}
+        # one full-attention call = the lse dispatch + the P/V dispatch; the
+        # measured step is the last n_launch calls (the warm-up step comes first)
+        attn = attn[-2 * n_launch:]
+        res[ctr] = {"attn_kib_per_launch": sum(attn) / n_launch, "calib_kib": calib[-1], "launches": n_launch}
     # one more pass: MFMA busy cycles of the same launches (utilisation of the matrix cores)
     d = os.path.join(out_root, "sq")
     sq_ctrs = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"]
@@ -141,9 +143,10 @@ def collect_traffic(args):
         sq.setdefault(i, {}).setdefault(row["Counter_Name"], 0.0)
         sq[i][row["Counter_Name"]] += float(row["Counter_Value"])
         dur[i] = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-9
-    last = sorted(sq)[-res["FETCH_SIZE"]["launches"]:]
-    sq_avg = {c: sum(sq[i].get(c, 0.0) for i in last) / len(last) for c in sq_ctrs}
-    dur_avg = sum(dur[i] for i in last) / len(last)
+    n_launch = res["FETCH_SIZE"]["launches"]
+    last = sorted(sq)[-2 * n_launch:]            # both dispatches of each call
+    sq_avg = {c: sum(sq[i].get(c, 0.0) for i in last) / n_launch for c in sq_ctrs}
+    dur_avg = sum(dur[i] for i in last) / n_launch
     # busy cycles of all 1024 SIMDs over the launch at the 2.4 GHz peak clock (a lower bound
     # on the utilisation when the clock runs below peak)
     mfma_util = sq_avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * dur_avg * 2.4e9)
@@ -153,7 +156,8 @@ def collect_traffic(args):
     write_b = res["WRITE_SIZE"]["attn_kib_per_launch"] * 1024.0 * f_write
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
-        f.write("# HBM traffic of the scored full-attention kernel (prefill_bf16_kernel), one launch of the\n")
+        f.write("# HBM traffic of one scored full-attention call (its two dispatches: prefill_bf16_kernel<H,1>,\n")
+        f.write("# the lse pass, and prefill_bf16_kernel<H,2>, the P/V pass), one call of the\n")
         f.write(f"# {args.workload} step ({res['FETCH_SIZE']['launches']} launches of {args.chunk} queries,"
                 " averaged), from rocprofv3 counter passes.\n")
         f.write("# command: python bench.py --collect-traffic   (runs, one pass per counter set:)\n")
@@ -318,7 +322,7 @@ def main():
         "config": {"workload": "prefill_128k", "seq_len": L, "query_heads": H, "kv_heads": 1, "head_dim": D,
                    "window": window, "topk": topk, "sparse_layers": n_sparse, "query_chunk": C,
                    "global_batch": 1, "parallelism": "single GPU"},
-        "roofline": {"kernel": "prefill_kernel (scored full attention)", "bound": "mfma",
+        "roofline": {"kernel": "hs2_full_attn_scored, prefill path (lse dispatch + P/V dispatch)", "bound": "mfma",
                      "achieved": fa_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": fa_tflops / BF16_PEAK_TFLOPS, "traffic": read_traffic(),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",

@@ -321,19 +321,20 @@ hipError_t launch_decode_kv(const AttnParams& p, const DecodeWs& ws, hipStream_t
 
 }  // namespace
 
-hipError_t launch_prefill(const AttnParams& p, int kv_kind, hipStream_t stream);  // attn_prefill.hip
+hipError_t launch_prefill(const AttnParams& p, int kv_kind, void* ws, hipStream_t stream);  // attn_prefill.hip
+size_t prefill_bf16_workspace_bytes(int B, int n_q, int H);                         // attn_prefill_bf16.hip
 
 bool attn_uses_decode(int n_q, int H) { return n_q * H <= 16; }
 
-size_t attn_workspace_bytes(int B, int n_q, int H, int64_t T, int /*kv_kind*/) {
-  if (!attn_uses_decode(n_q, H)) return 0;
+size_t attn_workspace_bytes(int B, int n_q, int H, int64_t T, int kv_kind) {
+  if (!attn_uses_decode(n_q, H)) return kv_kind == KV_F32 ? 0 : prefill_bf16_workspace_bytes(B, n_q, H);
   return decode_ws_layout(B, T, nullptr, nullptr);
 }
 
 hipError_t launch_full_attn(const AttnParams& p, int /*q_kind*/, int kv_kind, void* ws_ptr, size_t /*ws_bytes*/,
                             hipStream_t stream) {
   if (p.B * p.n_q == 0) return hipSuccess;
-  if (!attn_uses_decode(p.n_q, p.H)) return launch_prefill(p, kv_kind, stream);
+  if (!attn_uses_decode(p.n_q, p.H)) return launch_prefill(p, kv_kind, ws_ptr, stream);
   DecodeWs ws;
   decode_ws_layout(p.B, p.T, (char*)ws_ptr, &ws);
   switch (kv_kind) {

@@ -371,11 +371,11 @@ hipError_t launch_prefill_kv(const AttnParams& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t stream);  // attn_prefill_bf16.hip
+hipError_t launch_prefill_bf16(const AttnParams& p, void* ws, hipStream_t stream);  // attn_prefill_bf16.hip
 
-hipError_t launch_prefill(const AttnParams& p, int kv_kind, hipStream_t stream) {
+hipError_t launch_prefill(const AttnParams& p, int kv_kind, void* ws, hipStream_t stream) {
   if (p.B * p.n_q == 0) return hipSuccess;
-  return kv_kind == KV_F32 ? launch_prefill_kv<KV_F32>(p, stream) : launch_prefill_bf16(p, stream);
+  return kv_kind == KV_F32 ? launch_prefill_kv<KV_F32>(p, stream) : launch_prefill_bf16(p, ws, stream);
 }
 
 }  // namespace hs2

@@ -3,24 +3,26 @@
 // Same definition and the same two sweeps as attn_prefill.hip (HySparse2
 // pages, agihunt.info summary: the full layer's exact attention probabilities
 // score the tokens for the sparse layers; per head P_hj = exp(l_hj - lse_h),
-// score_j = sum_h P_hj), laid out for MI355X:
+// score_j = sum_h P_hj), laid out for MI355X as two kernels over the same
+// 256-row workgroups (64 query rows per wave = 64/H tokens x H heads):
 //
-//  * 64 query rows per wave (64/H tokens x H heads), 4 waves = 256 rows per
-//    workgroup, one wave per SIMD.  Every K or V fragment read from LDS feeds
-//    two 32-row MFMA tiles, which halves the LDS bytes per MFMA flop against
-//    32-row waves; the 64 x 256 float32 O accumulator of a wave fills the AGPR
-//    file.  Rows 0..31 of the wave's queries stay in VGPRs, rows 32..63 are
-//    parked in LDS: the freed registers hold operands fetched three MFMA steps
-//    ahead, which is what hides the LDS latency with a single wave per SIMD.
-//  * K/V tiles of 32 keys are double-buffered in LDS and filled with
-//    global_load_lds_dwordx4 (no register staging): the DMA of tile t+1 runs
-//    while tile t is computed, one barrier per tile.  Every buffer is its own
-//    LDS object and the loops are unrolled twice, so that the compiler sees
-//    that reads of one buffer do not depend on the DMA into the other.
-//  * sweep 1: S^T = K Q^T (a lane owns a row, online max/sum in registers,
-//    interleaved with the MFMAs of the next tile);
-//    sweep 2: S = Q K^T (a lane owns a key: float32 P, in-lane head sums for
-//    the scores), P -> LDS [key][row] -> transposed reads -> O += P V.
+//  * prefill_lse: S^T = K Q^T per 32-key tile (a lane owns a row, online
+//    max/sum in registers) -> lse of every row (log2 units, workspace).  It
+//    holds no O accumulator, so two workgroups share a CU and the two waves of
+//    a SIMD hide each other's LDS and MFMA latency; K tiles are triple-buffered.
+//  * prefill_pv: S = Q K^T (a lane owns a key: float32 P from the lse, in-lane
+//    head sums for the scores), P -> LDS [key][row] -> transposed reads ->
+//    O += P V.  The 64 x 256 float32 O accumulator of a wave fills the AGPR
+//    file (one wave per SIMD); rows 0..31 of the wave's queries stay in VGPRs,
+//    rows 32..63 are parked in LDS, and operands are read three MFMA steps
+//    ahead of their use.
+//
+// Both stream K (and V) in 32-key tiles through LDS with global_load_lds_dwordx4
+// (no register staging), one barrier per tile.  Every buffer is its own LDS
+// object and the loops are unrolled over the buffers, so that the compiler
+// sees that reads of one buffer do not depend on the DMA into another.  Every
+// K or V fragment read from LDS feeds two 32-row MFMA tiles, which halves the
+// LDS bytes per MFMA flop against 32-row waves.
 #include <type_traits>
 
 #include "hs2_device.hpp"
@@ -45,15 +47,10 @@ constexpr int PB_VTILE = 17 * 1024;             // 32 x 34 chunks = 17 DMA instr
 constexpr int PB_PP = 144;                      // P buffer pitch (bytes per key)
 constexpr int PB_AHEAD = 3;                     // operand prefetch distance (MFMA steps)
 
-template <int H>
-__global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnParams p) {
+template <int H, int PHASE>   // PHASE 1: prefill_lse, PHASE 2: prefill_pv
+__global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_kernel(const AttnParams p, float* lse2) {
   constexpr int TPW = PB_RW / H;       // tokens per wave
   constexpr int TPB = PB_WAVES * TPW;  // tokens per workgroup
-  __shared__ __attribute__((aligned(1024))) char lds_k0[PB_KTILE], lds_k1[PB_KTILE];
-  __shared__ __attribute__((aligned(1024))) char lds_v0[PB_VTILE], lds_v1[PB_VTILE];
-  __shared__ __attribute__((aligned(1024))) char lds_q[PB_WAVES * 16 * 1024];
-  __shared__ __attribute__((aligned(16))) char lds_p[PB_WAVES * PB_KT * PB_PP];
-  __shared__ __attribute__((aligned(16))) float lds_lse[PB_WAVES * PB_RW];
 
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int hb = l >> 5, l32 = l & 31;
@@ -70,33 +67,19 @@ __global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnP
   const int ntiles = (int)((n_keys + PB_KT - 1) / PB_KT);
   const char* kg = (const char*)p.k + (int64_t)b * p.T * 512;
   const char* vg = (const char*)p.v + (int64_t)b * p.T * 512;
-  char* const pbuf = lds_p + wave * PB_KT * PB_PP;
-  float* const lse_lds = lds_lse + wave * PB_RW;
+  const int64_t q_row0 = ((int64_t)b * p.n_q + tok_w0) * H;   // first query row of this wave
 
   auto tok_of_row = [&](int row) { return tok_w0 + row / H; };
   auto pos_of_row = [&](int row) -> int64_t {
     const int t = tok_of_row(row);
     return p.q_pos0 + (t < p.n_q ? t : p.n_q - 1);
   };
-
-  // ---- queries: rows 32*mt + l32 of this wave, K-step s covers dims 16s..16s+15.
-  // Rows 0..31 stay in registers; rows 32..63 go to LDS as [s][lane] (16 KB per
-  // wave), so that each fragment read is one conflict-free ds_read_b128.
-  const int64_t q_row0 = ((int64_t)b * p.n_q + tok_w0) * H;
-  bf16x8 qf[16];
-  char* const qlds = lds_q + wave * (16 * 1024) + l * 16;
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  // query row 32*mt + l32 of this wave, K-step s: dims 16s + 8hb .. +7
+  auto qload = [&](int mt, int s) -> u32x4 {
     const bool ok = tok_of_row(32 * mt + l32) < p.n_q;
     const bf16* qp = (const bf16*)p.q + (q_row0 + 32 * mt + l32) * kHeadDim + 8 * hb;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const u32x4 v = ok ? *(const u32x4*)(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u};
-      if (mt == 0) qf[s] = as_bf16x8(v);
-      else *(u32x4*)(qlds + s * 1024) = v;
-    }
-  }
-  auto q1frag = [&](int s) -> bf16x8 { return as_bf16x8(*(const u32x4*)(qlds + s * 1024)); };
+    return ok ? *(const u32x4*)(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+  };
 
   // ---- LDS DMA of one 32-key tile into its padded image: the image is cut into
   // 17 wave-instructions of 64 x 16 B (lane l of instruction i fills chunk
@@ -136,327 +119,348 @@ __global__ __launch_bounds__(PB_THREADS, 1) void prefill_bf16_kernel(const AttnP
   struct Pair {
     f32x16 v[2];
   };
-  // S^T = K Q^T of one tile (lane = row l32 (+32), regs = keys)
-  auto s_keys_rows = [&](const char* kb) __attribute__((always_inline)) {
-    Pair st = {{f32x16{}, f32x16{}}};
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const bf16x8 kf = kfrag(kb, s);
-      st.v[0] = mfma32(kf, qf[s], st.v[0]);
-      st.v[1] = mfma32(kf, q1frag(s), st.v[1]);
-    }
-    return st;
-  };
 
-  // =============================== sweep 1: lse per row ===============================
-  float m_run[2] = {kNegInf, kNegInf}, z_run[2] = {0.f, 0.f};
-  const int my_pos[2] = {(int)pos_of_row(l32), (int)pos_of_row(32 + l32)};
-  dma(kg, 0, lds_k0, koff);
-  wait_dma();
-  __syncthreads();
-  if (ntiles > 1) dma(kg, 1, lds_k1, koff);
-  Pair st_c = s_keys_rows(lds_k0);
-  // Online max / sum of one tile (lane: rows l32 and 32 + l32, keys kt*32 +
-  // 8(r/4) + 4hb + r%4).  Tiles left of the diagonal need no causal mask:
-  // that path is the bulk of the work, so it is kept free of selects.
-  auto lse_update = [&](Pair& st, int kt, bool masked) __attribute__((always_inline)) {
-    const int kbase = kt * PB_KT;
+  if constexpr (PHASE == 1) {
+    // =============================== prefill_lse ===============================
+    __shared__ __attribute__((aligned(1024))) char lds_k0[PB_KTILE], lds_k1[PB_KTILE], lds_k2[PB_KTILE];
+    bf16x8 qf[2][16];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int s = 0; s < 16; ++s) qf[mt][s] = as_bf16x8(qload(mt, s));
+    float m_run[2] = {kNegInf, kNegInf}, z_run[2] = {0.f, 0.f};
+    const int my_pos[2] = {(int)pos_of_row(l32), (int)pos_of_row(32 + l32)};
+    // Online max / sum of one tile (lane: rows l32 and 32 + l32, keys kt*32 +
+    // 8(r/4) + 4hb + r%4).  Tiles left of the diagonal need no causal mask:
+    // that path is the bulk of the work, so it is kept free of selects.
+    auto lse_update = [&](Pair& st, int kt, bool masked) __attribute__((always_inline)) {
+      const int kbase = kt * PB_KT;
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        if (!masked) {
+          float tmax = kNegInf;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st.v[n][r]);
+          const float m_new = fmaxf(m_run[n], tmax * p.scale_log2);  // scale > 0: max commutes
+          float acc = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc += fast_exp2(st.v[n][r] * p.scale_log2 - m_new);
+          z_run[n] = z_run[n] * fast_exp2(m_run[n] - m_new) + acc;  // exp2(-inf) = 0 on the first tile
+          m_run[n] = m_new;
+        } else {
+          float tmax = kNegInf;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float x = st.v[n][r] * p.scale_log2;
+            x = (kbase + 8 * (r >> 2) + 4 * hb + (r & 3) <= my_pos[n]) ? x : kNegInf;
+            st.v[n][r] = x;
+            tmax = fmaxf(tmax, x);
+          }
+          const float m_new = fmaxf(m_run[n], tmax);
+          const float m_use = m_new == kNegInf ? 0.f : m_new;  // all masked so far: every term is 0
+          float acc = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc += fast_exp2(st.v[n][r] - m_use);
+          z_run[n] = z_run[n] * fast_exp2(m_run[n] - m_use) + acc;
+          m_run[n] = m_new;
+        }
+      }
+    };
+    // Tile kt sits in kc; K(kt+2) goes to kd, which held K(kt-1).  K(kt+1)
+    // may still be in flight at the wait: each wave keeps its last batch of
+    // DMA instructions (5 for wave 0, 4 for the others) outstanding.
+    auto step1 = [&](int kt, const char* kc, char* kd) __attribute__((always_inline)) {
+      if (kt + 1 < ntiles) {
+        if (wv == 0) __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5)
+        else __builtin_amdgcn_s_waitcnt(0x0F74);           // vmcnt(4)
+      } else {
+        wait_dma();
+      }
+      __syncthreads();
+      if (kt + 2 < ntiles) dma(kg, kt + 2, kd, koff);
+      Pair st = {{f32x16{}, f32x16{}}};
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const bf16x8 kf = kfrag(kc, s);
+        st.v[0] = mfma32(kf, qf[0][s], st.v[0]);
+        st.v[1] = mfma32(kf, qf[1][s], st.v[1]);
+      }
+      lse_update(st, kt, (int64_t)kt * PB_KT + PB_KT - 1 > pos_first);
+    };
+    dma(kg, 0, lds_k0, koff);
+    if (ntiles > 1) dma(kg, 1, lds_k1, koff);
+    {
+      int kt = 0;
+      for (; kt + 2 < ntiles; kt += 3) {
+        step1(kt, lds_k0, lds_k2);
+        step1(kt + 1, lds_k1, lds_k0);
+        step1(kt + 2, lds_k2, lds_k1);
+      }
+      if (kt < ntiles) step1(kt, lds_k0, lds_k2);
+      if (kt + 1 < ntiles) step1(kt + 1, lds_k1, lds_k0);
+    }
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-      if (!masked) {
-        float tmax = kNegInf;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st.v[n][r]);
-        const float m_new = fmaxf(m_run[n], tmax * p.scale_log2);  // scale > 0: max commutes
-        float acc = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc += fast_exp2(st.v[n][r] * p.scale_log2 - m_new);
-        z_run[n] = z_run[n] * fast_exp2(m_run[n] - m_new) + acc;  // exp2(-inf) = 0 on the first tile
-        m_run[n] = m_new;
-      } else {
-        float tmax = kNegInf;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = st.v[n][r] * p.scale_log2;
-          x = (kbase + 8 * (r >> 2) + 4 * hb + (r & 3) <= my_pos[n]) ? x : kNegInf;
-          st.v[n][r] = x;
-          tmax = fmaxf(tmax, x);
-        }
-        const float m_new = fmaxf(m_run[n], tmax);
-        const float m_use = m_new == kNegInf ? 0.f : m_new;  // all masked so far: every term is 0
-        float acc = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc += fast_exp2(st.v[n][r] - m_use);
-        z_run[n] = z_run[n] * fast_exp2(m_run[n] - m_use) + acc;
-        m_run[n] = m_new;
+      const float mo = shfl_xor(m_run[n], 32), zo = shfl_xor(z_run[n], 32);
+      const float m = fmaxf(m_run[n], mo);
+      const float z = (m_run[n] == kNegInf ? 0.f : z_run[n] * fast_exp2(m_run[n] - m)) +
+                      (mo == kNegInf ? 0.f : zo * fast_exp2(mo - m));
+      if (hb == 0 && tok_of_row(32 * n + l32) < p.n_q) {
+        const float l2 = m + fast_log2(z);
+        lse2[q_row0 + 32 * n + l32] = l2;
+        if (p.lse) p.lse[q_row0 + 32 * n + l32] = l2 * kLn2;
       }
     }
-  };
-  // kd: buffer of tile kt (refilled with tile kt+2), kn: buffer of tile kt+1.
-  // While the VALU works on the max / sum of tile kt, the MFMA unit computes
-  // the logits of tile kt+1; the logits of the tile after the last are
-  // computed from a stale buffer and never used, which keeps the loop body
-  // straight-line.
-  auto step1 = [&](int kt, char* kd, const char* kn) __attribute__((always_inline)) {
-    wait_dma();
-    __syncthreads();
-    if (kt + 2 < ntiles) dma(kg, kt + 2, kd, koff);
-    const bool need_mask = (int64_t)kt * PB_KT + PB_KT - 1 > pos_first;
-    Pair st_n;
-    if (!need_mask) {
-      st_n = s_keys_rows(kn);
-      lse_update(st_c, kt, false);
-      // issue order: MFMA, operand read, VALU, MFMA, operand read, VALU, ...
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);
-      }
-    } else {
-      st_n = s_keys_rows(kn);
-      lse_update(st_c, kt, true);
-    }
-    st_c = st_n;
-  };
-  {
-    int kt = 0;
-    for (; kt + 1 < ntiles; kt += 2) {
-      step1(kt, lds_k0, lds_k1);
-      step1(kt + 1, lds_k1, lds_k0);
-    }
-    if (kt < ntiles) step1(kt, lds_k0, lds_k1);
-  }
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const float mo = shfl_xor(m_run[n], 32), zo = shfl_xor(z_run[n], 32);
-    const float m = fmaxf(m_run[n], mo);
-    const float z = (m_run[n] == kNegInf ? 0.f : z_run[n] * fast_exp2(m_run[n] - m)) +
-                    (mo == kNegInf ? 0.f : zo * fast_exp2(mo - m));
-    if (hb == 0) lse_lds[32 * n + l32] = m + fast_log2(z);
-  }
-  __syncthreads();
-
-  // =============================== sweep 2: P, scores, O ===============================
-  f32x16 oacc[2][8];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int n = 0; n < 8; ++n) oacc[mt][n] = f32x16{};
-  float* srow_base = p.scores + (int64_t)b * p.n_q * p.ld_scores;
-  // S = Q K^T (lane = key l32, regs = rows), operands PB_AHEAD steps ahead.
-  auto s_rows_keys = [&](const char* kb) __attribute__((always_inline)) {
-    Pair sa = {{f32x16{}, f32x16{}}};
-    bf16x8 kf[16], q1[16];
-#pragma unroll
-    for (int s = 0; s < PB_AHEAD; ++s) {
-      kf[s] = kfrag(kb, s);
-      q1[s] = q1frag(s);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    // =============================== prefill_pv ===============================
+    __shared__ __attribute__((aligned(1024))) char lds_k0[PB_KTILE], lds_k1[PB_KTILE];
+    __shared__ __attribute__((aligned(1024))) char lds_v0[PB_VTILE], lds_v1[PB_VTILE];
+    __shared__ __attribute__((aligned(1024))) char lds_q[PB_WAVES * 16 * 1024];
+    __shared__ __attribute__((aligned(16))) char lds_p[PB_WAVES * PB_KT * PB_PP];
+    __shared__ __attribute__((aligned(16))) float lds_lse[PB_WAVES * PB_RW];
+    char* const pbuf = lds_p + wave * PB_KT * PB_PP;
+    float* const lse_lds = lds_lse + wave * PB_RW;
+    // Rows 0..31 stay in registers; rows 32..63 go to LDS as [s][lane] (16 KB
+    // per wave), so that each fragment read is one conflict-free ds_read_b128.
+    bf16x8 qf[16];
+    char* const qlds = lds_q + wave * (16 * 1024) + l * 16;
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
-      sa.v[0] = mfma32(qf[s], kf[s], sa.v[0]);
-      if (s + PB_AHEAD < 16) kf[s + PB_AHEAD] = kfrag(kb, s + PB_AHEAD);
-      sa.v[1] = mfma32(q1[s], kf[s], sa.v[1]);
-      if (s + PB_AHEAD < 16) q1[s + PB_AHEAD] = q1frag(s + PB_AHEAD);
-      __builtin_amdgcn_sched_barrier(0);
+      qf[s] = as_bf16x8(qload(0, s));
+      *(u32x4*)(qlds + s * 1024) = qload(1, s);
     }
-    return sa;
-  };
-
-  // probabilities of tile kt (lane: key kbase + l32, rows 32mt + 8(r/4) + 4hb + r%4),
-  // the score of each token of the lane's key, and P (bf16) -> LDS [key][row]
-  auto probs = [&](Pair& sa, int kt, char* pb, float (&sc)[2][2], auto masked) __attribute__((always_inline)) {
-    constexpr bool need_mask = decltype(masked)::value;
-    const int64_t kbase = (int64_t)kt * PB_KT;
-    const int64_t key = kbase + l32;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 l4 = *(const f32x4*)(lse_lds + 32 * mt + 8 * q + 4 * hb);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * q + j;
-          const float e = fast_exp2(sa.v[mt][r] * p.scale_log2 - l4[j]);
-          if constexpr (need_mask)
-            sa.v[mt][r] = key <= pos_of_row(32 * mt + 8 * q + 4 * hb + j) ? e : 0.f;
-          else
-            sa.v[mt][r] = e;
-        }
-      }
-      if constexpr (H == 16) {
-        float t0 = 0.f, t1 = 0.f;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          t0 += sa.v[mt][r];
-          t1 += sa.v[mt][8 + r];
-        }
-        sc[mt][0] = halfwave_pair_sum(t0, t1);
-      } else if constexpr (H == 8) {
-        float t[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) t[q] = sa.v[mt][4 * q] + sa.v[mt][4 * q + 1] + sa.v[mt][4 * q + 2] + sa.v[mt][4 * q + 3];
-        sc[mt][0] = halfwave_pair_sum(t[0], t[1]);
-        sc[mt][1] = halfwave_pair_sum(t[2], t[3]);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bf16x4 v4;
-        v4[0] = to_bf16(sa.v[mt][4 * q]);
-        v4[1] = to_bf16(sa.v[mt][4 * q + 1]);
-        v4[2] = to_bf16(sa.v[mt][4 * q + 2]);
-        v4[3] = to_bf16(sa.v[mt][4 * q + 3]);
-        *(bf16x4*)(pb + l32 * PB_PP + (32 * mt + 8 * q + 4 * hb) * 2) = v4;
-      }
+    auto q1frag = [&](int s) -> bf16x8 { return as_bf16x8(*(const u32x4*)(qlds + s * 1024)); };
+    // lse of the wave's rows (log2 units); rows past the last token read row 0's
+    if (l < PB_RW) {
+      const int64_t r = tok_of_row(l) < p.n_q ? q_row0 + l : q_row0;
+      lse_lds[l] = lse2[r];
     }
-  };
-  // scores of tile kt to global memory (token sums of 32/H tokens per 32-row tile)
-  auto store_scores = [&](const Pair& sa, int kt, const float (&sc)[2][2]) __attribute__((always_inline)) {
-    const int64_t key = (int64_t)kt * PB_KT + l32;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      auto put = [&](int row_in_tile0, float val) {
-        const int tok = tok_of_row(32 * mt + row_in_tile0);
-        if (tok < p.n_q && key <= p.q_pos0 + tok) srow_base[(int64_t)tok * p.ld_scores + key] = val;
-      };
-      if constexpr (H == 16) {
-        put(16 * hb, sc[mt][0]);
-      } else if constexpr (H == 8) {
-        put(8 * hb, sc[mt][0]);
-        put(16 + 8 * hb, sc[mt][1]);
-      } else if constexpr (H == 4) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          put(8 * q + 4 * hb, sa.v[mt][4 * q] + sa.v[mt][4 * q + 1] + sa.v[mt][4 * q + 2] + sa.v[mt][4 * q + 3]);
-      } else if constexpr (H == 2) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-            put(8 * q + 4 * hb + 2 * jj, sa.v[mt][4 * q + 2 * jj] + sa.v[mt][4 * q + 2 * jj + 1]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) put(8 * (r >> 2) + 4 * hb + (r & 3), sa.v[mt][r]);
-      }
-    }
-  };
-  // O += P V for one tile (A = P rows x keys, B = V keys x dims, both via
-  // transposed reads).  Step j = (ks, n) = (j / 8, j % 8); the V fragment of
-  // step j is read PB_AHEAD steps before it is used, P of K-step 1 at step 4.
-  auto pv = [&](const char* pb, const char* vb) __attribute__((always_inline)) {
-    bf16x8 a[2][2], bv[16];
-    auto read_a = [&](int ks) {
-      const int krow = 16 * ks + 8 * (G >> 1) + (s16 >> 2);
-      const int off = 16 * (G & 1) + 4 * (s16 & 3);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16* pa = (const bf16*)(pb + krow * PB_PP) + 32 * mt + off;
-        a[ks][mt] = cat8(lds_tr16(pa), lds_tr16(pa + 4 * (PB_PP / 2)));
-      }
-    };
-    auto read_b = [&](int j) {
-      const int ks = j >> 3, n = j & 7;
-      const int krow = 16 * ks + 8 * (G >> 1) + (s16 >> 2);
-      const int off = 16 * (G & 1) + 4 * (s16 & 3);
-      const bf16* vrow = (const bf16*)(vb + krow * (PB_VC * 16)) + off;
-      bv[j] = cat8(lds_tr16(vrow + 32 * n), lds_tr16(vrow + 4 * (PB_VC * 8) + 32 * n));
-    };
-    read_a(0);
-#pragma unroll
-    for (int j = 0; j < PB_AHEAD; ++j) read_b(j);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int ks = j >> 3, n = j & 7;
-      oacc[0][n] = mfma32(a[ks][0], bv[j], oacc[0][n]);
-      if (j + PB_AHEAD < 16) read_b(j + PB_AHEAD);
-      oacc[1][n] = mfma32(a[ks][1], bv[j], oacc[1][n]);
-      if (j == 4) read_a(1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // Sweep 2: per tile, S -> P (float32 -> scores, bf16 -> LDS) -> O += P V.
-  // K and V of the next tile are fetched while this one is computed.  With
-  // H >= 8 the scores of a tile are two (four) floats per lane; they are
-  // written one tile late, right after the DMA issue, so that the stores have
-  // long completed when the next wait on the vector-memory counter comes.
-  float sc_prev[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-  auto step2 = [&](int kt, const char* kc, const char* vc, char* kn, char* vn) __attribute__((always_inline)) {
-    wait_dma();
     __syncthreads();
-    if (kt + 1 < ntiles) {
-      dma(kg, kt + 1, kn, koff);
-      dma(vg, kt + 1, vn, voff);
-    }
-    if constexpr (H >= 8) {
-      if (kt > 0) store_scores(Pair{}, kt - 1, sc_prev);
-    }
-    Pair sa = s_rows_keys(kc);
-    float sc[2][2];
-    // tiles left of the diagonal need no causal mask (uniform branch)
-    if ((int64_t)kt * PB_KT + PB_KT - 1 > pos_first)
-      probs(sa, kt, pbuf, sc, std::true_type{});
-    else
-      probs(sa, kt, pbuf, sc, std::false_type{});
-    if constexpr (H >= 8) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) sc_prev[mt][0] = sc[mt][0], sc_prev[mt][1] = sc[mt][1];
-    } else {
-      store_scores(sa, kt, sc);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_sched_barrier(0);
-    pv(pbuf, vc);
-  };
-  dma(kg, 0, lds_k0, koff);
-  dma(vg, 0, lds_v0, voff);
-  {
-    int kt = 0;
-    for (; kt + 1 < ntiles; kt += 2) {
-      step2(kt, lds_k0, lds_v0, lds_k1, lds_v1);
-      step2(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
-    }
-    if (kt < ntiles) step2(kt, lds_k0, lds_v0, lds_k1, lds_v1);
-  }
-  if constexpr (H >= 8) store_scores(Pair{}, ntiles - 1, sc_prev);
 
-  // ---- outputs: lane holds O[32mt + 8(r/4) + 4hb + r%4][32n + l32]
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 32 * mt + 8 * (r >> 2) + 4 * hb + (r & 3);
-      if (tok_of_row(row) >= p.n_q) continue;
-      bf16* orow = (bf16*)p.o + (q_row0 + row) * kHeadDim;
-#pragma unroll
-      for (int n = 0; n < 8; ++n) orow[32 * n + l32] = to_bf16(oacc[mt][n][r]);
+    // =============================== sweep 2: P, scores, O ===============================
+    f32x16 oacc[2][8];
+  #pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+  #pragma unroll
+      for (int n = 0; n < 8; ++n) oacc[mt][n] = f32x16{};
+    float* srow_base = p.scores + (int64_t)b * p.n_q * p.ld_scores;
+    // S = Q K^T (lane = key l32, regs = rows), operands PB_AHEAD steps ahead.
+    auto s_rows_keys = [&](const char* kb) __attribute__((always_inline)) {
+      Pair sa = {{f32x16{}, f32x16{}}};
+      bf16x8 kf[16], q1[16];
+  #pragma unroll
+      for (int s = 0; s < PB_AHEAD; ++s) {
+        kf[s] = kfrag(kb, s);
+        q1[s] = q1frag(s);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        sa.v[0] = mfma32(qf[s], kf[s], sa.v[0]);
+        if (s + PB_AHEAD < 16) kf[s + PB_AHEAD] = kfrag(kb, s + PB_AHEAD);
+        sa.v[1] = mfma32(q1[s], kf[s], sa.v[1]);
+        if (s + PB_AHEAD < 16) q1[s + PB_AHEAD] = q1frag(s + PB_AHEAD);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return sa;
+    };
+
+    // probabilities of tile kt (lane: key kbase + l32, rows 32mt + 8(r/4) + 4hb + r%4),
+    // the score of each token of the lane's key, and P (bf16) -> LDS [key][row]
+    auto probs = [&](Pair& sa, int kt, char* pb, float (&sc)[2][2], auto masked) __attribute__((always_inline)) {
+      constexpr bool need_mask = decltype(masked)::value;
+      const int64_t kbase = (int64_t)kt * PB_KT;
+      const int64_t key = kbase + l32;
+  #pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 l4 = *(const f32x4*)(lse_lds + 32 * mt + 8 * q + 4 * hb);
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = 4 * q + j;
+            const float e = fast_exp2(sa.v[mt][r] * p.scale_log2 - l4[j]);
+            if constexpr (need_mask)
+              sa.v[mt][r] = key <= pos_of_row(32 * mt + 8 * q + 4 * hb + j) ? e : 0.f;
+            else
+              sa.v[mt][r] = e;
+          }
+        }
+        if constexpr (H == 16) {
+          float t0 = 0.f, t1 = 0.f;
+  #pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            t0 += sa.v[mt][r];
+            t1 += sa.v[mt][8 + r];
+          }
+          sc[mt][0] = halfwave_pair_sum(t0, t1);
+        } else if constexpr (H == 8) {
+          float t[4];
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) t[q] = sa.v[mt][4 * q] + sa.v[mt][4 * q + 1] + sa.v[mt][4 * q + 2] + sa.v[mt][4 * q + 3];
+          sc[mt][0] = halfwave_pair_sum(t[0], t[1]);
+          sc[mt][1] = halfwave_pair_sum(t[2], t[3]);
+        }
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bf16x4 v4;
+          v4[0] = to_bf16(sa.v[mt][4 * q]);
+          v4[1] = to_bf16(sa.v[mt][4 * q + 1]);
+          v4[2] = to_bf16(sa.v[mt][4 * q + 2]);
+          v4[3] = to_bf16(sa.v[mt][4 * q + 3]);
+          *(bf16x4*)(pb + l32 * PB_PP + (32 * mt + 8 * q + 4 * hb) * 2) = v4;
+        }
+      }
+    };
+    // scores of tile kt to global memory (token sums of 32/H tokens per 32-row tile)
+    auto store_scores = [&](const Pair& sa, int kt, const float (&sc)[2][2]) __attribute__((always_inline)) {
+      const int64_t key = (int64_t)kt * PB_KT + l32;
+  #pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        auto put = [&](int row_in_tile0, float val) {
+          const int tok = tok_of_row(32 * mt + row_in_tile0);
+          if (tok < p.n_q && key <= p.q_pos0 + tok) srow_base[(int64_t)tok * p.ld_scores + key] = val;
+        };
+        if constexpr (H == 16) {
+          put(16 * hb, sc[mt][0]);
+        } else if constexpr (H == 8) {
+          put(8 * hb, sc[mt][0]);
+          put(16 + 8 * hb, sc[mt][1]);
+        } else if constexpr (H == 4) {
+  #pragma unroll
+          for (int q = 0; q < 4; ++q)
+            put(8 * q + 4 * hb, sa.v[mt][4 * q] + sa.v[mt][4 * q + 1] + sa.v[mt][4 * q + 2] + sa.v[mt][4 * q + 3]);
+        } else if constexpr (H == 2) {
+  #pragma unroll
+          for (int q = 0; q < 4; ++q)
+  #pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+              put(8 * q + 4 * hb + 2 * jj, sa.v[mt][4 * q + 2 * jj] + sa.v[mt][4 * q + 2 * jj + 1]);
+        } else {
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) put(8 * (r >> 2) + 4 * hb + (r & 3), sa.v[mt][r]);
+        }
+      }
+    };
+    // O += P V for one tile (A = P rows x keys, B = V keys x dims, both via
+    // transposed reads).  Step j = (ks, n) = (j / 8, j % 8); the V fragment of
+    // step j is read PB_AHEAD steps before it is used, P of K-step 1 at step 4.
+    auto pv = [&](const char* pb, const char* vb) __attribute__((always_inline)) {
+      bf16x8 a[2][2], bv[16];
+      auto read_a = [&](int ks) {
+        const int krow = 16 * ks + 8 * (G >> 1) + (s16 >> 2);
+        const int off = 16 * (G & 1) + 4 * (s16 & 3);
+  #pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const bf16* pa = (const bf16*)(pb + krow * PB_PP) + 32 * mt + off;
+          a[ks][mt] = cat8(lds_tr16(pa), lds_tr16(pa + 4 * (PB_PP / 2)));
+        }
+      };
+      auto read_b = [&](int j) {
+        const int ks = j >> 3, n = j & 7;
+        const int krow = 16 * ks + 8 * (G >> 1) + (s16 >> 2);
+        const int off = 16 * (G & 1) + 4 * (s16 & 3);
+        const bf16* vrow = (const bf16*)(vb + krow * (PB_VC * 16)) + off;
+        bv[j] = cat8(lds_tr16(vrow + 32 * n), lds_tr16(vrow + 4 * (PB_VC * 8) + 32 * n));
+      };
+      read_a(0);
+  #pragma unroll
+      for (int j = 0; j < PB_AHEAD; ++j) read_b(j);
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int ks = j >> 3, n = j & 7;
+        oacc[0][n] = mfma32(a[ks][0], bv[j], oacc[0][n]);
+        if (j + PB_AHEAD < 16) read_b(j + PB_AHEAD);
+        oacc[1][n] = mfma32(a[ks][1], bv[j], oacc[1][n]);
+        if (j == 4) read_a(1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    // Sweep 2: per tile, S -> P (float32 -> scores, bf16 -> LDS) -> O += P V.
+    // K and V of the next tile are fetched while this one is computed.  With
+    // H >= 8 the scores of a tile are two (four) floats per lane; they are
+    // written one tile late, right after the DMA issue, so that the stores have
+    // long completed when the next wait on the vector-memory counter comes.
+    float sc_prev[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    auto step2 = [&](int kt, const char* kc, const char* vc, char* kn, char* vn) __attribute__((always_inline)) {
+      wait_dma();
+      __syncthreads();
+      if (kt + 1 < ntiles) {
+        dma(kg, kt + 1, kn, koff);
+        dma(vg, kt + 1, vn, voff);
+      }
+      if constexpr (H >= 8) {
+        if (kt > 0) store_scores(Pair{}, kt - 1, sc_prev);
+      }
+      Pair sa = s_rows_keys(kc);
+      float sc[2][2];
+      // tiles left of the diagonal need no causal mask (uniform branch)
+      if ((int64_t)kt * PB_KT + PB_KT - 1 > pos_first)
+        probs(sa, kt, pbuf, sc, std::true_type{});
+      else
+        probs(sa, kt, pbuf, sc, std::false_type{});
+      if constexpr (H >= 8) {
+  #pragma unroll
+        for (int mt = 0; mt < 2; ++mt) sc_prev[mt][0] = sc[mt][0], sc_prev[mt][1] = sc[mt][1];
+      } else {
+        store_scores(sa, kt, sc);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_sched_barrier(0);
+      pv(pbuf, vc);
+    };
+    dma(kg, 0, lds_k0, koff);
+    dma(vg, 0, lds_v0, voff);
+    {
+      int kt = 0;
+      for (; kt + 1 < ntiles; kt += 2) {
+        step2(kt, lds_k0, lds_v0, lds_k1, lds_v1);
+        step2(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+      }
+      if (kt < ntiles) step2(kt, lds_k0, lds_v0, lds_k1, lds_v1);
     }
-  if (p.lse && hb == 0) {
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-      if (tok_of_row(32 * n + l32) < p.n_q) p.lse[q_row0 + 32 * n + l32] = lse_lds[32 * n + l32] * kLn2;
+    if constexpr (H >= 8) store_scores(Pair{}, ntiles - 1, sc_prev);
+
+    // ---- outputs: lane holds O[32mt + 8(r/4) + 4hb + r%4][32n + l32]
+  #pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * mt + 8 * (r >> 2) + 4 * hb + (r & 3);
+        if (tok_of_row(row) >= p.n_q) continue;
+        bf16* orow = (bf16*)p.o + (q_row0 + row) * kHeadDim;
+  #pragma unroll
+        for (int n = 0; n < 8; ++n) orow[32 * n + l32] = to_bf16(oacc[mt][n][r]);
+      }
   }
 }
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t stream) {
-  const int tpb = PB_WAVES * PB_RW / p.H;
+size_t prefill_bf16_workspace_bytes(int B, int n_q, int H) {
+  return ((size_t)B * n_q * H * 4 + 255) & ~(size_t)255;   // lse of every row, log2 units
+}
+
+template <int H>
+hipError_t launch_prefill_bf16_h(const AttnParams& p, float* lse2, hipStream_t stream) {
+  const int tpb = PB_WAVES * PB_RW / H;
   const unsigned nblk = (unsigned)(p.B * ((p.n_q + tpb - 1) / tpb));
-  switch (p.H) {
-    case 1: hipLaunchKernelGGL(prefill_bf16_kernel<1>, dim3(nblk), dim3(PB_THREADS), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(prefill_bf16_kernel<2>, dim3(nblk), dim3(PB_THREADS), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(prefill_bf16_kernel<4>, dim3(nblk), dim3(PB_THREADS), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL(prefill_bf16_kernel<8>, dim3(nblk), dim3(PB_THREADS), 0, stream, p); break;
-    default: hipLaunchKernelGGL(prefill_bf16_kernel<16>, dim3(nblk), dim3(PB_THREADS), 0, stream, p); break;
-  }
+  hipLaunchKernelGGL((prefill_bf16_kernel<H, 1>), dim3(nblk), dim3(PB_THREADS), 0, stream, p, lse2);
+  hipLaunchKernelGGL((prefill_bf16_kernel<H, 2>), dim3(nblk), dim3(PB_THREADS), 0, stream, p, lse2);
   return hipGetLastError();
+}
+
+hipError_t launch_prefill_bf16(const AttnParams& p, void* ws, hipStream_t stream) {
+  float* lse2 = (float*)ws;
+  switch (p.H) {
+    case 1: return launch_prefill_bf16_h<1>(p, lse2, stream);
+    case 2: return launch_prefill_bf16_h<2>(p, lse2, stream);
+    case 4: return launch_prefill_bf16_h<4>(p, lse2, stream);
+    case 8: return launch_prefill_bf16_h<8>(p, lse2, stream);
+    default: return launch_prefill_bf16_h<16>(p, lse2, stream);
+  }
 }
 
 }  // namespace hs2
