@@ -92,6 +92,13 @@ int hs2_full_attn_scored(const void* q, int q_dtype, int B, int n_q, int H, int 
                          void* o, float* lse, float* scores, int64_t ld_scores,
                          void* workspace, size_t ws_bytes, void* stream);
 
+/* Workspace of hs2_full_attn_scored for these shapes:
+ *   decode (n_q * H <= 16): float32 logits of every key and row plus the
+ *     partial softmax states of the key chunks (about B * T * 64 bytes);
+ *   bf16 prefill: the lse of every row in log2 units (B * n_q * H * 4 bytes),
+ *     written by the lse pass and read by the probability pass;
+ *   float32 prefill: none (0).
+ * The contents are scratch; calls that share a workspace must not overlap. */
 size_t hs2_full_attn_workspace_bytes(int B, int n_q, int H, int64_t T, int kv_dtype);
 
 /*

@@ -74,6 +74,7 @@ def test_workspace_sizes(lib):
     big = lib.hs2_full_attn_workspace_bytes(1, 1, 16, 1 << 20, FP8)
     assert big >= (1 << 20) * 16 * 4
     assert lib.hs2_full_attn_workspace_bytes(1, 2048, 4, 2048, F32) == 0
+    assert lib.hs2_full_attn_workspace_bytes(1, 32768, 16, 131072, BF16) >= 32768 * 16 * 4   # lse pass -> P/V pass
     assert lib.hs2_full_attn_workspace_bytes(16, 1, 16, 32768, BF16) >= 16 * 32768 * 16 * 4
     assert lib.hs2_bridge_workspace_bytes(4, 2048, 256) == 0
     # few long rows (decode) use the multi-workgroup selector: histograms + per-segment counts
