@@ -11,7 +11,8 @@
 // above tau plus the first (topk - #above) candidates equal to tau in index
 // order, followed by the window; this is already ascending.
 //
-// Design: one 1024-thread workgroup per query row.  Scores are >= 0, so their
+// Design: one 1024-thread workgroup per query row.  Usually the row is read
+// once (sampled path below); otherwise, as a fallback:  scores are >= 0, so their
 // float32 bit patterns order like unsigned integers.  A first pass finds the
 // smallest and largest candidate pattern; the bits above their highest
 // differing bit are common to all candidates, so the radix digits (11 bits,
@@ -87,8 +88,62 @@ __device__ __forceinline__ int block_excl_scan_n(int v, int tid, SelShared& sh, 
   return before + inc - v;
 }
 
+// ---- sampled single-read path (the common case) ----------------------------
+// Rows up to SEL_CAP candidates, and rows whose candidates at or above a
+// threshold estimated from a strided sample number between topk and SEL_CAP,
+// are selected from one read of the row: the candidates at or above the
+// estimate are compacted into LDS in index order, and tau is found there.
+// Anything else (a sample that misleads, e.g. many equal scores) falls back to
+// the exact multi-pass radix below, so the result never depends on the sample.
+constexpr int SEL_CAP = 8192;      // candidates kept in LDS (64 KB)
+constexpr int SEL_SAMPLE = 4096;   // strided sample of a long row
+
+// The k-th largest of the n bit patterns v[0..n-1] in LDS (k >= 1, n >= k):
+// returns tau and how many of the values equal to tau rank inside the top k.
+__device__ void lds_radix_select(const uint32_t* v, int n, int k, SelShared& sh, uint32_t& tau, int& need_eq) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0u;
+  int krem = k;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int w = pass == 2 ? 10 : 11;
+    const int nbins = 1 << w;
+    // 64-bit shifts: shift + w is 32 on the first pass
+    const uint64_t want = (uint64_t)prefix >> (shift + w);
+    for (int b = tid; b < nbins; b += SEL_THREADS) sh.hist[b] = 0;
+    __syncthreads();
+    for (int j = tid; j < n; j += SEL_THREADS) {
+      const uint32_t u = v[j];
+      if (((uint64_t)u >> (shift + w)) == want) atomicAdd(&sh.hist[(u >> shift) & (nbins - 1)], 1);
+    }
+    __syncthreads();
+    const int d0 = nbins - 1 - 2 * tid, d1 = d0 - 1;
+    const int c0 = d0 >= 0 ? sh.hist[d0] : 0;
+    const int c1 = d1 >= 0 ? sh.hist[d1] : 0;
+    int total;
+    const int before = block_excl_scan(c0 + c1, tid, sh, total);
+    if (d0 >= 0) {
+      if (before < krem && krem <= before + c0) {
+        sh.pick_digit = d0;
+        sh.pick_above = before;
+      } else if (d1 >= 0 && before + c0 < krem && krem <= before + c0 + c1) {
+        sh.pick_digit = d1;
+        sh.pick_above = before + c0;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sh.pick_digit << shift;
+    krem -= sh.pick_above;
+    __syncthreads();
+  }
+  tau = prefix;
+  need_eq = krem;
+}
+
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const SelectParams p) {
   __shared__ SelShared sh;
+  __shared__ uint32_t cval[SEL_CAP];
+  __shared__ int32_t cidx[SEL_CAP];
   const int tid = threadIdx.x;
   const int qid = xcd_remap(blockIdx.x, gridDim.x);
   const int i = qid % p.n_q;
@@ -104,6 +159,84 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const SelectParams 
     if (tid == 0) p.count[qid] = (int32_t)n;
     return;
   }
+
+  // ---- sampled path: threshold estimate (0 = keep everything for short rows)
+  uint32_t u_est = 0u;
+  if (n_cand > SEL_CAP) {
+    for (int i = tid; i < SEL_SAMPLE; i += SEL_THREADS) cval[i] = fbits(row[(int64_t)i * n_cand / SEL_SAMPLE]);
+    __syncthreads();
+    // aim at about 2 topk candidates at or above the estimate
+    const int r = (int)min<int64_t>(SEL_SAMPLE, max<int64_t>(1, (2 * (int64_t)p.topk * SEL_SAMPLE + n_cand - 1) / n_cand));
+    int unused;
+    lds_radix_select(cval, SEL_SAMPLE, r, sh, u_est, unused);
+  }
+  // one read of the row: candidates >= u_est into LDS, in index order.  Each
+  // thread takes 16 consecutive candidates per round (one block scan per 16K
+  // candidates), and the loads of the next round are issued before the scan.
+  constexpr int PER = 16;
+  auto load16 = [&](int64_t j0, uint32_t (&u)[PER]) {
+    if (j0 + PER - 1 < n_cand) {
+#pragma unroll
+      for (int q = 0; q < PER / 4; ++q) {
+        const f32x4 v = *(const f32x4*)(row + j0 + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[4 * q + e] = fbits(v[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) u[e] = (j0 + e < n_cand) ? fbits(row[j0 + e]) : 0u;
+    }
+  };
+  int kept = 0;
+  uint32_t ucur[PER], unext[PER];
+  load16(PER * (int64_t)tid, ucur);
+  for (int64_t base = 0; base < n_cand; base += PER * SEL_THREADS) {
+    const int64_t j0 = base + PER * (int64_t)tid;
+    if (base + PER * SEL_THREADS < n_cand) load16(j0 + PER * SEL_THREADS, unext);
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) c += (j0 + e < n_cand && ucur[e] >= u_est) ? 1 : 0;
+    int tot;
+    int pos = kept + block_excl_scan(c, tid, sh, tot);
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      if (j0 + e < n_cand && ucur[e] >= u_est) {
+        if (pos < SEL_CAP) {
+          cval[pos] = ucur[e];
+          cidx[pos] = (int32_t)(j0 + e);
+        }
+        ++pos;
+      }
+    kept += tot;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) ucur[e] = unext[e];
+  }
+  __syncthreads();
+  if (kept >= p.topk && kept <= SEL_CAP) {
+    // every pick is at or above u_est (at least topk candidates are), so the
+    // exact tau of the row is the topk-th largest of the kept ones
+    uint32_t tau;
+    int need_eq;
+    lds_radix_select(cval, kept, p.topk, sh, tau, need_eq);
+    int eq_seen = 0, sel_seen = 0;
+    for (int base = 0; base < kept; base += SEL_THREADS) {
+      const int j = base + tid;
+      const uint32_t u = j < kept ? cval[j] : 0u;
+      const bool eq = j < kept && u == tau;
+      int eq_total;
+      const int eq_rank = eq_seen + block_excl_scan(eq ? 1 : 0, tid, sh, eq_total);
+      const bool sel = j < kept && (u > tau || (eq && eq_rank < need_eq));
+      int sel_total;
+      const int opos = sel_seen + block_excl_scan(sel ? 1 : 0, tid, sh, sel_total);
+      if (sel && opos < p.topk) out[opos] = cidx[j];
+      eq_seen += eq_total;
+      sel_seen += sel_total;
+    }
+    for (int w = tid; w < p.window; w += SEL_THREADS) out[p.topk + w] = (int32_t)(n_cand + w);
+    if (tid == 0) p.count[qid] = max_sel;
+    return;
+  }
+  // the estimate was off (too few or too many kept): exact multi-pass radix
 
   // ---- pass 0: smallest and largest candidate bit pattern
   uint32_t mx = 0u, mn = 0xFFFFFFFFu;
