@@ -47,6 +47,34 @@ constexpr int PB_VTILE = 17 * 1024;             // 32 x 34 chunks = 17 DMA instr
 constexpr int PB_PP = 144;                      // P buffer pitch (bytes per key)
 constexpr int PB_AHEAD = 3;                     // operand prefetch distance (MFMA steps)
 
+// 32x32x16 bf16 MFMAs whose accumulator is pinned to VGPRs.  The P/V kernel
+// keeps its 64 x 256 float32 O accumulator in the 256 AGPRs; a builtin MFMA for
+// S would also be given AGPRs and the compiler would shuffle O tiles in and out
+// of VGPRs every tile.  Written as inline asm, the S accumulators stay in VGPRs.
+// The compiler inserts no hazard wait states around inline asm, so each block
+// carries its own (gfx950, 8-pass XDL):
+//  * before each MFMA, 3 wait states cover a VALU write of an A/B operand;
+//  * the last block of a chain ends with 20 wait states, more than an XDL
+//    result needs before a VALU, LDS or memory instruction may read it.
+// Back-to-back MFMAs on the same accumulator need none.  LDS loads feeding the
+// operands are covered by the compiler's s_waitcnt insertion (it sees asm uses).
+__device__ __forceinline__ void mfma32v_first(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32v(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// last step of two chains sharing the B operand, then the read-after-write wait
+__device__ __forceinline__ void mfma32v_last2(f32x16& acc0, f32x16& acc1, bf16x8 a0, bf16x8 a1, bf16x8 b) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %3, %4, %1\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 3"
+      : "+v"(acc0), "+v"(acc1)
+      : "v"(a0), "v"(a1), "v"(b));
+}
+
 template <int H, int PHASE>   // PHASE 1: prefill_lse, PHASE 2: prefill_pv
 __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_kernel(const AttnParams p, float* lse2) {
   constexpr int TPW = PB_RW / H;       // tokens per wave
@@ -246,7 +274,7 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
     float* srow_base = p.scores + (int64_t)b * p.n_q * p.ld_scores;
     // S = Q K^T (lane = key l32, regs = rows), operands PB_AHEAD steps ahead.
     auto s_rows_keys = [&](const char* kb) __attribute__((always_inline)) {
-      Pair sa = {{f32x16{}, f32x16{}}};
+      Pair sa;
       bf16x8 kf[16], q1[16];
   #pragma unroll
       for (int s = 0; s < PB_AHEAD; ++s) {
@@ -256,62 +284,19 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
       __builtin_amdgcn_sched_barrier(0);
   #pragma unroll
       for (int s = 0; s < 16; ++s) {
-        sa.v[0] = mfma32(qf[s], kf[s], sa.v[0]);
-        if (s + PB_AHEAD < 16) kf[s + PB_AHEAD] = kfrag(kb, s + PB_AHEAD);
-        sa.v[1] = mfma32(q1[s], kf[s], sa.v[1]);
-        if (s + PB_AHEAD < 16) q1[s + PB_AHEAD] = q1frag(s + PB_AHEAD);
+        if (s == 15) {
+          mfma32v_last2(sa.v[0], sa.v[1], qf[s], q1[s], kf[s]);
+        } else {
+          if (s == 0) mfma32v_first(sa.v[0], qf[s], kf[s]); else mfma32v(sa.v[0], qf[s], kf[s]);
+          if (s + PB_AHEAD < 16) kf[s + PB_AHEAD] = kfrag(kb, s + PB_AHEAD);
+          if (s == 0) mfma32v_first(sa.v[1], q1[s], kf[s]); else mfma32v(sa.v[1], q1[s], kf[s]);
+          if (s + PB_AHEAD < 16) q1[s + PB_AHEAD] = q1frag(s + PB_AHEAD);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       return sa;
     };
 
-    // probabilities of tile kt (lane: key kbase + l32, rows 32mt + 8(r/4) + 4hb + r%4),
-    // the score of each token of the lane's key, and P (bf16) -> LDS [key][row]
-    auto probs = [&](Pair& sa, int kt, char* pb, float (&sc)[2][2], auto masked) __attribute__((always_inline)) {
-      constexpr bool need_mask = decltype(masked)::value;
-      const int64_t kbase = (int64_t)kt * PB_KT;
-      const int64_t key = kbase + l32;
-  #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-  #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 l4 = *(const f32x4*)(lse_lds + 32 * mt + 8 * q + 4 * hb);
-  #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 4 * q + j;
-            const float e = fast_exp2(sa.v[mt][r] * p.scale_log2 - l4[j]);
-            if constexpr (need_mask)
-              sa.v[mt][r] = key <= pos_of_row(32 * mt + 8 * q + 4 * hb + j) ? e : 0.f;
-            else
-              sa.v[mt][r] = e;
-          }
-        }
-        if constexpr (H == 16) {
-          float t0 = 0.f, t1 = 0.f;
-  #pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            t0 += sa.v[mt][r];
-            t1 += sa.v[mt][8 + r];
-          }
-          sc[mt][0] = halfwave_pair_sum(t0, t1);
-        } else if constexpr (H == 8) {
-          float t[4];
-  #pragma unroll
-          for (int q = 0; q < 4; ++q) t[q] = sa.v[mt][4 * q] + sa.v[mt][4 * q + 1] + sa.v[mt][4 * q + 2] + sa.v[mt][4 * q + 3];
-          sc[mt][0] = halfwave_pair_sum(t[0], t[1]);
-          sc[mt][1] = halfwave_pair_sum(t[2], t[3]);
-        }
-  #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          bf16x4 v4;
-          v4[0] = to_bf16(sa.v[mt][4 * q]);
-          v4[1] = to_bf16(sa.v[mt][4 * q + 1]);
-          v4[2] = to_bf16(sa.v[mt][4 * q + 2]);
-          v4[3] = to_bf16(sa.v[mt][4 * q + 3]);
-          *(bf16x4*)(pb + l32 * PB_PP + (32 * mt + 8 * q + 4 * hb) * 2) = v4;
-        }
-      }
-    };
     // scores of tile kt to global memory (token sums of 32/H tokens per 32-row tile)
     auto store_scores = [&](const Pair& sa, int kt, const float (&sc)[2][2]) __attribute__((always_inline)) {
       const int64_t key = (int64_t)kt * PB_KT + l32;
@@ -342,12 +327,11 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
         }
       }
     };
-    // O += P V for one tile (A = P rows x keys, B = V keys x dims, both via
-    // transposed reads).  Step j = (ks, n) = (j / 8, j % 8); the V fragment of
-    // step j is read PB_AHEAD steps before it is used, P of K-step 1 at step 4.
-    auto pv = [&](const char* pb, const char* vb) __attribute__((always_inline)) {
-      bf16x8 a[2][2], bv[16];
-      auto read_a = [&](int ks) {
+    // A operands of O += P V (P rows x keys, transposed reads of the [key][row]
+    // buffer), all four read at once so that the buffer is free for the next P.
+    auto read_pa = [&](const char* pb, bf16x8 (&a)[2][2]) __attribute__((always_inline)) {
+  #pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
         const int krow = 16 * ks + 8 * (G >> 1) + (s16 >> 2);
         const int off = 16 * (G & 1) + 4 * (s16 & 3);
   #pragma unroll
@@ -355,73 +339,183 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
           const bf16* pa = (const bf16*)(pb + krow * PB_PP) + 32 * mt + off;
           a[ks][mt] = cat8(lds_tr16(pa), lds_tr16(pa + 4 * (PB_PP / 2)));
         }
-      };
-      auto read_b = [&](int j) {
-        const int ks = j >> 3, n = j & 7;
-        const int krow = 16 * ks + 8 * (G >> 1) + (s16 >> 2);
-        const int off = 16 * (G & 1) + 4 * (s16 & 3);
-        const bf16* vrow = (const bf16*)(vb + krow * (PB_VC * 16)) + off;
-        bv[j] = cat8(lds_tr16(vrow + 32 * n), lds_tr16(vrow + 4 * (PB_VC * 8) + 32 * n));
-      };
-      read_a(0);
+      }
+    };
+    // V fragment of PV step j = (ks, n) = (j / 8, j % 8): keys 16 ks + ..., dims 32 n + ...
+    auto read_b = [&](const char* vb, int j) __attribute__((always_inline)) {
+      const int ks = j >> 3, n = j & 7;
+      const int krow = 16 * ks + 8 * (G >> 1) + (s16 >> 2);
+      const int off = 16 * (G & 1) + 4 * (s16 & 3);
+      const bf16* vrow = (const bf16*)(vb + krow * (PB_VC * 16)) + off;
+      return cat8(lds_tr16(vrow + 32 * n), lds_tr16(vrow + 4 * (PB_VC * 8) + 32 * n));
+    };
+    // O += P V for the last tile alone (V fragments PB_AHEAD steps ahead)
+    auto pv_only = [&](const bf16x8 (&a)[2][2], const char* vb) __attribute__((always_inline)) {
+      bf16x8 bv[16];
   #pragma unroll
-      for (int j = 0; j < PB_AHEAD; ++j) read_b(j);
+      for (int j = 0; j < PB_AHEAD; ++j) bv[j] = read_b(vb, j);
       __builtin_amdgcn_sched_barrier(0);
   #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int ks = j >> 3, n = j & 7;
         oacc[0][n] = mfma32(a[ks][0], bv[j], oacc[0][n]);
-        if (j + PB_AHEAD < 16) read_b(j + PB_AHEAD);
+        if (j + PB_AHEAD < 16) bv[j + PB_AHEAD] = read_b(vb, j + PB_AHEAD);
         oacc[1][n] = mfma32(a[ks][1], bv[j], oacc[1][n]);
-        if (j == 4) read_a(1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // The probabilities of tile kt woven into the 16 steps of O += P(kt-1) V(kt-1)
+    // (two MFMAs per step, with_pv) or alone (first tile).  Step s handles the
+    // logits r = 4q + 2(s%2) + {0,1} of row block mt = s/8, q = (s/2)%4 (lane:
+    // key kbase + l32, rows 32mt + 8q + 4hb + j): exp2 against the row lse, then
+    // at the end of a q group P (bf16) -> LDS [key][row], at the end of a row
+    // block the head sums of the scores.  The order is fixed per step, so that
+    // at most PB_AHEAD V fragments and two lse vectors are in flight.
+    auto pv_probs = [&](const bf16x8 (&a)[2][2], const char* vb, Pair& sa, int kt, char* pb, float (&sc)[2][2],
+                        auto masked, auto with_pv) __attribute__((always_inline)) {
+      constexpr bool need_mask = decltype(masked)::value;
+      constexpr bool do_pv = decltype(with_pv)::value;
+      const int64_t key = (int64_t)kt * PB_KT + l32;
+      auto lse4 = [&](int g) { return *(const f32x4*)(lse_lds + 32 * (g >> 2) + 8 * (g & 3) + 4 * hb); };
+      bf16x8 bv[16];
+      if constexpr (do_pv) {
+  #pragma unroll
+        for (int j = 0; j < PB_AHEAD; ++j) bv[j] = read_b(vb, j);
+      }
+      f32x4 lcur = lse4(0), lnext = lse4(1);
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int st = 0; st < 16; ++st) {
+        if constexpr (do_pv) {
+          const int ks = st >> 3, n = st & 7;
+          oacc[0][n] = mfma32(a[ks][0], bv[st], oacc[0][n]);
+          if (st + PB_AHEAD < 16) bv[st + PB_AHEAD] = read_b(vb, st + PB_AHEAD);
+          oacc[1][n] = mfma32(a[ks][1], bv[st], oacc[1][n]);
+        }
+        const int g = st >> 1, mt = st >> 3, q = g & 3;
+  #pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int j = 2 * (st & 1) + jj, r = 4 * q + j;
+          const float e = fast_exp2(sa.v[mt][r] * p.scale_log2 - lcur[j]);
+          if constexpr (need_mask)
+            sa.v[mt][r] = key <= pos_of_row(32 * mt + 8 * q + 4 * hb + j) ? e : 0.f;
+          else
+            sa.v[mt][r] = e;
+        }
+        if (st & 1) {
+          bf16x4 v4;
+          v4[0] = to_bf16(sa.v[mt][4 * q]);
+          v4[1] = to_bf16(sa.v[mt][4 * q + 1]);
+          v4[2] = to_bf16(sa.v[mt][4 * q + 2]);
+          v4[3] = to_bf16(sa.v[mt][4 * q + 3]);
+          *(bf16x4*)(pb + l32 * PB_PP + (32 * mt + 8 * q + 4 * hb) * 2) = v4;
+          lcur = lnext;
+          if (g + 2 < 8) lnext = lse4(g + 2);
+        }
+        if ((st & 7) == 7) {
+          if constexpr (H == 16) {
+            float t0 = 0.f, t1 = 0.f;
+  #pragma unroll
+            for (int r = 0; r < 8; ++r) {
+              t0 += sa.v[mt][r];
+              t1 += sa.v[mt][8 + r];
+            }
+            sc[mt][0] = halfwave_pair_sum(t0, t1);
+          } else if constexpr (H == 8) {
+            float t[4];
+  #pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+              t[qq] = sa.v[mt][4 * qq] + sa.v[mt][4 * qq + 1] + sa.v[mt][4 * qq + 2] + sa.v[mt][4 * qq + 3];
+            sc[mt][0] = halfwave_pair_sum(t[0], t[1]);
+            sc[mt][1] = halfwave_pair_sum(t[2], t[3]);
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     };
 
-    // Sweep 2: per tile, S -> P (float32 -> scores, bf16 -> LDS) -> O += P V.
-    // K and V of the next tile are fetched while this one is computed.  With
-    // H >= 8 the scores of a tile are two (four) floats per lane; they are
+    // Sweep 2, software-pipelined over tiles: iteration t computes S(t), then
+    // the probabilities of tile t on the VALU while the MFMAs compute
+    // O += P(t-1) V(t-1).  Iteration t waits for K(t) and V(t-1) (issued in
+    // iteration t-1), then fetches K(t+1) and V(t): V is one tile behind K, so
+    // two buffers of each suffice.  P(t-1) is read into registers before P(t)
+    // overwrites the wave's P buffer.  With H >= 8 the scores of a tile are
     // written one tile late, right after the DMA issue, so that the stores have
     // long completed when the next wait on the vector-memory counter comes.
     float sc_prev[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-    auto step2 = [&](int kt, const char* kc, const char* vc, char* kn, char* vn) __attribute__((always_inline)) {
-      wait_dma();
-      __syncthreads();
-      if (kt + 1 < ntiles) {
-        dma(kg, kt + 1, kn, koff);
-        dma(vg, kt + 1, vn, voff);
-      }
-      if constexpr (H >= 8) {
-        if (kt > 0) store_scores(Pair{}, kt - 1, sc_prev);
-      }
-      Pair sa = s_rows_keys(kc);
-      float sc[2][2];
-      // tiles left of the diagonal need no causal mask (uniform branch)
-      if ((int64_t)kt * PB_KT + PB_KT - 1 > pos_first)
-        probs(sa, kt, pbuf, sc, std::true_type{});
-      else
-        probs(sa, kt, pbuf, sc, std::false_type{});
+    auto finish_scores = [&](const Pair& sa, int kt, const float (&sc)[2][2]) __attribute__((always_inline)) {
       if constexpr (H >= 8) {
   #pragma unroll
         for (int mt = 0; mt < 2; ++mt) sc_prev[mt][0] = sc[mt][0], sc_prev[mt][1] = sc[mt][1];
       } else {
         store_scores(sa, kt, sc);
       }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_sched_barrier(0);
-      pv(pbuf, vc);
     };
-    dma(kg, 0, lds_k0, koff);
-    dma(vg, 0, lds_v0, voff);
-    {
-      int kt = 0;
-      for (; kt + 1 < ntiles; kt += 2) {
-        step2(kt, lds_k0, lds_v0, lds_k1, lds_v1);
-        step2(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+    // Start of tile kt: K(kt) and V(kt-1) have landed; P(kt-1) is read into
+    // registers before the DMA of K(kt+1) and V(kt) is issued, so that these
+    // LDS reads need no wait on the DMA just issued.
+    auto begin_tile = [&](int kt, char* kn, char* vn, bf16x8 (&pa)[2][2], bool read_p) __attribute__((always_inline)) {
+      wait_dma();
+      __syncthreads();
+      if (read_p) {
+        read_pa(pbuf, pa);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (kt < ntiles) step2(kt, lds_k0, lds_v0, lds_k1, lds_v1);
+      if (kt + 1 < ntiles) dma(kg, kt + 1, kn, koff);
+      dma(vg, kt, vn, voff);
+      if constexpr (H >= 8) {
+        if (kt > 0) store_scores(Pair{}, kt - 1, sc_prev);
+      }
+    };
+    auto iter = [&](int kt, const char* kc, char* kn, const char* vp, char* vn, auto masked) __attribute__((always_inline)) {
+      bf16x8 pa[2][2];
+      begin_tile(kt, kn, vn, pa, true);
+      Pair sa = s_rows_keys(kc);
+      float sc[2][2];
+      pv_probs(pa, vp, sa, kt, pbuf, sc, masked, std::true_type{});
+      finish_scores(sa, kt, sc);
+    };
+    // first tile is never preceded by a PV block
+    const int t_mask = (int)((pos_first + 1) / PB_KT);   // tiles >= t_mask need the causal mask
+    dma(kg, 0, lds_k0, koff);
+    {
+      bf16x8 none[2][2] = {};
+      begin_tile(0, lds_k1, lds_v0, none, false);
+      Pair sa = s_rows_keys(lds_k0);
+      float sc[2][2];
+      if (t_mask == 0)
+        pv_probs(none, lds_v0, sa, 0, pbuf, sc, std::true_type{}, std::false_type{});
+      else
+        pv_probs(none, lds_v0, sa, 0, pbuf, sc, std::false_type{}, std::false_type{});
+      finish_scores(sa, 0, sc);
     }
+    {
+      int kt = 1;
+      for (; kt + 1 < t_mask; kt += 2) {
+        iter(kt, lds_k1, lds_k0, lds_v0, lds_v1, std::false_type{});
+        iter(kt + 1, lds_k0, lds_k1, lds_v1, lds_v0, std::false_type{});
+      }
+      if (kt < t_mask) {
+        iter(kt, lds_k1, lds_k0, lds_v0, lds_v1, std::false_type{});
+        ++kt;
+      }
+      // The few tiles on the diagonal pick their buffers at run time: one copy
+      // of the body, and no register pressure from two unrolled copies.
+      for (; kt < ntiles; ++kt) {
+        const bool odd = kt & 1;
+        iter(kt, odd ? lds_k1 : lds_k0, odd ? lds_k0 : lds_k1, odd ? lds_v0 : lds_v1, odd ? lds_v1 : lds_v0,
+             std::true_type{});
+      }
+    }
+    // last PV block
+    wait_dma();
+    __syncthreads();
     if constexpr (H >= 8) store_scores(Pair{}, ntiles - 1, sc_prev);
+    {
+      bf16x8 pa[2][2];
+      read_pa(pbuf, pa);
+      pv_only(pa, ((ntiles - 1) & 1) ? lds_v1 : lds_v0);
+    }
 
     // ---- outputs: lane holds O[32mt + 8(r/4) + 4hb + r%4][32n + l32]
   #pragma unroll
