@@ -113,8 +113,11 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
   // 17 wave-instructions of 64 x 16 B (lane l of instruction i fills chunk
   // 64 i + l); instruction i is issued by wave i % 4.  Pad chunks and the slack
   // after the last row load a valid row and are never read.  The per-lane
-  // source offsets inside a tile are loop invariant; a tile that ends past the
-  // last key clamps its rows to that key (masked later).
+  // source offsets inside a tile are loop invariant.  The loads go through a
+  // buffer resource that ends at the tile's last valid key, so rows past it
+  // read as zeros (and are masked later).  Buffer loads to LDS rather than
+  // global_load_lds: after the latter the compiler can no longer count LDS
+  // reads in order and waits for all of them at every use.
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   uint32_t koff[5], voff[5];
 #pragma unroll
@@ -126,17 +129,15 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
     voff[i] = (uint32_t)(min(vr, PB_KT - 1) * 512 + (vc < 32 ? vc : 0) * 16);
   }
   auto dma = [&](const char* g, int kt, char* buf, const uint32_t (&off)[5]) __attribute__((always_inline)) {
-    const int64_t last = n_keys - 1 - (int64_t)kt * PB_KT;   // last valid row of the tile
-    const bool partial = last < PB_KT - 1;
-    const char* gt = g + (int64_t)kt * (PB_KT * 512);
+    // buffer resource over the valid rows of the tile: loads past them return 0
+    const int64_t rows = min((int64_t)PB_KT, n_keys - (int64_t)kt * PB_KT);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(g + (int64_t)kt * (PB_KT * 512)), 0, (int)(rows * 512), 0x00020000);
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
       const int ins = wv + 4 * i;
-      if (i < 4 || wv == 0) {   // 17 instructions: wave 0 issues the last one
-        uint32_t o = off[i];
-        if (partial) o = min(o, (o & 511u) | ((uint32_t)last << 9));
-        __builtin_amdgcn_global_load_lds((const void*)(gt + o), (void HS2_LDS*)((char HS2_LDS*)buf + ins * 1024), 16, 0, 0);
-      }
+      if (i < 4 || wv == 0)   // 17 instructions: wave 0 issues the last one
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void HS2_LDS*)((char HS2_LDS*)buf + ins * 1024), 16, off[i], 0, 0, 0);
     }
   };
   auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
