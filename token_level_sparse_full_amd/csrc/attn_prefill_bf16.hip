@@ -128,17 +128,22 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
     koff[i] = (uint32_t)(min(kr, PB_KT - 1) * 512 + (kc < 32 ? kc : 0) * 16);
     voff[i] = (uint32_t)(min(vr, PB_KT - 1) * 512 + (vc < 32 ? vc : 0) * 16);
   }
+  // buffer resource over the valid rows of tile kt (none past the last key):
+  // loads past them return 0
+  auto tile_rsrc = [&](const char* g, int kt) __attribute__((always_inline)) {
+    const int64_t rows = max((int64_t)0, min((int64_t)PB_KT, n_keys - (int64_t)kt * PB_KT));
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(g + (int64_t)kt * (PB_KT * 512)), 0, (int)(rows * 512), 0x00020000);
+  };
+  // DMA instruction i (0..4) of this wave for one tile image
+  auto dma_one = [&](const __amdgpu_buffer_rsrc_t& rs, char* buf, const uint32_t (&off)[5], int i) __attribute__((always_inline)) {
+    const int ins = wv + 4 * i;
+    if (i < 4 || wv == 0)   // 17 instructions: wave 0 issues the last one
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void HS2_LDS*)((char HS2_LDS*)buf + ins * 1024), 16, off[i], 0, 0, 0);
+  };
   auto dma = [&](const char* g, int kt, char* buf, const uint32_t (&off)[5]) __attribute__((always_inline)) {
-    // buffer resource over the valid rows of the tile: loads past them return 0
-    const int64_t rows = min((int64_t)PB_KT, n_keys - (int64_t)kt * PB_KT);
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(g + (int64_t)kt * (PB_KT * 512)), 0, (int)(rows * 512), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(g, kt);
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      const int ins = wv + 4 * i;
-      if (i < 4 || wv == 0)   // 17 instructions: wave 0 issues the last one
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void HS2_LDS*)((char HS2_LDS*)buf + ins * 1024), 16, off[i], 0, 0, 0);
-    }
+    for (int i = 0; i < 5; ++i) dma_one(rs, buf, off, i);
   };
   auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
   // K fragment for K-step s: key l32 of the tile, dims 16s + 8hb .. +7
@@ -273,8 +278,9 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
   #pragma unroll
       for (int n = 0; n < 8; ++n) oacc[mt][n] = f32x16{};
     float* srow_base = p.scores + (int64_t)b * p.n_q * p.ld_scores;
-    // S = Q K^T (lane = key l32, regs = rows), operands PB_AHEAD steps ahead.
-    auto s_rows_keys = [&](const char* kb) __attribute__((always_inline)) {
+    // S = Q K^T (lane = key l32, regs = rows), operands PB_AHEAD steps ahead;
+    // hook(s) runs inside step s (the next tile's DMA, the scores)
+    auto s_rows_keys = [&](const char* kb, auto hook) __attribute__((always_inline)) {
       Pair sa;
       bf16x8 kf[16], q1[16];
   #pragma unroll
@@ -293,6 +299,7 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
           if (s == 0) mfma32v_first(sa.v[1], q1[s], kf[s]); else mfma32v(sa.v[1], q1[s], kf[s]);
           if (s + PB_AHEAD < 16) q1[s + PB_AHEAD] = q1frag(s + PB_AHEAD);
         }
+        hook(s);
         __builtin_amdgcn_sched_barrier(0);
       }
       return sa;
@@ -454,24 +461,28 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
     };
     // Start of tile kt: K(kt) and V(kt-1) have landed; P(kt-1) is read into
     // registers before the DMA of K(kt+1) and V(kt) is issued, so that these
-    // LDS reads need no wait on the DMA just issued.
-    auto begin_tile = [&](int kt, char* kn, char* vn, bf16x8 (&pa)[2][2], bool read_p) __attribute__((always_inline)) {
+    // LDS reads need no wait on that DMA.
+    auto sync_tile = [&](bf16x8 (&pa)[2][2], bool read_p) __attribute__((always_inline)) {
       wait_dma();
       __syncthreads();
       if (read_p) {
         read_pa(pbuf, pa);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (kt + 1 < ntiles) dma(kg, kt + 1, kn, koff);
-      dma(vg, kt, vn, voff);
-      if constexpr (H >= 8) {
-        if (kt > 0) store_scores(Pair{}, kt - 1, sc_prev);
-      }
     };
+    // The DMA of K(kt+1) (zeros past the last tile) and V(kt), one instruction
+    // per S step so that the issue overlaps the MFMAs, then the deferred scores.
     auto iter = [&](int kt, const char* kc, char* kn, const char* vp, char* vn, auto masked) __attribute__((always_inline)) {
       bf16x8 pa[2][2];
-      begin_tile(kt, kn, vn, pa, true);
-      Pair sa = s_rows_keys(kc);
+      sync_tile(pa, true);
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kg, kt + 1), rv = tile_rsrc(vg, kt);
+      Pair sa = s_rows_keys(kc, [&](int st) __attribute__((always_inline)) {
+        if (st < 5) dma_one(rk, kn, koff, st);
+        else if (st < 10) dma_one(rv, vn, voff, st - 5);
+        if constexpr (H >= 8) {
+          if (st == 10) store_scores(Pair{}, kt - 1, sc_prev);
+        }
+      });
       float sc[2][2];
       pv_probs(pa, vp, sa, kt, pbuf, sc, masked, std::true_type{});
       finish_scores(sa, kt, sc);
@@ -481,8 +492,10 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
     dma(kg, 0, lds_k0, koff);
     {
       bf16x8 none[2][2] = {};
-      begin_tile(0, lds_k1, lds_v0, none, false);
-      Pair sa = s_rows_keys(lds_k0);
+      sync_tile(none, false);
+      if (ntiles > 1) dma(kg, 1, lds_k1, koff);
+      dma(vg, 0, lds_v0, voff);
+      Pair sa = s_rows_keys(lds_k0, [](int) {});
       float sc[2][2];
       if (t_mask == 0)
         pv_probs(none, lds_v0, sa, 0, pbuf, sc, std::true_type{}, std::false_type{});
