@@ -137,7 +137,7 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
   // DMA instruction i (0..4) of this wave for one tile image
   auto dma_one = [&](const __amdgpu_buffer_rsrc_t& rs, char* buf, const uint32_t (&off)[5], int i) __attribute__((always_inline)) {
     const int ins = wv + 4 * i;
-    if (i < 4 || wv == 0)   // 17 instructions: wave 0 issues the last one
+    if (i < 4 || (i == 4 && wv == 0))   // 17 instructions: wave 0 issues the last one
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void HS2_LDS*)((char HS2_LDS*)buf + ins * 1024), 16, off[i], 0, 0, 0);
   };
   auto dma = [&](const char* g, int kt, char* buf, const uint32_t (&off)[5]) __attribute__((always_inline)) {
@@ -200,29 +200,34 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
         }
       }
     };
-    // Tile kt sits in kc; K(kt+2) goes to kd, which held K(kt-1).  K(kt+1)
-    // may still be in flight at the wait: each wave keeps its last batch of
-    // DMA instructions (5 for wave 0, 4 for the others) outstanding.
+    // Tile kt sits in kc; K(kt+2) goes to kd, which held K(kt-1) (past the last
+    // tile the buffer resource is empty and the DMA writes zeros, so that every
+    // tile issues the same instructions).  K(kt+1) may still be in flight at
+    // the wait: each wave keeps its last batch of DMA instructions (5 for wave
+    // 0, 4 for the others) outstanding.  The batch is spread over the MFMA
+    // steps (one instruction every third step).
     auto step1 = [&](int kt, const char* kc, char* kd) __attribute__((always_inline)) {
-      if (kt + 1 < ntiles) {
-        if (wv == 0) __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5)
-        else __builtin_amdgcn_s_waitcnt(0x0F74);           // vmcnt(4)
-      } else {
-        wait_dma();
-      }
+      if (wv == 0) __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5)
+      else __builtin_amdgcn_s_waitcnt(0x0F74);           // vmcnt(4)
       __syncthreads();
-      if (kt + 2 < ntiles) dma(kg, kt + 2, kd, koff);
-      Pair st = {{f32x16{}, f32x16{}}};
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kg, kt + 2);
+      Pair st;
+      bf16x8 kf[16];
+#pragma unroll
+      for (int s = 0; s < PB_AHEAD; ++s) kf[s] = kfrag(kc, s);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
-        const bf16x8 kf = kfrag(kc, s);
-        st.v[0] = mfma32(kf, qf[0][s], st.v[0]);
-        st.v[1] = mfma32(kf, qf[1][s], st.v[1]);
+        st.v[0] = mfma32(kf[s], qf[0][s], s == 0 ? f32x16{} : st.v[0]);
+        if (s + PB_AHEAD < 16) kf[s + PB_AHEAD] = kfrag(kc, s + PB_AHEAD);
+        st.v[1] = mfma32(kf[s], qf[1][s], s == 0 ? f32x16{} : st.v[1]);
+        if (s % 3 == 0 && s < 15) dma_one(rk, kd, koff, s / 3);
+        __builtin_amdgcn_sched_barrier(0);
       }
       lse_update(st, kt, (int64_t)kt * PB_KT + PB_KT - 1 > pos_first);
     };
     dma(kg, 0, lds_k0, koff);
-    if (ntiles > 1) dma(kg, 1, lds_k1, koff);
+    dma(kg, 1, lds_k1, koff);
     {
       int kt = 0;
       for (; kt + 2 < ntiles; kt += 3) {
@@ -232,6 +237,7 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
       }
       if (kt < ntiles) step1(kt, lds_k0, lds_k2);
       if (kt + 1 < ntiles) step1(kt + 1, lds_k1, lds_k0);
+      wait_dma();   // the zero-filling DMA past the last tile
     }
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
@@ -380,7 +386,7 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
     // block the head sums of the scores.  The order is fixed per step, so that
     // at most PB_AHEAD V fragments and two lse vectors are in flight.
     auto pv_probs = [&](const bf16x8 (&a)[2][2], const char* vb, Pair& sa, int kt, char* pb, float (&sc)[2][2],
-                        auto masked, auto with_pv) __attribute__((always_inline)) {
+                        auto masked, auto with_pv, auto hook) __attribute__((always_inline)) {
       constexpr bool need_mask = decltype(masked)::value;
       constexpr bool do_pv = decltype(with_pv)::value;
       const int64_t key = (int64_t)kt * PB_KT + l32;
@@ -438,6 +444,7 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
             sc[mt][1] = halfwave_pair_sum(t[2], t[3]);
           }
         }
+        hook(st);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -470,21 +477,23 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    // The DMA of K(kt+1) (zeros past the last tile) and V(kt), one instruction
-    // per S step so that the issue overlaps the MFMAs, then the deferred scores.
+    // The DMA of K(kt+1) (zeros past the last tile) in the S steps and of V(kt)
+    // in the PV steps, one instruction every third step: a CU moves about 46
+    // bytes per clock into LDS, and a burst would stall the issuing wave.
     auto iter = [&](int kt, const char* kc, char* kn, const char* vp, char* vn, auto masked) __attribute__((always_inline)) {
       bf16x8 pa[2][2];
       sync_tile(pa, true);
       const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kg, kt + 1), rv = tile_rsrc(vg, kt);
       Pair sa = s_rows_keys(kc, [&](int st) __attribute__((always_inline)) {
-        if (st < 5) dma_one(rk, kn, koff, st);
-        else if (st < 10) dma_one(rv, vn, voff, st - 5);
+        if (st % 3 == 0 && st < 15) dma_one(rk, kn, koff, st / 3);
         if constexpr (H >= 8) {
-          if (st == 10) store_scores(Pair{}, kt - 1, sc_prev);
+          if (st == 14) store_scores(Pair{}, kt - 1, sc_prev);
         }
       });
       float sc[2][2];
-      pv_probs(pa, vp, sa, kt, pbuf, sc, masked, std::true_type{});
+      pv_probs(pa, vp, sa, kt, pbuf, sc, masked, std::true_type{}, [&](int st) __attribute__((always_inline)) {
+        if (st % 3 == 0 && st < 15) dma_one(rv, vn, voff, st / 3);
+      });
       finish_scores(sa, kt, sc);
     };
     // first tile is never preceded by a PV block
@@ -498,9 +507,9 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
       Pair sa = s_rows_keys(lds_k0, [](int) {});
       float sc[2][2];
       if (t_mask == 0)
-        pv_probs(none, lds_v0, sa, 0, pbuf, sc, std::true_type{}, std::false_type{});
+        pv_probs(none, lds_v0, sa, 0, pbuf, sc, std::true_type{}, std::false_type{}, [](int) {});
       else
-        pv_probs(none, lds_v0, sa, 0, pbuf, sc, std::false_type{}, std::false_type{});
+        pv_probs(none, lds_v0, sa, 0, pbuf, sc, std::false_type{}, std::false_type{}, [](int) {});
       finish_scores(sa, 0, sc);
     }
     {
