@@ -42,7 +42,7 @@ constexpr int kMergeFan = 32;   // partial states merged per workgroup and level
 int decode_chunk(int B, int64_t T) {
   const int64_t total = (int64_t)B * T;
   int ch = 256;
-  while (ch < 4096 && total / ch > 1024) ch *= 2;
+  while (ch < 8192 && total / ch > 512) ch *= 2;   // about two workgroups per CU
   return ch;
 }
 
@@ -152,11 +152,246 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(const AttnP
       }
     z_run = z_run * alpha + psum;
     m_run = m_new;
+    if (__any(alpha != 1.f)) {   // the running max rarely moves after the first steps
 #pragma unroll
-    for (int t = 0; t < 16; ++t) oacc[t] *= alpha;
+      for (int t = 0; t < 16; ++t) oacc[t] *= alpha;
+    }
     wave_lds_order();
     pv_step<KV>(stage, pr, g, c16, oacc);
     wave_lds_order();
+  }
+
+  // ---- merge the 4 lane groups and 4 waves into this chunk's partial state
+  z_run += shfl_xor(z_run, 16);
+  z_run += shfl_xor(z_run, 32);
+  __syncthreads();
+  float* red_o = (float*)smem;
+  float* red_m = red_o + DC_WAVES * 16 * kRedPitch;
+  float* red_z = red_m + DC_WAVES * 16;
+  if (l < 16) {
+    red_m[wave * 16 + l] = m_run;
+    red_z[wave * 16 + l] = z_run;
+  }
+#pragma unroll
+  for (int t = 0; t < 16; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red_o[(wave * 16 + c16) * kRedPitch + 16 * t + 4 * g + r] = oacc[t][r];
+  __syncthreads();
+  const int64_t pbase = ((int64_t)b * ws.nch + chunk) * 16;
+  for (int e = tid; e < R * kHeadDim; e += DC_THREADS) {
+    const int row = e / kHeadDim, d = e % kHeadDim;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < DC_WAVES; ++w) M = fmaxf(M, red_m[w * 16 + row]);
+    float Z = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < DC_WAVES; ++w) {
+      const float mw = red_m[w * 16 + row];
+      if (mw != kNegInf) {
+        const float f = fast_exp2(mw - M);
+        Z += red_z[w * 16 + row] * f;
+        acc += red_o[(w * 16 + row) * kRedPitch + d] * f;
+      }
+    }
+    ws.part_o[(pbase + row) * kHeadDim + d] = acc;
+    if (d == 0) {
+      ws.part_m[pbase + row] = M;
+      ws.part_z[pbase + row] = Z;
+    }
+  }
+}
+
+// bf16 / e4m3 caches: the 4 waves of a workgroup take turns over the chunk's
+// 16-key steps (together they stream one contiguous range), and each wave
+// keeps its next step's K and V rows in flight (registers) while the current
+// step is computed, so that every wave always has about 16 KB of HBM reads
+// outstanding.  S^T (16 keys x 16 rows) is 8 MFMAs
+// 16x16x32 with K straight from the registers; V goes through a wave-private
+// LDS tile and feeds O^T += V^T P^T as 16 MFMAs 16x16x16 (A = V^T by
+// transposed reads, B = P^T straight from the S^T layout).
+constexpr int DS_STEP = 16;
+constexpr int DS_VPITCH = 272;                       // bf16 elements per staged V row (544 B)
+constexpr int DS_VTILE = DS_STEP * DS_VPITCH * 2;    // 8704 B per wave
+constexpr int DS_RED = (DC_WAVES * 16 * kRedPitch + 2 * DC_WAVES * 16) * 4;
+constexpr int DS_SMEM = DC_WAVES * DS_VTILE > DS_RED ? DC_WAVES * DS_VTILE : DS_RED;
+
+template <int KV>
+struct DsRegs {
+  static constexpr int NK = KV == KV_BF16 ? 8 : 4;   // 16-byte K pieces per lane
+  u32x4 k[NK];
+  float ks[4], vs[4];                                // e4m3 row scales of keys kb + 4g + i
+};
+template <int KV>
+struct DsVRegs {
+  static constexpr int NV = KV == KV_BF16 ? 8 : 4;   // 16-byte V pieces per lane
+  u32x4 v[NV];
+};
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+template <int KV, int H>
+__global__ __launch_bounds__(DC_THREADS, 2) void decode_stream_kernel(const AttnParams p, const DecodeWs ws) {
+  constexpr int ROWB = (KV == KV_BF16) ? 512 : 256;
+  __shared__ __attribute__((aligned(16))) char smem[DS_SMEM];
+
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int g = l >> 4, c16 = l & 15;
+  const int chunk = blockIdx.x, b = blockIdx.y;
+  const int R = p.n_q * H;
+  const bool row_ok = c16 < R;
+  const int64_t row_pos = row_ok ? p.q_pos0 + c16 / H : -1;
+  const int64_t n_keys = p.q_pos0 + p.n_q;
+  const int64_t key0 = (int64_t)chunk * ws.chunk;
+  const int64_t key1 = min(n_keys, key0 + ws.chunk);
+  // the 4 waves interleave 16-key steps: together they stream one contiguous range
+  const int wvu = __builtin_amdgcn_readfirstlane(wave);
+  const int64_t kw0 = key0 + wvu * DS_STEP;               // first key of this wave's first step
+  const int64_t kw1 = key1;
+  const int nst_all = key1 > key0 ? (int)((key1 - key0 + DS_STEP - 1) / DS_STEP) : 0;
+  const int nst = nst_all > wvu ? (nst_all - wvu + DC_WAVES - 1) / DC_WAVES : 0;
+  const int64_t kv_row0 = (int64_t)b * p.T;
+  const char* kseq = (const char*)p.k + kv_row0 * ROWB;
+  const char* vseq = (const char*)p.v + kv_row0 * ROWB;
+  float* lg = ws.logits + kv_row0 * 16;
+  bf16* vt = (bf16*)(smem + wave * DS_VTILE);
+
+  QFrag qf;
+  load_qfrag<KV>((const char*)p.q + ((int64_t)b * R + c16) * kHeadDim * 2, row_ok, g, qf);
+
+  // ---- loads of step st: K of key kb + c16 (the lane's MFMA row) and the
+  // e4m3 scales of keys kb + 4g + i
+  // Keys past the wave's range load its last row instead (no branches around
+  // the loads, so the compiler can count them): their logits are masked and
+  // their probabilities are zero.  The K/V stream is read once: nontemporal
+  // loads (measured on the box: 6.2-6.9 TB/s for a plain stream against
+  // 4.4 TB/s with ordinary loads).
+  // V: each load instruction reads whole rows (bf16: two rows of 512 B, e4m3:
+  // four rows of 256 B), so that every cache line is requested once
+  constexpr int VRPI = 1024 / ROWB;   // rows per load instruction
+  auto load_v = [&](int st, DsVRegs<KV>& r) __attribute__((always_inline)) {
+    const int64_t kb = kw0 + (int64_t)st * (DS_STEP * DC_WAVES);
+#pragma unroll
+    for (int j = 0; j < DsVRegs<KV>::NV; ++j) {
+      const int64_t kv = min(kb + VRPI * j + l / (64 / VRPI), kw1 - 1);
+      r.v[j] = ld_nt((const u32x4*)(vseq + kv * ROWB + 16 * (l % (64 / VRPI))));
+    }
+  };
+  auto load_k = [&](int st, DsRegs<KV>& r) __attribute__((always_inline)) {
+    const int64_t kb = kw0 + (int64_t)st * (DS_STEP * DC_WAVES);
+    const int64_t kk = min(kb + c16, kw1 - 1);
+    const char* kp = kseq + kk * ROWB;
+#pragma unroll
+    for (int j = 0; j < DsRegs<KV>::NK; ++j) {
+      const int off = (KV == KV_BF16) ? (32 * j + 8 * g) * 2 : 64 * j + 16 * g;
+      r.k[j] = ld_nt((const u32x4*)(kp + off));
+    }
+    if constexpr (KV == KV_E4M3) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t key = min(kb + 4 * g + i, kw1 - 1);
+        r.ks[i] = p.k_scale[kv_row0 + key];
+        r.vs[i] = p.v_scale[kv_row0 + key];
+      }
+    }
+  };
+  // logits of the wave's keys through a buffer resource that ends at its last
+  // key: stores past it are dropped (rows >= R hold unused slots)
+  const __amdgpu_buffer_rsrc_t lg_rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(lg + key0 * 16), 0, (int)(max((int64_t)0, key1 - key0) * 64), 0x00020000);
+  // V rows of the step -> the wave's LDS tile (bf16, row pitch DS_VPITCH)
+  auto stage = [&](const DsVRegs<KV>& r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < DsVRegs<KV>::NV; ++j) {
+      bf16* row = vt + (VRPI * j + l / (64 / VRPI)) * DS_VPITCH;
+      if constexpr (KV == KV_BF16) {
+        *(u32x4*)(row + 8 * (l % 32)) = r.v[j];
+      } else {
+        bf16* dst = row + 16 * (l % 16);
+        *(bf16x8*)dst = e4m3x8_to_bf16(r.v[j][0], r.v[j][1]);
+        *(bf16x8*)(dst + 8) = e4m3x8_to_bf16(r.v[j][2], r.v[j][3]);
+      }
+    }
+  };
+
+  float m_run = kNegInf, z_run = 0.f;   // z_run: this lane's keys only (summed over g at the end)
+  f32x4 oacc[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int st, const DsRegs<KV>& r) __attribute__((always_inline)) {
+    const int64_t kb = kw0 + (int64_t)st * (DS_STEP * DC_WAVES);
+    // S^T: lane holds keys kb + 4g + i of row c16
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (KV == KV_BF16) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc = mfma16(as_bf16x8(r.k[j]), qf.b[j], acc);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc = mfma16(e4m3x8_to_bf16(r.k[j][0], r.k[j][1]), qf.b[2 * j], acc);
+        acc = mfma16(e4m3x8_to_bf16(r.k[j][2], r.k[j][3]), qf.b[2 * j + 1], acc);
+      }
+    }
+    float x[4];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t key = kb + 4 * g + i;
+      float v = acc[i] * p.scale_log2;
+      if constexpr (KV == KV_E4M3) v *= r.ks[i];
+      v = (key < kw1 && key <= row_pos) ? v : kNegInf;
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), lg_rs, (int)(((key - key0) * 16 + c16) * 4), 0, 0);
+      x[i] = v;
+      tmax = fmaxf(tmax, v);
+    }
+    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+    bf16x4 pb;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float e = (x[i] == kNegInf) ? 0.f : fast_exp2(x[i] - m_new);
+      psum += e;
+      if constexpr (KV == KV_E4M3) e *= r.vs[i];   // finite: the clamped key's scale
+      pb[i] = to_bf16(e);
+    }
+    z_run = z_run * alpha + psum;
+    m_run = m_new;
+    if (__any(alpha != 1.f)) {   // the running max rarely moves after the first steps
+#pragma unroll
+      for (int t = 0; t < 16; ++t) oacc[t] *= alpha;
+    }
+    // O^T += V^T P^T: A lane = column 16t + c16 of the tile rows 4g..4g+3
+    const bf16* vr = vt + (4 * g + (c16 >> 2)) * DS_VPITCH + 4 * (c16 & 3);
+    const i16x4_t pbi = __builtin_bit_cast(i16x4_t, pb);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const i16x4_t a = __builtin_bit_cast(i16x4_t, lds_tr16(vr + 16 * t));
+      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pbi, oacc[t], 0, 0, 0);
+    }
+  };
+
+  // K (and the scales) double-buffered in registers; the one set of V
+  // registers is refilled with the next step's rows as soon as they are in LDS.
+  DsRegs<KV> r0, r1;
+  DsVRegs<KV> vr;
+  if (nst > 0) {
+    load_k(0, r0);
+    load_v(0, vr);
+  }
+  for (int st = 0; st < nst; st += 2) {
+    if (st + 1 < nst) load_k(st + 1, r1);
+    stage(vr);
+    if (st + 1 < nst) load_v(st + 1, vr);
+    compute(st, r0);
+    if (st + 1 < nst) {
+      if (st + 2 < nst) load_k(st + 2, r0);
+      stage(vr);
+      if (st + 2 < nst) load_v(st + 2, vr);
+      compute(st + 1, r1);
+    }
   }
 
   // ---- merge the 4 lane groups and 4 waves into this chunk's partial state
@@ -282,7 +517,10 @@ template <int KV, int H>
 hipError_t launch_decode_h(const AttnParams& p, const DecodeWs& ws, hipStream_t stream) {
   const int64_t n_keys = p.q_pos0 + p.n_q;
   const unsigned nch = (unsigned)((n_keys + ws.chunk - 1) / ws.chunk);
-  hipLaunchKernelGGL((decode_split_kernel<KV, H>), dim3(nch, p.B), dim3(DC_THREADS), 0, stream, p, ws);
+  if constexpr (KV == KV_F32)
+    hipLaunchKernelGGL((decode_split_kernel<KV, H>), dim3(nch, p.B), dim3(DC_THREADS), 0, stream, p, ws);
+  else
+    hipLaunchKernelGGL((decode_stream_kernel<KV, H>), dim3(nch, p.B), dim3(DC_THREADS), 0, stream, p, ws);
   const int R = p.n_q * p.H;
   // merge tree over the chunk states: part -> mid -> part -> ... -> final
   MergeIO io{ws.part_m, ws.part_z, ws.part_o, ws.mid_m, ws.mid_z, ws.mid_o, ws.nch, (int)nch, ws.nmid};
