@@ -394,6 +394,7 @@ def other_workloads(dev):
         cnt = torch.empty((B, 1), dtype=torch.int32, device=dev)
         o2 = [torch.empty_like(x) for x in qs]
         l2 = [torch.empty((B, 1, H), dtype=torch.float32, device=dev) for _ in qs]
+        ws_sp = hs2.workspace(hs2.sparse_workspace_bytes(B, 1, H, ms), dev)
 
         def run(mark):
             hs2.hs2_full_attn_scored(q, k, v, q_pos0=p, sm_scale=scale, k_scale=ks, v_scale=vs, o=o, lse=lse,
@@ -403,7 +404,7 @@ def other_workloads(dev):
             mark()
             for i, x in enumerate(qs):
                 hs2.hs2_sparse_attn_reuse(x, k, v, idx, cnt, sm_scale=scale, k_scale=ks, v_scale=vs, o=o2[i],
-                                          lse=l2[i])
+                                          lse=l2[i], ws=ws_sp)
             mark()
         return _timed(run, 3, flush=flush)
 

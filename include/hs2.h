@@ -156,13 +156,23 @@ size_t hs2_select_workspace_bytes(int B, int n_q, int64_t T, int64_t q_pos0);
  *   lse    [B, n_q, H]       float32, may be NULL
  * count is clamped to [0, max_sel]; entries outside [0, T) are skipped (never
  * read).  An empty set yields o = 0 and lse = -inf.  Requires 1 <= max_sel <=
- * HS2_MAX_SELECT.
+ * HS2_MAX_SELECT, and a workspace of hs2_sparse_workspace_bytes() bytes when
+ * that is not 0 (else workspace may be NULL).
  */
 int hs2_sparse_attn_reuse(const void* q, int q_dtype, int B, int n_q, int H, int d,
                           const void* k, const void* v, int kv_dtype,
                           const float* k_scale, const float* v_scale, int64_t T,
                           const int32_t* idx, const int32_t* count, int max_sel, float sm_scale,
-                          void* o, float* lse, void* stream);
+                          void* o, float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace of hs2_sparse_attn_reuse for these shapes.  It is 0 when the
+ * queries are many (B * n_q > 64: one workgroup per query); fewer queries (the
+ * decode case) split each selected set into pieces of 128 keys, one workgroup
+ * each, and keep every piece's softmax max, sum and unnormalised output there
+ * (B * n_q * ceil(max_sel / 128) * 16 * 258 * 4 bytes, rounded up).  The
+ * contents are scratch; calls that share a workspace must not overlap.
+ * Returns 0 for out-of-range arguments (the call itself then rejects them). */
+size_t hs2_sparse_workspace_bytes(int B, int n_q, int H, int max_sel);
 
 /*
  * hs2_bridge_kv_proj - KV Bridging re-projection.

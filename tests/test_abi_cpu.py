@@ -19,7 +19,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = hs2.header_symbols()
-    assert len(names) == 10
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
 
@@ -81,6 +81,12 @@ def test_workspace_sizes(lib):
     assert lib.hs2_select_workspace_bytes(1, 1, 1 << 20, (1 << 20) - 1) >= 3 * 2048 * 4 + (1 << 20) // 4096 * 8
     assert lib.hs2_select_workspace_bytes(1, 32768, 131072, 98304) == 0     # many rows: one workgroup per row
     assert lib.hs2_select_workspace_bytes(16, 1, 32768, 32767) == 0         # 16 rows below 32768 candidates
+    # few queries (decode) split each selected set into 128-key pieces: per piece max, sum and output
+    assert lib.hs2_sparse_workspace_bytes(16, 1, 16, 1152) >= 16 * 9 * 16 * 258 * 4
+    assert lib.hs2_sparse_workspace_bytes(1, 64, 16, 1152) > 0
+    assert lib.hs2_sparse_workspace_bytes(1, 65, 16, 1152) == 0             # many queries: one workgroup each
+    assert lib.hs2_sparse_workspace_bytes(1, 32768, 16, 1152) == 0
+    assert lib.hs2_sparse_workspace_bytes(1, 1, 16, 0) == 0
 
 
 def sel(lib, **kw):
@@ -109,11 +115,11 @@ def test_select_rejects(lib, kw, code):
 
 def sparse(lib, **kw):
     a = dict(q=A, qd=BF16, B=1, n_q=1, H=16, d=256, k=A, v=A, kvd=BF16, ks=None, vs=None, T=100, idx=A, count=A,
-             ms=1152, sc=0.0625, o=A, lse=None)
+             ms=1152, sc=0.0625, o=A, lse=None, ws=A, wsb=1 << 40)
     a.update(kw)
     return lib.hs2_sparse_attn_reuse(a["q"], a["qd"], a["B"], a["n_q"], a["H"], a["d"], a["k"], a["v"], a["kvd"],
                                      a["ks"], a["vs"], a["T"], a["idx"], a["count"], a["ms"], a["sc"], a["o"],
-                                     a["lse"], None)
+                                     a["lse"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -127,6 +133,9 @@ def sparse(lib, **kw):
     (dict(o=MIS), hs2.HS2_ERR_ALIGN),
     (dict(lse=A + 2), hs2.HS2_ERR_ALIGN),
     (dict(T=0), hs2.HS2_ERR_SHAPE),
+    (dict(ws=None), hs2.HS2_ERR_WORKSPACE),
+    (dict(wsb=1024), hs2.HS2_ERR_WORKSPACE),
+    (dict(ws=A + 16), hs2.HS2_ERR_ALIGN),
 ])
 def test_sparse_rejects(lib, kw, code):
     assert sparse(lib, **kw) == code

@@ -43,10 +43,13 @@ def _random_sets(rng, B, n_q, T, sizes, max_sel, with_invalid):
     return idx, cnt
 
 
-@pytest.mark.parametrize("kv,H", [("bf16", 16), ("bf16", 4), ("e4m3", 16), ("f32", 4), ("f32", 16), ("bf16", 1)])
-def test_sparse_reuse_parity(kv, H):
-    say("sparse", kv, H)
-    B, n_q, T, max_sel = 2, 24, 3000, 1152
+# B * n_q = 48 takes the split form (128-key pieces merged by a second kernel), 80 one workgroup per query
+@pytest.mark.parametrize("kv,H,n_q", [("bf16", 16, 24), ("bf16", 4, 24), ("e4m3", 16, 24), ("f32", 4, 24),
+                                      ("f32", 16, 24), ("bf16", 1, 24), ("bf16", 16, 40), ("e4m3", 8, 40),
+                                      ("f32", 2, 40)])
+def test_sparse_reuse_parity(kv, H, n_q):
+    say("sparse", kv, H, n_q)
+    B, T, max_sel = 2, 3000, 1152
     inp = inputs.attention_inputs(B=B, n_q=n_q, T=T, H=H, d=256, kv=kv, n_sparse=0, seed=11, device=DEV)
     rng = np.random.default_rng(5)
     idx, cnt = _random_sets(rng, B, n_q, T, [0, 1, 5, 31, 32, 33, 100, 1152, 700, 17], max_sel, True)

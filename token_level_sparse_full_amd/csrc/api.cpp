@@ -157,20 +157,32 @@ int hs2_select_topk_window(const float* scores, int64_t ld_scores, int B, int n_
   return hip_status(hs2::launch_select(p, workspace, ws_bytes, (hipStream_t)stream), "hs2_select_topk_window");
 }
 
+size_t hs2_sparse_workspace_bytes(int B, int n_q, int H, int max_sel) {
+  if (B < 1 || n_q < 1 || !heads_ok(H) || max_sel < 1 || max_sel > HS2_MAX_SELECT) return 0;
+  return hs2::sparse_workspace_bytes(B, n_q, max_sel);
+}
+
 int hs2_sparse_attn_reuse(const void* q, int q_dtype, int B, int n_q, int H, int d, const void* k, const void* v,
                           int kv_dtype, const float* k_scale, const float* v_scale, int64_t T, const int32_t* idx,
-                          const int32_t* count, int max_sel, float sm_scale, void* o, float* lse, void* stream) {
+                          const int32_t* count, int max_sel, float sm_scale, void* o, float* lse, void* workspace,
+                          size_t ws_bytes, void* stream) {
   int rc = check_attn_common(q, q_dtype, B, n_q, H, d, k, v, kv_dtype, k_scale, v_scale, T, sm_scale, o, lse);
   if (rc != HS2_OK) return rc;
   if (!idx || !count) return fail(HS2_ERR_NULL, "idx and count are required");
   if (!aligned(idx, 4) || !aligned(count, 4)) return fail(HS2_ERR_ALIGN, "idx and count must be 4-byte aligned");
   if (max_sel < 1 || max_sel > HS2_MAX_SELECT) return fail(HS2_ERR_SHAPE, "max_sel must be in [1, %d]", HS2_MAX_SELECT);
+  const size_t need = hs2::sparse_workspace_bytes(B, n_q, max_sel);
+  if (need > 0) {
+    if (!workspace) return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if (!aligned(workspace, 256)) return fail(HS2_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (ws_bytes < need) return fail(HS2_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  }
   hs2::SparseParams p;
   p.q = q; p.k = k; p.v = v; p.k_scale = k_scale; p.v_scale = v_scale;
   p.idx = idx; p.count = count; p.o = o; p.lse = lse;
   p.B = B; p.n_q = n_q; p.H = H; p.T = T; p.max_sel = max_sel;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
-  return hip_status(hs2::launch_sparse_attn(p, kv_kind(q_dtype), kv_kind(kv_dtype), (hipStream_t)stream),
+  return hip_status(hs2::launch_sparse_attn(p, kv_kind(q_dtype), kv_kind(kv_dtype), workspace, (hipStream_t)stream),
                     "hs2_sparse_attn_reuse");
 }
 

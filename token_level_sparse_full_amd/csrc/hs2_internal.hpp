@@ -28,7 +28,8 @@ struct SparseParams {
   int max_sel;
   float scale_log2;  // sm_scale * log2(e)
 };
-hipError_t launch_sparse_attn(const SparseParams& p, int q_kind, int kv_kind, hipStream_t stream);
+size_t sparse_workspace_bytes(int B, int n_q, int max_sel);
+hipError_t launch_sparse_attn(const SparseParams& p, int q_kind, int kv_kind, void* ws, hipStream_t stream);
 
 struct SelectParams {
   const float* scores;

@@ -16,7 +16,10 @@
 //    contiguous bytes of a gathered row per load instruction); V rows are
 //    staged row-major in LDS and read back transposed;
 //  * e4m3 caches are widened to bf16 exactly in registers; the row scales
-//    multiply the logits (K) and are folded into P (V).
+//    multiply the logits (K) and are folded into P (V);
+//  * few queries (decode: B * n_q <= 64) would leave most CUs idle, so their
+//    selected sets are also split into 128-key pieces, one workgroup each,
+//    whose partial states (max, sum, unnormalised O) a second kernel merges.
 #include "attn_tile.hpp"
 #include "hs2_internal.hpp"
 
@@ -31,8 +34,43 @@ constexpr int kRedPitch = 260;
 constexpr int kRedBytes = (SP_WAVES * 16 * kRedPitch + 2 * SP_WAVES * 16) * 4;
 constexpr int kSmemBytes = (SP_WAVES * kWaveBytes > kRedBytes) ? SP_WAVES * kWaveBytes : kRedBytes;
 
-template <int KV, int H>
-__global__ __launch_bounds__(SP_THREADS, 2) void sparse_attn_kernel(const SparseParams p) {
+constexpr int SP_SPLIT_KEYS = 128;   // selected keys per workgroup in the split form
+constexpr int SP_SPLIT_MAXQ = 64;     // queries (B * n_q) up to which the set is split
+
+struct SparseWs {
+  float* m;   // [B*n_q][nsplit][16]
+  float* z;   // [B*n_q][nsplit][16]
+  float* o;   // [B*n_q][nsplit][16][256]
+  int nsplit;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// layout of the split workspace (base may be null: sizes only)
+size_t sparse_ws_layout(int B, int n_q, int max_sel, char* base, SparseWs* ws) {
+  const int64_t nq = (int64_t)B * n_q;
+  if (nq > SP_SPLIT_MAXQ) {
+    if (ws) *ws = SparseWs{nullptr, nullptr, nullptr, 1};
+    return 0;
+  }
+  const int nsplit = (max_sel + SP_SPLIT_KEYS - 1) / SP_SPLIT_KEYS;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* ptr = base ? base + off : nullptr;
+    off += align256(bytes);
+    return (float*)ptr;
+  };
+  SparseWs w;
+  w.m = take((size_t)nq * nsplit * 16 * 4);
+  w.z = take((size_t)nq * nsplit * 16 * 4);
+  w.o = take((size_t)nq * nsplit * 16 * kHeadDim * 4);
+  w.nsplit = nsplit;
+  if (ws) *ws = w;
+  return off;
+}
+
+template <int KV, int H, bool SPLIT>
+__global__ __launch_bounds__(SP_THREADS, 2) void sparse_attn_kernel(const SparseParams p, const SparseWs ws) {
   constexpr int STEP = TileCfg<KV>::STEP;
   constexpr int NMT = STEP / 16;
   constexpr int ROWB = (KV == KV_F32) ? 1024 : (KV == KV_BF16 ? 512 : 256);
@@ -64,7 +102,11 @@ __global__ __launch_bounds__(SP_THREADS, 2) void sparse_attn_kernel(const Sparse
 #pragma unroll
   for (int t = 0; t < 16; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int st = wave; st < nsteps; st += SP_WAVES) {
+  // split form: this workgroup takes the steps of keys [split * 128, split * 128 + 128)
+  const int split = SPLIT ? (int)blockIdx.y : 0;
+  const int st_first = SPLIT ? split * (SP_SPLIT_KEYS / STEP) : 0;
+  const int st_end = SPLIT ? min(nsteps, st_first + SP_SPLIT_KEYS / STEP) : nsteps;
+  for (int st = st_first + wave; st < st_end; st += SP_WAVES) {
     // ---- slot table of this step (key index or -1, scales)
     if (l < STEP) {
       const int pos = st * STEP + l;
@@ -150,6 +192,28 @@ __global__ __launch_bounds__(SP_THREADS, 2) void sparse_attn_kernel(const Sparse
 
   for (int e = tid; e < H * kHeadDim; e += SP_THREADS) {
     const int h = e / kHeadDim, d = e % kHeadDim;
+    if constexpr (SPLIT) {
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < SP_WAVES; ++w) M = fmaxf(M, red_m[w * 16 + h]);
+      float Z = 0.f, acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < SP_WAVES; ++w) {
+        const float mw = red_m[w * 16 + h];
+        if (mw != kNegInf) {
+          const float f = fast_exp2(mw - M);
+          Z += red_z[w * 16 + h] * f;
+          acc += red_o[(w * 16 + h) * kRedPitch + d] * f;
+        }
+      }
+      const int64_t pi = ((int64_t)qid * ws.nsplit + split) * 16 + h;
+      ws.o[pi * kHeadDim + d] = acc;
+      if (d == 0) {
+        ws.m[pi] = M;
+        ws.z[pi] = Z;
+      }
+      continue;
+    }
     float M = kNegInf;
 #pragma unroll
     for (int w = 0; w < SP_WAVES; ++w) M = fmaxf(M, red_m[w * 16 + h]);
@@ -173,27 +237,66 @@ __global__ __launch_bounds__(SP_THREADS, 2) void sparse_attn_kernel(const Sparse
   }
 }
 
+// Merge of the split partial states: workgroup (query, head), thread = dim.
+template <int QKIND>
+__global__ __launch_bounds__(256) void sparse_merge_kernel(const SparseParams p, const SparseWs ws) {
+  const int qid = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+  const int64_t b0 = (int64_t)qid * ws.nsplit * 16 + h;
+  float M = kNegInf;
+  for (int i = 0; i < ws.nsplit; ++i) M = fmaxf(M, ws.m[b0 + i * 16]);
+  float Z = 0.f, acc = 0.f;
+  for (int i = 0; i < ws.nsplit; ++i) {
+    const float mi = ws.m[b0 + i * 16];
+    if (mi != kNegInf) {
+      const float f = fast_exp2(mi - M);
+      Z += ws.z[b0 + i * 16] * f;
+      acc += ws.o[(b0 + i * 16) * kHeadDim + d] * f;
+    }
+  }
+  const float out = Z > 0.f ? acc / Z : 0.f;
+  const int64_t oi = ((int64_t)qid * gridDim.y + h) * kHeadDim + d;
+  if constexpr (QKIND == KV_F32)
+    ((float*)p.o)[oi] = out;
+  else
+    ((bf16*)p.o)[oi] = to_bf16(out);
+  if (d == 0 && p.lse) p.lse[(int64_t)qid * gridDim.y + h] = Z > 0.f ? (M + fast_log2(Z)) * kLn2 : kNegInf;
+}
+
+template <int KV, int H>
+void launch_h(const SparseParams& p, const SparseWs& ws, bool split, hipStream_t stream) {
+  const unsigned nq = (unsigned)(p.B * p.n_q);
+  if (split) {
+    hipLaunchKernelGGL((sparse_attn_kernel<KV, H, true>), dim3(nq, ws.nsplit), dim3(SP_THREADS), 0, stream, p, ws);
+    hipLaunchKernelGGL((sparse_merge_kernel<KV == KV_F32 ? KV_F32 : KV_BF16>), dim3(nq, H), dim3(256), 0, stream, p, ws);
+  } else {
+    hipLaunchKernelGGL((sparse_attn_kernel<KV, H, false>), dim3(nq), dim3(SP_THREADS), 0, stream, p, ws);
+  }
+}
+
 template <int KV>
-hipError_t launch_kv(const SparseParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.B * p.n_q)), block(SP_THREADS);
+hipError_t launch_kv(const SparseParams& p, const SparseWs& ws, bool split, hipStream_t stream) {
   switch (p.H) {
-    case 1: hipLaunchKernelGGL((sparse_attn_kernel<KV, 1>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((sparse_attn_kernel<KV, 2>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((sparse_attn_kernel<KV, 4>), grid, block, 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((sparse_attn_kernel<KV, 8>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((sparse_attn_kernel<KV, 16>), grid, block, 0, stream, p); break;
+    case 1: launch_h<KV, 1>(p, ws, split, stream); break;
+    case 2: launch_h<KV, 2>(p, ws, split, stream); break;
+    case 4: launch_h<KV, 4>(p, ws, split, stream); break;
+    case 8: launch_h<KV, 8>(p, ws, split, stream); break;
+    default: launch_h<KV, 16>(p, ws, split, stream); break;
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_sparse_attn(const SparseParams& p, int /*q_kind*/, int kv_kind, hipStream_t stream) {
+size_t sparse_workspace_bytes(int B, int n_q, int max_sel) { return sparse_ws_layout(B, n_q, max_sel, nullptr, nullptr); }
+
+hipError_t launch_sparse_attn(const SparseParams& p, int /*q_kind*/, int kv_kind, void* ws_ptr, hipStream_t stream) {
   if (p.B * p.n_q == 0) return hipSuccess;
+  SparseWs ws;
+  const bool split = sparse_ws_layout(p.B, p.n_q, p.max_sel, (char*)ws_ptr, &ws) > 0;
   switch (kv_kind) {
-    case KV_F32: return launch_kv<KV_F32>(p, stream);
-    case KV_BF16: return launch_kv<KV_BF16>(p, stream);
-    default: return launch_kv<KV_E4M3>(p, stream);
+    case KV_F32: return launch_kv<KV_F32>(p, ws, split, stream);
+    case KV_BF16: return launch_kv<KV_BF16>(p, ws, split, stream);
+    default: return launch_kv<KV_E4M3>(p, ws, split, stream);
   }
 }
 

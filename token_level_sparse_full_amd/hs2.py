@@ -31,7 +31,8 @@ _PROTOS = {
     "hs2_select_topk_window": (_i, [_vp, _i64, _i, _i, _i64, _i64, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "hs2_select_workspace_bytes": (_sz, [_i, _i, _i64, _i64]),
     "hs2_sparse_attn_reuse": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp, _i64, _vp, _vp, _i, _f, _vp, _vp,
-                                   _vp]),
+                                   _vp, _sz, _vp]),
+    "hs2_sparse_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "hs2_bridge_kv_proj": (_i, [_vp, _i64, _i, _vp, _vp, _i, _i, _vp, _vp, _i64, _vp, _sz, _vp]),
     "hs2_bridge_workspace_bytes": (_sz, [_i, _i, _i]),
     "hs2_status_str": (ctypes.c_char_p, [_i]),
@@ -92,6 +93,10 @@ def full_attn_workspace_bytes(B: int, n_q: int, H: int, T: int, kv_dtype: int) -
     return int(lib().hs2_full_attn_workspace_bytes(B, n_q, H, T, kv_dtype))
 
 
+def sparse_workspace_bytes(B: int, n_q: int, H: int, max_sel: int) -> int:
+    return int(lib().hs2_sparse_workspace_bytes(B, n_q, H, max_sel))
+
+
 def workspace(nbytes: int, device) -> torch.Tensor | None:
     """Device scratch of at least nbytes (torch's allocator returns 256-byte aligned blocks)."""
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device) if nbytes > 0 else None
@@ -142,7 +147,7 @@ def hs2_select_topk_window(scores, *, q_pos0: int, T: int, n_q: int | None = Non
 
 
 def hs2_sparse_attn_reuse(q, k, v, idx, count, *, sm_scale: float | None = None, k_scale=None, v_scale=None,
-                          o=None, lse=None, stream=None, want_lse: bool = True):
+                          o=None, lse=None, ws=None, stream=None, want_lse: bool = True):
     """Sparse layer over reused indices.  q [B,n_q,H,256]; idx [B,n_q,max_sel]; returns (o, lse)."""
     B, n_q, H, d = q.shape
     T = k.shape[1]
@@ -153,9 +158,12 @@ def hs2_sparse_attn_reuse(q, k, v, idx, count, *, sm_scale: float | None = None,
         o = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, n_q, H), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(sparse_workspace_bytes(B, n_q, H, max_sel), q.device)
     rc = lib().hs2_sparse_attn_reuse(_ptr(q), _dtype_code(q), B, n_q, H, d, _ptr(k), _ptr(v), _dtype_code(k),
                                      _ptr(k_scale), _ptr(v_scale), T, _ptr(idx), _ptr(count), max_sel, sm_scale,
-                                     _ptr(o), _ptr(lse), _stream(stream))
+                                     _ptr(o), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(),
+                                     _stream(stream))
     check("hs2_sparse_attn_reuse", rc)
     return o, lse
 
