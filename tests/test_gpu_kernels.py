@@ -97,7 +97,7 @@ def test_select_parity(q_pos0, n_q, T):
     for b in range(B):
         for i in range(n_q):
             n = q_pos0 + i + 1
-            mode = (b * n_q + i) % 5
+            mode = (b * n_q + i) % 6
             if mode == 0:      # smooth random
                 row = rng.random(n, dtype=np.float32) / n
             elif mode == 1:    # heavy ties
@@ -107,8 +107,10 @@ def test_select_parity(q_pos0, n_q, T):
             elif mode == 3:    # zeros with a few spikes
                 row = np.zeros(n, dtype=np.float32)
                 row[rng.integers(0, n, size=min(n, 50))] = 1.0
-            else:              # near-uniform: differences only in low mantissa bits
+            elif mode == 4:    # near-uniform: differences only in low mantissa bits
                 row = (np.float32(1.0 / 4096) * (1 + rng.integers(0, 16, n) * np.float32(2 ** -20))).astype(np.float32)
+            else:              # spread over many octaves
+                row = (rng.lognormal(0.0, 3.0, n) / n).astype(np.float32)
             sc[b, i, :n] = row
     _select_case(sc, q_pos0, T, 128, 1024)
 

@@ -11,7 +11,7 @@
 // above tau plus the first (topk - #above) candidates equal to tau in index
 // order, followed by the window; this is already ascending.
 //
-// Design: one 1024-thread workgroup per query row.  Usually the row is read
+// Design: one 512-thread workgroup per query row.  Usually the row is read
 // once (sampled path below); otherwise, as a fallback:  scores are >= 0, so their
 // float32 bit patterns order like unsigned integers.  A first pass finds the
 // smallest and largest candidate pattern; the bits above their highest
@@ -27,7 +27,7 @@
 namespace hs2 {
 namespace {
 
-constexpr int SEL_THREADS = 1024;
+constexpr int SEL_THREADS = 512;
 constexpr int SEL_WAVES = SEL_THREADS / kWave;
 constexpr int SEL_DIGIT = 11;
 constexpr int SEL_BINS = 1 << SEL_DIGIT;
@@ -35,6 +35,7 @@ constexpr int SEL_BINS = 1 << SEL_DIGIT;
 struct SelShared {
   int hist[SEL_BINS];
   int wave_tot[SEL_WAVES];
+  int wave_tot2[2][SEL_WAVES];
   uint32_t wave_u[2 * SEL_WAVES];
   int pick_digit;
   int pick_above;
@@ -42,14 +43,46 @@ struct SelShared {
 
 __device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
 
-// Inclusive scan of v over the wave.
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
+// v plus the value DPP control CTRL moves into this lane (0 where it moves
+// none: lanes shifted in from outside the row, rows outside ROWMASK).
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ int dpp_add(int v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xf, false);
+}
+
+// Inclusive scan of v over the wave: Hillis-Steele steps inside each 16-lane
+// row (row_shr 1, 2, 4, 8), then the row totals are carried across rows
+// (row_bcast 15 into rows 1 and 3, row_bcast 31 into rows 2 and 3).
+__device__ __forceinline__ int wave_incl_scan(int v, int /*lane*/) {
+  v = dpp_add<0x111>(v);
+  v = dpp_add<0x112>(v);
+  v = dpp_add<0x114>(v);
+  v = dpp_add<0x118>(v);
+  v = dpp_add<0x142, 0xa>(v);
+  v = dpp_add<0x143, 0xc>(v);
   return v;
+}
+
+// Exclusive block-wide scan with a single barrier.  The wave totals go to one
+// of two slots, alternating per call (par, uniform over the block): a slot is
+// rewritten two scans later, after every thread has passed the barrier of
+// the scan in between and so has finished reading it.
+__device__ __forceinline__ int block_excl_scan1(int v, int tid, SelShared& sh, int& par, int& total) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int inc = wave_incl_scan(v, lane);
+  int* wt = sh.wave_tot2[par];
+  if (lane == 63) wt[wave] = inc;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < SEL_WAVES; ++w) {
+    const int t = wt[w];
+    before += (w < wave) ? t : 0;
+    total += t;
+  }
+  par ^= 1;
+  return before + inc - v;
 }
 
 // Exclusive block-wide scan; returns the exclusive prefix of v and the block total.
@@ -88,59 +121,111 @@ __device__ __forceinline__ int block_excl_scan_n(int v, int tid, SelShared& sh, 
   return before + inc - v;
 }
 
+// Digit pick of one radix pass.  sh.hist holds the counts of nbins digits;
+// thread t owns the SEL_BINS / SEL_THREADS digits below nbins - per * t, so
+// the block scan runs from the top digit down.  The digit that holds the
+// krem-th largest value goes to sh.pick_digit, the count above it to
+// sh.pick_above (visible to every thread on return).
+__device__ __forceinline__ void pick_digit(SelShared& sh, int nbins, int krem, int& par) {
+  constexpr int PERB = SEL_BINS / SEL_THREADS;
+  const int tid = threadIdx.x;
+  int c[PERB];
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < PERB; ++i) {
+    const int d = nbins - 1 - PERB * tid - i;
+    c[i] = d >= 0 ? sh.hist[d] : 0;
+    mine += c[i];
+  }
+  int total;
+  int before = block_excl_scan1(mine, tid, sh, par, total);
+#pragma unroll
+  for (int i = 0; i < PERB; ++i) {
+    const int d = nbins - 1 - PERB * tid - i;
+    if (d >= 0 && before < krem && krem <= before + c[i]) {
+      sh.pick_digit = d;
+      sh.pick_above = before;
+    }
+    before += c[i];
+  }
+  __syncthreads();
+}
+
 // ---- sampled single-read path (the common case) ----------------------------
 // Rows up to SEL_CAP candidates, and rows whose candidates at or above a
-// threshold estimated from a strided sample number between topk and SEL_CAP,
+// threshold estimated from a sample of the row number between topk and SEL_CAP,
 // are selected from one read of the row: the candidates at or above the
 // estimate are compacted into LDS in index order, and tau is found there.
 // Anything else (a sample that misleads, e.g. many equal scores) falls back to
 // the exact multi-pass radix below, so the result never depends on the sample.
 constexpr int SEL_CAP = 8192;      // candidates kept in LDS (64 KB)
-constexpr int SEL_SAMPLE = 4096;   // strided sample of a long row
+constexpr int SEL_SAMPLE = 4096;   // sampled scores of a long row (128 blocks of 32)
+constexpr int SEL_SPT = SEL_SAMPLE / SEL_THREADS;  // sampled scores per thread
+static_assert(SEL_SAMPLE % (4 * SEL_THREADS) == 0 && SEL_CAP >= 32, "whole float4s per thread");
 
-// The k-th largest of the n bit patterns v[0..n-1] in LDS (k >= 1, n >= k):
-// returns tau and how many of the values equal to tau rank inside the top k.
-__device__ void lds_radix_select(const uint32_t* v, int n, int k, SelShared& sh, uint32_t& tau, int& need_eq) {
+// Block-wide minimum and maximum of the per-thread lo and hi (returned to
+// every thread); ends with a barrier, which also orders the LDS writes made
+// before the call.
+__device__ __forceinline__ void block_min_max(uint32_t& lo, uint32_t& hi, SelShared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, kWave));
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, kWave));
+  }
+  if (lane == 0) {
+    sh.wave_u[wave] = hi;
+    sh.wave_u[SEL_WAVES + wave] = lo;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < SEL_WAVES; ++w) {
+    hi = max(hi, sh.wave_u[w]);
+    lo = min(lo, sh.wave_u[SEL_WAVES + w]);
+  }
+}
+
+// The k-th largest of the n bit patterns v[0..n-1] in LDS (k >= 1, n >= k),
+// all of them in [lo, hi]: returns tau and how many of the values equal to
+// tau rank inside the top k.  The bits above the highest bit where lo and hi
+// differ are common to every value, so the 11-bit digits start right below
+// them and split the actual range (few values share a histogram bin, which
+// keeps the LDS atomics apart).  After max_pass digits the search stops:
+// tau then has its lower bits 0, a lower bound of the k-th largest that only
+// the values sharing all of its higher bits pass.
+__device__ void lds_radix_select(const uint32_t* v, int n, int k, uint32_t lo, uint32_t hi, int max_pass,
+                                 SelShared& sh, int& par, uint32_t& tau, int& need_eq) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0u;
   int krem = k;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int w = pass == 2 ? 10 : 11;
+  if (lo == hi) {  // every value equal
+    tau = lo;
+    need_eq = krem;
+    return;
+  }
+  int shift = 32 - __builtin_clz(lo ^ hi);
+  uint64_t prefix = (uint64_t)hi >> shift << shift;
+  for (int pass = 0; shift > 0 && pass < max_pass; ++pass) {
+    const int w = min(SEL_DIGIT, shift);
+    shift -= w;
     const int nbins = 1 << w;
-    // 64-bit shifts: shift + w is 32 on the first pass
-    const uint64_t want = (uint64_t)prefix >> (shift + w);
+    // 64-bit shifts: shift + w may be 32
+    const uint64_t want = prefix >> (shift + w);
     for (int b = tid; b < nbins; b += SEL_THREADS) sh.hist[b] = 0;
     __syncthreads();
     for (int j = tid; j < n; j += SEL_THREADS) {
-      const uint32_t u = v[j];
-      if (((uint64_t)u >> (shift + w)) == want) atomicAdd(&sh.hist[(u >> shift) & (nbins - 1)], 1);
+      const uint64_t u = v[j];
+      if ((u >> (shift + w)) == want) atomicAdd(&sh.hist[(u >> shift) & (nbins - 1)], 1);
     }
     __syncthreads();
-    const int d0 = nbins - 1 - 2 * tid, d1 = d0 - 1;
-    const int c0 = d0 >= 0 ? sh.hist[d0] : 0;
-    const int c1 = d1 >= 0 ? sh.hist[d1] : 0;
-    int total;
-    const int before = block_excl_scan(c0 + c1, tid, sh, total);
-    if (d0 >= 0) {
-      if (before < krem && krem <= before + c0) {
-        sh.pick_digit = d0;
-        sh.pick_above = before;
-      } else if (d1 >= 0 && before + c0 < krem && krem <= before + c0 + c1) {
-        sh.pick_digit = d1;
-        sh.pick_above = before + c0;
-      }
-    }
-    __syncthreads();
-    prefix |= (uint32_t)sh.pick_digit << shift;
+    pick_digit(sh, nbins, krem, par);
+    prefix |= (uint64_t)sh.pick_digit << shift;
     krem -= sh.pick_above;
-    __syncthreads();
   }
-  tau = prefix;
+  tau = (uint32_t)prefix;
   need_eq = krem;
 }
 
-__global__ __launch_bounds__(SEL_THREADS) void select_kernel(const SelectParams p) {
+__global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(const SelectParams p) {
   __shared__ SelShared sh;
   __shared__ uint32_t cval[SEL_CAP];
   __shared__ int32_t cidx[SEL_CAP];
@@ -153,6 +238,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const SelectParams 
   int32_t* out = p.idx + (int64_t)qid * max_sel;
   const float* row = p.scores + (int64_t)qid * p.ld_scores;
   const int64_t n_cand = n > p.window ? n - p.window : 0;
+  int par = 0;  // slot of the next single-barrier scan
 
   if (n_cand <= p.topk) {  // every key 0..p is selected
     for (int j = tid; j < max_sel; j += SEL_THREADS) out[j] = j < n ? j : -1;
@@ -163,74 +249,145 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const SelectParams 
   // ---- sampled path: threshold estimate (0 = keep everything for short rows)
   uint32_t u_est = 0u;
   if (n_cand > SEL_CAP) {
-    for (int i = tid; i < SEL_SAMPLE; i += SEL_THREADS) cval[i] = fbits(row[(int64_t)i * n_cand / SEL_SAMPLE]);
-    __syncthreads();
-    // aim at about 2 topk candidates at or above the estimate
+    // 128 evenly spaced blocks of 32 consecutive scores, each one 128-byte
+    // line: about 3 % of the row's bytes (single strided values would touch
+    // up to every line of the row)
+    uint32_t smin = 0xFFFFFFFFu, smax = 0u;
+#pragma unroll
+    for (int h = 0; h < SEL_SPT / 4; ++h) {
+      const int i = tid + h * SEL_THREADS;
+      const int64_t blk = i >> 3;
+      const int64_t start = (blk * (n_cand - 32) / (SEL_SAMPLE / 32 - 1)) & ~(int64_t)31;
+      const f32x4 v = *(const f32x4*)(row + start + 4 * (i & 7));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t u = fbits(v[e]);
+        cval[4 * i + e] = u;
+        smin = min(smin, u);
+        smax = max(smax, u);
+      }
+    }
+    block_min_max(smin, smax, sh);
+    // aim at about 2 topk candidates at or above the estimate; two digits
+    // (22 bits below the sample's common prefix) are precise enough
     const int r = (int)min<int64_t>(SEL_SAMPLE, max<int64_t>(1, (2 * (int64_t)p.topk * SEL_SAMPLE + n_cand - 1) / n_cand));
     int unused;
-    lds_radix_select(cval, SEL_SAMPLE, r, sh, u_est, unused);
+    lds_radix_select(cval, SEL_SAMPLE, r, smin, smax, 2, sh, par, u_est, unused);
   }
-  // one read of the row: candidates >= u_est into LDS, in index order.  Each
-  // thread takes 16 consecutive candidates per round (one block scan per 16K
-  // candidates), and the loads of the next round are issued before the scan.
+  // one read of the row: candidates >= u_est into LDS, in index order.  A
+  // round covers 8192 candidates: wave wv takes 1024 consecutive ones, its
+  // kept positions come from ballots and mbcnt, and one barrier orders the
+  // waves.  The loads of the next round are issued before the barrier.  The
+  // smallest and largest kept pattern bound the exact search below.
   constexpr int PER = 16;
-  auto load16 = [&](int64_t j0, uint32_t (&u)[PER]) {
-    if (j0 + PER - 1 < n_cand) {
+  constexpr int ROUND = PER * SEL_THREADS;  // candidates per round
+  const int lane = tid & 63, wv = tid >> 6;
+  // load q of lane l is the float4 at 256 q + 4 l of the wave's piece
+  auto load16 = [&](int64_t base, uint32_t (&u)[PER]) {
 #pragma unroll
-      for (int q = 0; q < PER / 4; ++q) {
-        const f32x4 v = *(const f32x4*)(row + j0 + 4 * q);
+    for (int q = 0; q < PER / 4; ++q) {
+      const int64_t j = base + 1024 * wv + 256 * q + 4 * lane;
+      if (j + 3 < n_cand) {
+        const f32x4 v = *(const f32x4*)(row + j);
 #pragma unroll
         for (int e = 0; e < 4; ++e) u[4 * q + e] = fbits(v[e]);
-      }
-    } else {
+      } else {
 #pragma unroll
-      for (int e = 0; e < PER; ++e) u[e] = (j0 + e < n_cand) ? fbits(row[j0 + e]) : 0u;
+        for (int e = 0; e < 4; ++e) u[4 * q + e] = (j + e < n_cand) ? fbits(row[j + e]) : 0u;
+      }
     }
   };
   int kept = 0;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   uint32_t ucur[PER], unext[PER];
-  load16(PER * (int64_t)tid, ucur);
-  for (int64_t base = 0; base < n_cand; base += PER * SEL_THREADS) {
-    const int64_t j0 = base + PER * (int64_t)tid;
-    if (base + PER * SEL_THREADS < n_cand) load16(j0 + PER * SEL_THREADS, unext);
-    int c = 0;
+  load16(0, ucur);
+  for (int64_t base = 0; base < n_cand; base += ROUND) {
+    if (base + ROUND < n_cand) load16(base + ROUND, unext);
+    uint64_t bal[PER];
+    int wtot = 0;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) c += (j0 + e < n_cand && ucur[e] >= u_est) ? 1 : 0;
-    int tot;
-    int pos = kept + block_excl_scan(c, tid, sh, tot);
+    for (int q = 0; q < PER / 4; ++q)
 #pragma unroll
-    for (int e = 0; e < PER; ++e)
-      if (j0 + e < n_cand && ucur[e] >= u_est) {
-        if (pos < SEL_CAP) {
-          cval[pos] = ucur[e];
-          cidx[pos] = (int32_t)(j0 + e);
-        }
-        ++pos;
+      for (int e = 0; e < 4; ++e) {
+        const int64_t j = base + 1024 * wv + 256 * q + 4 * lane + e;
+        const bool keep = j < n_cand && ucur[4 * q + e] >= u_est;
+        bal[4 * q + e] = __ballot(keep);
+        wtot += __popcll(bal[4 * q + e]);
+        kmin = min(kmin, keep ? ucur[4 * q + e] : 0xFFFFFFFFu);
+        kmax = max(kmax, keep ? ucur[4 * q + e] : 0u);
       }
+    int* wt = sh.wave_tot2[par];
+    if (lane == 0) wt[wv] = wtot;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < SEL_WAVES; ++w) {
+      const int t = wt[w];
+      before += (w < wv) ? t : 0;
+      tot += t;
+    }
+    par ^= 1;
+    int pos = kept + before;
+#pragma unroll
+    for (int q = 0; q < PER / 4; ++q) {
+      int p = pos;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        p += __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[4 * q + e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal[4 * q + e], 0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if ((bal[4 * q + e] >> lane) & 1) {
+          if (p < SEL_CAP) {
+            cval[p] = ucur[4 * q + e];
+            cidx[p] = (int32_t)(base + 1024 * wv + 256 * q + 4 * lane + e);
+          }
+          ++p;
+        }
+        pos += __popcll(bal[4 * q + e]);
+      }
+    }
     kept += tot;
 #pragma unroll
     for (int e = 0; e < PER; ++e) ucur[e] = unext[e];
   }
-  __syncthreads();
+  block_min_max(kmin, kmax, sh);
   if (kept >= p.topk && kept <= SEL_CAP) {
     // every pick is at or above u_est (at least topk candidates are), so the
     // exact tau of the row is the topk-th largest of the kept ones
     uint32_t tau;
     int need_eq;
-    lds_radix_select(cval, kept, p.topk, sh, tau, need_eq);
-    int eq_seen = 0, sel_seen = 0;
-    for (int base = 0; base < kept; base += SEL_THREADS) {
-      const int j = base + tid;
-      const uint32_t u = j < kept ? cval[j] : 0u;
-      const bool eq = j < kept && u == tau;
-      int eq_total;
-      const int eq_rank = eq_seen + block_excl_scan(eq ? 1 : 0, tid, sh, eq_total);
-      const bool sel = j < kept && (u > tau || (eq && eq_rank < need_eq));
-      int sel_total;
-      const int opos = sel_seen + block_excl_scan(sel ? 1 : 0, tid, sh, sel_total);
-      if (sel && opos < p.topk) out[opos] = cidx[j];
-      eq_seen += eq_total;
-      sel_seen += sel_total;
+    lds_radix_select(cval, kept, p.topk, kmin, kmax, 3, sh, par, tau, need_eq);
+    // a pick's output slot is the number of picks before it: the values above
+    // tau before it plus the first need_eq ties.  One scan of the packed
+    // counts (above << 16 | ties) per 4 * SEL_THREADS kept values.
+    int gt_seen = 0, eq_seen = 0;
+    for (int base = 0; base < kept; base += 4 * SEL_THREADS) {
+      const int j0 = base + 4 * tid;
+      uint32_t u[4];
+      int ngt = 0, neq = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u[e] = j0 + e < kept ? cval[j0 + e] : 0u;
+        ngt += (j0 + e < kept && u[e] > tau) ? 1 : 0;
+        neq += (j0 + e < kept && u[e] == tau) ? 1 : 0;
+      }
+      int tot;
+      const int pre = block_excl_scan1((ngt << 16) | neq, tid, sh, par, tot);
+      int gt_b = gt_seen + (pre >> 16), eq_b = eq_seen + (pre & 0xffff);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (j0 + e >= kept) continue;
+        if (u[e] > tau) {
+          const int opos = gt_b + min(eq_b, need_eq);
+          if (opos < p.topk) out[opos] = cidx[j0 + e];
+          ++gt_b;
+        } else if (u[e] == tau) {
+          if (eq_b < need_eq && gt_b + eq_b < p.topk) out[gt_b + eq_b] = cidx[j0 + e];
+          ++eq_b;
+        }
+      }
+      gt_seen += tot >> 16;
+      eq_seen += tot & 0xffff;
     }
     for (int w = tid; w < p.window; w += SEL_THREADS) out[p.topk + w] = (int32_t)(n_cand + w);
     if (tid == 0) p.count[qid] = max_sel;
@@ -304,22 +461,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const SelectParams 
         if ((u >> (shift + w)) == want) atomicAdd(&sh.hist[(u >> shift) & (nbins - 1)], 1);
       }
       __syncthreads();
-      // scan the bins from the top digit down; thread t owns digits nbins-1-2t, nbins-2-2t
-      const int d0 = nbins - 1 - 2 * tid, d1 = d0 - 1;
-      const int c0 = d0 >= 0 ? sh.hist[d0] : 0;
-      const int c1 = d1 >= 0 ? sh.hist[d1] : 0;
-      int total;
-      const int before = block_excl_scan(c0 + c1, tid, sh, total);
-      if (d0 >= 0) {
-        if (before < krem && krem <= before + c0) {
-          sh.pick_digit = d0;
-          sh.pick_above = before;
-        } else if (d1 >= 0 && before + c0 < krem && krem <= before + c0 + c1) {
-          sh.pick_digit = d1;
-          sh.pick_above = before + c0;
-        }
-      }
-      __syncthreads();
+      pick_digit(sh, nbins, krem, par);
       prefix |= (uint64_t)sh.pick_digit << shift;
       krem -= sh.pick_above;
       __syncthreads();
