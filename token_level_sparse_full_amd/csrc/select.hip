@@ -11,14 +11,18 @@
 // above tau plus the first (topk - #above) candidates equal to tau in index
 // order, followed by the window; this is already ascending.
 //
-// Design: one 512-thread workgroup per query row.  Usually the row is read
-// once (sampled path below); otherwise, as a fallback:  scores are >= 0, so their
-// float32 bit patterns order like unsigned integers.  A first pass finds the
-// smallest and largest candidate pattern; the bits above their highest
-// differing bit are common to all candidates, so the radix digits (11 bits,
-// LDS histograms) start right below them and split the actual value range
-// instead of the (nearly constant) exponent.  The compaction pass is a
-// block-wide ordered scan that stops as soon as topk candidates are out.
+// Design: one 512-thread workgroup per query row, four rows per CU.  Scores
+// are >= 0, so their float32 bit patterns order like unsigned integers.
+// Usually the row is read once: a 4096-score sample (128 blocks of 32) gives
+// a threshold estimate that about 2 topk candidates reach; those are
+// compacted into LDS in index order (up to 4096 of them) and an LDS radix
+// select finds tau among them exactly.  The radix digits (10 bits, LDS
+// histograms) start right below the bits common to the smallest and largest
+// value searched, so they split the actual value range instead of the nearly
+// constant exponent.  When the estimate keeps fewer than topk or more than
+// 4096 candidates, an exact path reads the row again: a min/max pass, radix
+// histogram passes, and a block-wide ordered compaction that stops as soon as
+// topk candidates are out.
 // Few long rows (at most 64 rows, at least 32768 candidates, the decode case)
 // go to a multi-workgroup version of the same selection (below).
 #include "hs2_device.hpp"
@@ -29,7 +33,7 @@ namespace {
 
 constexpr int SEL_THREADS = 512;
 constexpr int SEL_WAVES = SEL_THREADS / kWave;
-constexpr int SEL_DIGIT = 11;
+constexpr int SEL_DIGIT = 10;
 constexpr int SEL_BINS = 1 << SEL_DIGIT;
 
 struct SelShared {
@@ -158,7 +162,7 @@ __device__ __forceinline__ void pick_digit(SelShared& sh, int nbins, int krem, i
 // estimate are compacted into LDS in index order, and tau is found there.
 // Anything else (a sample that misleads, e.g. many equal scores) falls back to
 // the exact multi-pass radix below, so the result never depends on the sample.
-constexpr int SEL_CAP = 8192;      // candidates kept in LDS (64 KB)
+constexpr int SEL_CAP = 4096;      // candidates kept in LDS (32 KB: four rows share a CU)
 constexpr int SEL_SAMPLE = 4096;   // sampled scores of a long row (128 blocks of 32)
 constexpr int SEL_SPT = SEL_SAMPLE / SEL_THREADS;  // sampled scores per thread
 static_assert(SEL_SAMPLE % (4 * SEL_THREADS) == 0 && SEL_CAP >= 32, "whole float4s per thread");
@@ -188,7 +192,7 @@ __device__ __forceinline__ void block_min_max(uint32_t& lo, uint32_t& hi, SelSha
 // The k-th largest of the n bit patterns v[0..n-1] in LDS (k >= 1, n >= k),
 // all of them in [lo, hi]: returns tau and how many of the values equal to
 // tau rank inside the top k.  The bits above the highest bit where lo and hi
-// differ are common to every value, so the 11-bit digits start right below
+// differ are common to every value, so the 10-bit digits start right below
 // them and split the actual range (few values share a histogram bin, which
 // keeps the LDS atomics apart).  After max_pass digits the search stops:
 // tau then has its lower bits 0, a lower bound of the k-th largest that only
@@ -225,7 +229,7 @@ __device__ void lds_radix_select(const uint32_t* v, int n, int k, uint32_t lo, u
   need_eq = krem;
 }
 
-__global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(const SelectParams p) {
+__global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void select_kernel(const SelectParams p) {
   __shared__ SelShared sh;
   __shared__ uint32_t cval[SEL_CAP];
   __shared__ int32_t cidx[SEL_CAP];
@@ -268,25 +272,28 @@ __global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(4))
       }
     }
     block_min_max(smin, smax, sh);
-    // aim at about 2 topk candidates at or above the estimate; two digits
-    // (22 bits below the sample's common prefix) are precise enough
-    const int r = (int)min<int64_t>(SEL_SAMPLE, max<int64_t>(1, (2 * (int64_t)p.topk * SEL_SAMPLE + n_cand - 1) / n_cand));
+    // aim at about 2 topk candidates at or above the estimate (less for a
+    // topk above SEL_CAP / 3, to stay inside the LDS); two digits (20 bits
+    // below the sample's common prefix) are precise enough
+    const int64_t aim = min<int64_t>(2 * (int64_t)p.topk, ((int64_t)p.topk + SEL_CAP) / 2);
+    const int r = (int)min<int64_t>(SEL_SAMPLE, max<int64_t>(1, (aim * SEL_SAMPLE + n_cand - 1) / n_cand));
     int unused;
     lds_radix_select(cval, SEL_SAMPLE, r, smin, smax, 2, sh, par, u_est, unused);
   }
   // one read of the row: candidates >= u_est into LDS, in index order.  A
-  // round covers 8192 candidates: wave wv takes 1024 consecutive ones, its
+  // round covers 4096 candidates: wave wv takes PIECE consecutive ones, its
   // kept positions come from ballots and mbcnt, and one barrier orders the
   // waves.  The loads of the next round are issued before the barrier.  The
   // smallest and largest kept pattern bound the exact search below.
-  constexpr int PER = 16;
+  constexpr int PER = 8;
   constexpr int ROUND = PER * SEL_THREADS;  // candidates per round
+  constexpr int PIECE = PER * kWave;        // consecutive candidates of one wave per round
   const int lane = tid & 63, wv = tid >> 6;
   // load q of lane l is the float4 at 256 q + 4 l of the wave's piece
   auto load16 = [&](int64_t base, uint32_t (&u)[PER]) {
 #pragma unroll
     for (int q = 0; q < PER / 4; ++q) {
-      const int64_t j = base + 1024 * wv + 256 * q + 4 * lane;
+      const int64_t j = base + PIECE * wv + 256 * q + 4 * lane;
       if (j + 3 < n_cand) {
         const f32x4 v = *(const f32x4*)(row + j);
 #pragma unroll
@@ -309,7 +316,7 @@ __global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(4))
     for (int q = 0; q < PER / 4; ++q)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t j = base + 1024 * wv + 256 * q + 4 * lane + e;
+        const int64_t j = base + PIECE * wv + 256 * q + 4 * lane + e;
         const bool keep = j < n_cand && ucur[4 * q + e] >= u_est;
         bal[4 * q + e] = __ballot(keep);
         wtot += __popcll(bal[4 * q + e]);
@@ -339,7 +346,7 @@ __global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(4))
         if ((bal[4 * q + e] >> lane) & 1) {
           if (p < SEL_CAP) {
             cval[p] = ucur[4 * q + e];
-            cidx[p] = (int32_t)(base + 1024 * wv + 256 * q + 4 * lane + e);
+            cidx[p] = (int32_t)(base + PIECE * wv + 256 * q + 4 * lane + e);
           }
           ++p;
         }
