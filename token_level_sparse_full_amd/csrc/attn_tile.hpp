@@ -53,80 +53,121 @@ __device__ __forceinline__ void load_qfrag(const void* qrow, bool ok, int g, QFr
   }
 }
 
-// One 16x16 tile of S^T for the 16 keys of this lane's tile row (`krow` is
-// the K row of key c16 of the tile, or nullptr for an absent key).
+// Register counts of one tile's K fragment and of one step's V rows per lane
+// (loaded first, consumed later, so that the loads of one step can be in
+// flight while the previous step computes).
 template <int KV>
-__device__ __forceinline__ f32x4 s_tile(const void* krow, int g, const QFrag& qf) {
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const bool ok = krow != nullptr;
+struct FragRegs {
+  static constexpr int K = (KV == KV_E4M3) ? 4 : (KV == KV_BF16 ? 8 : 16);  // u32x4 per 16-key tile
+  static constexpr int V = (KV == KV_E4M3) ? 8 : 16;                        // u32x4 per step
+};
+
+// This lane's K fragment of one 16-key tile; `krow` is the K row of key c16
+// of the tile and must be readable (an absent key is given some valid row,
+// and its logit masked later, so the loads need no branch).
+template <int KV>
+__device__ __forceinline__ void load_k_tile(const void* krow, int g, u32x4* kr) {
   if constexpr (KV == KV_F32) {
     const float* kp = (const float*)krow;
-    f32x4 kf[16];
 #pragma unroll
-    for (int cs = 0; cs < 16; ++cs) kf[cs] = ok ? *(const f32x4*)(kp + 16 * cs + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int cs = 0; cs < 16; ++cs)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc = mfma16_f32(kf[cs][j], qf.f[cs][j], acc);
+    for (int cs = 0; cs < 16; ++cs) kr[cs] = *(const u32x4*)(kp + 16 * cs + 4 * g);
   } else if constexpr (KV == KV_BF16) {
     const bf16* kp = (const bf16*)krow;
-    bf16x8 kf[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) kf[s] = ok ? as_bf16x8(*(const u32x4*)(kp + 32 * s + 8 * g)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-#pragma unroll
-    for (int s = 0; s < 8; ++s) acc = mfma16(kf[s], qf.b[s], acc);
+    for (int s = 0; s < 8; ++s) kr[s] = *(const u32x4*)(kp + 32 * s + 8 * g);
   } else {
     const uint8_t* kp = (const uint8_t*)krow;
-    u32x4 raw[4];
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) raw[s2] = ok ? *(const u32x4*)(kp + 64 * s2 + 16 * g) : u32x4{0u, 0u, 0u, 0u};
+    for (int s2 = 0; s2 < 4; ++s2) kr[s2] = *(const u32x4*)(kp + 64 * s2 + 16 * g);
+  }
+}
+
+// One 16x16 tile of S^T from a loaded K fragment.
+template <int KV>
+__device__ __forceinline__ f32x4 s_from_k(const u32x4* kr, const QFrag& qf) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (KV == KV_F32) {
+#pragma unroll
+    for (int cs = 0; cs < 16; ++cs) {
+      const f32x4 kf = __builtin_bit_cast(f32x4, kr[cs]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = mfma16_f32(kf[j], qf.f[cs][j], acc);
+    }
+  } else if constexpr (KV == KV_BF16) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc = mfma16(as_bf16x8(kr[s]), qf.b[s], acc);
+  } else {
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
-      acc = mfma16(e4m3x8_to_bf16(raw[s2][0], raw[s2][1]), qf.b[2 * s2], acc);
-      acc = mfma16(e4m3x8_to_bf16(raw[s2][2], raw[s2][3]), qf.b[2 * s2 + 1], acc);
+      acc = mfma16(e4m3x8_to_bf16(kr[s2][0], kr[s2][1]), qf.b[2 * s2], acc);
+      acc = mfma16(e4m3x8_to_bf16(kr[s2][2], kr[s2][3]), qf.b[2 * s2 + 1], acc);
     }
   }
   return acc;
 }
 
-// Stage the V rows of one step into LDS.  rowptr(slot) returns the V row of
-// step slot `slot` (0..STEP-1) or nullptr for an absent key.
-template <int KV, typename RowPtr>
-__device__ __forceinline__ void stage_v(char* stage, int l, RowPtr rowptr) {
+// One 16x16 tile of S^T for the 16 keys of this lane's tile row (`krow` is
+// nullptr for an absent key: zeros).
+template <int KV>
+__device__ __forceinline__ f32x4 s_tile(const void* krow, int g, const QFrag& qf) {
+  u32x4 kr[FragRegs<KV>::K];
+#pragma unroll
+  for (int i = 0; i < FragRegs<KV>::K; ++i) kr[i] = u32x4{0u, 0u, 0u, 0u};
+  if (krow != nullptr) load_k_tile<KV>(krow, g, kr);
+  return s_from_k<KV>(kr, qf);
+}
+
+// This lane's share of the V rows of one step.  rowptr(slot) returns the V
+// row of step slot `slot` (0..STEP-1); with NULLABLE it may return nullptr
+// for an absent key (zeros), else it must return a readable row.
+template <int KV, bool NULLABLE, typename RowPtr>
+__device__ __forceinline__ void load_v_rows(int l, RowPtr rowptr, u32x4* vr) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  auto ld = [&](const char* vp, int off) -> u32x4 {
+    if constexpr (NULLABLE) return vp ? *(const u32x4*)(vp + off) : z;
+    return *(const u32x4*)(vp + off);
+  };
+  if constexpr (KV == KV_F32) {
+#pragma unroll
+    for (int it = 0; it < 16; ++it) vr[it] = ld((const char*)rowptr(it), 16 * l);
+  } else if constexpr (KV == KV_BF16) {
+#pragma unroll
+    for (int it = 0; it < 16; ++it) vr[it] = ld((const char*)rowptr(2 * it + (l >> 5)), 16 * (l & 31));
+  } else {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) vr[it] = ld((const char*)rowptr(4 * it + (l >> 4)), 16 * (l & 15));
+  }
+}
+
+// Write the loaded V rows into the LDS stage (row-major, bf16 or f32).
+template <int KV>
+__device__ __forceinline__ void store_v_rows(char* stage, int l, const u32x4* vr) {
   constexpr int PITCH = TileCfg<KV>::PITCH;
   if constexpr (KV == KV_F32) {
     float* stg = (float*)stage;
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const float* vp = (const float*)rowptr(it);
-      const f32x4 val = vp ? *(const f32x4*)(vp + 4 * l) : f32x4{0.f, 0.f, 0.f, 0.f};
-      *(f32x4*)(stg + it * PITCH + 4 * l) = val;
-    }
+    for (int it = 0; it < 16; ++it) *(u32x4*)(stg + it * PITCH + 4 * l) = vr[it];
   } else if constexpr (KV == KV_BF16) {
     bf16* stg = (bf16*)stage;
-    u32x4 val[16];
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const bf16* vp = (const bf16*)rowptr(2 * it + (l >> 5));
-      val[it] = vp ? *(const u32x4*)(vp + 8 * (l & 31)) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int it = 0; it < 16; ++it) *(u32x4*)(stg + (2 * it + (l >> 5)) * PITCH + 8 * (l & 31)) = val[it];
+    for (int it = 0; it < 16; ++it) *(u32x4*)(stg + (2 * it + (l >> 5)) * PITCH + 8 * (l & 31)) = vr[it];
   } else {
     bf16* stg = (bf16*)stage;
-    u32x4 val[8];
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const uint8_t* vp = (const uint8_t*)rowptr(4 * it + (l >> 4));
-      val[it] = vp ? *(const u32x4*)(vp + 16 * (l & 15)) : u32x4{0u, 0u, 0u, 0u};
-    }
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       bf16* dst = stg + (4 * it + (l >> 4)) * PITCH + 16 * (l & 15);
-      *(bf16x8*)dst = e4m3x8_to_bf16(val[it][0], val[it][1]);
-      *(bf16x8*)(dst + 8) = e4m3x8_to_bf16(val[it][2], val[it][3]);
+      *(bf16x8*)dst = e4m3x8_to_bf16(vr[it][0], vr[it][1]);
+      *(bf16x8*)(dst + 8) = e4m3x8_to_bf16(vr[it][2], vr[it][3]);
     }
   }
+}
+
+// Stage the V rows of one step into LDS.
+template <int KV, typename RowPtr>
+__device__ __forceinline__ void stage_v(char* stage, int l, RowPtr rowptr) {
+  u32x4 vr[FragRegs<KV>::V];
+  load_v_rows<KV, true>(l, rowptr, vr);
+  store_v_rows<KV>(stage, l, vr);
 }
 
 // O^T += V^T P^T for one step.  pr[mt][r] is the (already V-scaled)

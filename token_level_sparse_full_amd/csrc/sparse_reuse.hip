@@ -83,9 +83,9 @@ __global__ __launch_bounds__(SP_THREADS, 2) void sparse_attn_kernel(const Sparse
   const int64_t T = p.T;
 
   char* stage = smem + wave * kWaveBytes;
-  int* s_key = (int*)(stage + kTileStageBytes);
-  float* s_ksc = (float*)(s_key + 32);
-  float* s_vsc = s_ksc + 32;
+  int* tab = (int*)(stage + kTileStageBytes);  // key of each slot of the step, or -1
+  float* tks = (float*)(tab + 32);             // K row scales (e4m3)
+  float* tvs = tks + 32;                       // V row scales (e4m3)
 
   QFrag qf;
   load_qfrag<KV>((const char*)p.q + ((int64_t)qid * H + c16) * kHeadDim * (KV == KV_F32 ? 4 : 2), c16 < H, g, qf);
@@ -106,33 +106,50 @@ __global__ __launch_bounds__(SP_THREADS, 2) void sparse_attn_kernel(const Sparse
   const int split = SPLIT ? (int)blockIdx.y : 0;
   const int st_first = SPLIT ? split * (SP_SPLIT_KEYS / STEP) : 0;
   const int st_end = SPLIT ? min(nsteps, st_first + SP_SPLIT_KEYS / STEP) : nsteps;
-  for (int st = st_first + wave; st < st_end; st += SP_WAVES) {
-    // ---- slot table of this step (key index or -1, scales)
-    if (l < STEP) {
-      const int pos = st * STEP + l;
-      int key = -1;
-      if (pos < nsel) {
-        const int j = irow[pos];
-        if (j >= 0 && (int64_t)j < T) key = j;
-      }
-      s_key[l] = key;
-      if constexpr (KV == KV_E4M3) {
-        s_ksc[l] = key >= 0 ? p.k_scale[kv_row0 + key] : 0.f;
-        s_vsc[l] = key >= 0 ? p.v_scale[kv_row0 + key] : 0.f;
-      }
-    }
+
+  // Each step of a wave has one gather latency on its path: the index
+  // entries of the next step are read while this one computes, and the K
+  // rows, V rows (and scales) of a step are all issued together before the
+  // first of them is waited for.  An absent key (past the count, or an index
+  // outside [0, T)) reads row 0 and is masked out of the softmax, so every
+  // load is unconditional.  The float32 cache loads V after the logits: its
+  // K and V fragments together would not fit in the registers.
+  constexpr bool V_EARLY = KV != KV_F32;
+  auto fetch_key = [&](int st) -> int {  // lanes < STEP: key of slot l of step st, or -1
+    const int pos = st * STEP + l;
+    const bool in = l < STEP && st < st_end && pos < nsel;
+    const int j = irow[in ? pos : 0];
+    return (in && j >= 0 && (int64_t)j < T) ? j : -1;
+  };
+  int st = st_first + wave;
+  int key = fetch_key(st);
+  for (; st < st_end; st += SP_WAVES) {
+    if (l < STEP) tab[l] = key;
     wave_lds_order();
+    float ksc = 0.f, vsc = 0.f;
+    if constexpr (KV == KV_E4M3) {
+      ksc = p.k_scale[kv_row0 + max(key, 0)];
+      vsc = p.v_scale[kv_row0 + max(key, 0)];
+    }
+    u32x4 kr[NMT][FragRegs<KV>::K], vr[FragRegs<KV>::V];
+    auto load_v = [&] { load_v_rows<KV, false>(l, [&](int slot) { return vseq + (int64_t)max(tab[slot], 0) * ROWB; }, vr); };
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) load_k_tile<KV>(kseq + (int64_t)max(tab[16 * mt + c16], 0) * ROWB, g, kr[mt]);
+    if constexpr (V_EARLY) load_v();
+    key = fetch_key(st + SP_WAVES);
 
     f32x4 sacc[NMT];
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-      const int key = s_key[16 * mt + c16];
-      sacc[mt] = s_tile<KV>(key >= 0 ? kseq + (int64_t)key * ROWB : nullptr, g, qf);
+    for (int mt = 0; mt < NMT; ++mt) sacc[mt] = s_from_k<KV>(kr[mt], qf);
+    if constexpr (!V_EARLY) load_v();
+    store_v_rows<KV>(stage, l, vr);
+    if constexpr (KV == KV_E4M3) {
+      if (l < STEP) {
+        tks[l] = ksc;
+        tvs[l] = vsc;
+      }
     }
-    stage_v<KV>(stage, l, [&](int slot) -> const char* {
-      const int key = s_key[slot];
-      return key >= 0 ? vseq + (int64_t)key * ROWB : nullptr;
-    });
+    wave_lds_order();
 
     // ---- online softmax (log2 domain); lane: row c16, key slots 16mt + 4g + r
     float x[NMT][4];
@@ -143,8 +160,8 @@ __global__ __launch_bounds__(SP_THREADS, 2) void sparse_attn_kernel(const Sparse
       for (int r = 0; r < 4; ++r) {
         const int slot = 16 * mt + 4 * g + r;
         float v = sacc[mt][r] * p.scale_log2;
-        if constexpr (KV == KV_E4M3) v *= s_ksc[slot];
-        v = s_key[slot] >= 0 ? v : kNegInf;
+        if constexpr (KV == KV_E4M3) v *= tks[slot];
+        v = tab[slot] >= 0 ? v : kNegInf;
         x[mt][r] = v;
         tmax = fmaxf(tmax, v);
       }
@@ -161,14 +178,13 @@ __global__ __launch_bounds__(SP_THREADS, 2) void sparse_attn_kernel(const Sparse
         const float e = (x[mt][r] == kNegInf) ? 0.f : fast_exp2(x[mt][r] - m_new);
         psum += e;
         pr[mt][r] = e;
-        if constexpr (KV == KV_E4M3) pr[mt][r] = e * s_vsc[16 * mt + 4 * g + r];
+        if constexpr (KV == KV_E4M3) pr[mt][r] = e * tvs[16 * mt + 4 * g + r];
       }
     z_run = z_run * alpha + psum;
     m_run = m_new;
 #pragma unroll
     for (int t = 0; t < 16; ++t) oacc[t] *= alpha;
 
-    wave_lds_order();
     pv_step<KV>(stage, pr, g, c16, oacc);
     wave_lds_order();
   }
