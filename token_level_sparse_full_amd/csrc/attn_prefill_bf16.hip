@@ -255,19 +255,25 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
     // =============================== prefill_pv ===============================
     __shared__ __attribute__((aligned(1024))) char lds_k0[PB_KTILE], lds_k1[PB_KTILE];
     __shared__ __attribute__((aligned(1024))) char lds_v0[PB_VTILE], lds_v1[PB_VTILE];
-    __shared__ __attribute__((aligned(1024))) char lds_q[PB_WAVES * 16 * 1024];
     __shared__ __attribute__((aligned(16))) char lds_p[PB_WAVES * PB_KT * PB_PP];
     __shared__ __attribute__((aligned(16))) float lds_lse[PB_WAVES * PB_RW];
     char* const pbuf = lds_p + wave * PB_KT * PB_PP;
     float* const lse_lds = lds_lse + wave * PB_RW;
-    // Rows 0..31 stay in registers; rows 32..63 go to LDS as [s][lane] (16 KB
-    // per wave), so that each fragment read is one conflict-free ds_read_b128.
-    bf16x8 qf[16];
-    char* const qlds = lds_q + wave * (16 * 1024) + l * 16;
+    // With H = 16 all 64 query rows of the wave stay in registers (128 VGPRs),
+    // so the S block reads only K from LDS.  The smaller H run out of
+    // registers that way: their rows 32..63 go to LDS as [s][lane] (16 KB per
+    // wave), so that each fragment read is one conflict-free ds_read_b128.
+    constexpr bool QREG = H == 16;
+    __shared__ __attribute__((aligned(1024))) char lds_q[QREG ? 16 : PB_WAVES * 16 * 1024];
+    char* const qlds = lds_q + (QREG ? 0 : wave * (16 * 1024) + l * 16);
+    bf16x8 qf[16], qf1[QREG ? 16 : 1];
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       qf[s] = as_bf16x8(qload(0, s));
-      *(u32x4*)(qlds + s * 1024) = qload(1, s);
+      if constexpr (QREG)
+        qf1[s] = as_bf16x8(qload(1, s));
+      else
+        *(u32x4*)(qlds + s * 1024) = qload(1, s);
     }
     auto q1frag = [&](int s) -> bf16x8 { return as_bf16x8(*(const u32x4*)(qlds + s * 1024)); };
     // lse of the wave's rows (log2 units); rows past the last token read row 0's
@@ -288,22 +294,28 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
     // hook(s) runs inside step s (the next tile's DMA, the scores)
     auto s_rows_keys = [&](const char* kb, auto hook) __attribute__((always_inline)) {
       Pair sa;
-      bf16x8 kf[16], q1[16];
+      bf16x8 kf[16], q1[QREG ? 1 : 16];
   #pragma unroll
       for (int s = 0; s < PB_AHEAD; ++s) {
         kf[s] = kfrag(kb, s);
-        q1[s] = q1frag(s);
+        if constexpr (!QREG) q1[s] = q1frag(s);
       }
+      // rows 32..63, K-step s: from registers, or prefetched from LDS
+      auto q1op = [&](int s) -> bf16x8 {
+        if constexpr (QREG) return qf1[s]; else return q1[s];
+      };
       __builtin_amdgcn_sched_barrier(0);
   #pragma unroll
       for (int s = 0; s < 16; ++s) {
         if (s == 15) {
-          mfma32v_last2(sa.v[0], sa.v[1], qf[s], q1[s], kf[s]);
+          mfma32v_last2(sa.v[0], sa.v[1], qf[s], q1op(s), kf[s]);
         } else {
           if (s == 0) mfma32v_first(sa.v[0], qf[s], kf[s]); else mfma32v(sa.v[0], qf[s], kf[s]);
           if (s + PB_AHEAD < 16) kf[s + PB_AHEAD] = kfrag(kb, s + PB_AHEAD);
-          if (s == 0) mfma32v_first(sa.v[1], q1[s], kf[s]); else mfma32v(sa.v[1], q1[s], kf[s]);
-          if (s + PB_AHEAD < 16) q1[s + PB_AHEAD] = q1frag(s + PB_AHEAD);
+          if (s == 0) mfma32v_first(sa.v[1], q1op(s), kf[s]); else mfma32v(sa.v[1], q1op(s), kf[s]);
+          if constexpr (!QREG) {
+            if (s + PB_AHEAD < 16) q1[s + PB_AHEAD] = q1frag(s + PB_AHEAD);
+          }
         }
         hook(s);
         __builtin_amdgcn_sched_barrier(0);
