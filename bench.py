@@ -69,9 +69,9 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """Per-launch HBM bytes of the full-attention kernel recorded by --collect-traffic,
-    or None when there is no record or the kernel sources changed since it was taken."""
+def read_traffic_record() -> dict:
+    """The counter record written by --collect-traffic, or {} when there is none or the
+    kernel sources changed since it was taken."""
     try:
         rec = {}
         with open(TRAFFIC_FILE) as f:
@@ -79,10 +79,25 @@ def read_traffic():
                 if "=" in line and not line.startswith("#"):
                     key, val = line.split("=", 1)
                     rec[key.strip()] = val.strip()
-        if rec.get("kernel_source_sha256_16") != kernel_source_hash():
-            return None
-        return float(rec["traffic_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
+        return rec if rec.get("kernel_source_sha256_16") == kernel_source_hash() else {}
+    except OSError:
+        return {}
+
+
+def read_traffic():
+    """Per-launch HBM bytes of the full-attention kernel recorded by --collect-traffic,
+    or None when there is no record or the kernel sources changed since it was taken."""
+    try:
+        return float(read_traffic_record()["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def read_mfma_busy():
+    """MFMA busy fraction (counters, against 2.4 GHz) of the same record, or None."""
+    try:
+        return float(read_traffic_record()["mfma_busy_frac_at_2p4ghz"])
+    except (KeyError, ValueError):
         return None
 
 
@@ -326,7 +341,10 @@ def main():
                      "achieved": fa_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": fa_tflops / BF16_PEAK_TFLOPS, "traffic": read_traffic(),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "algorithmic_flop_per_step": fa_flop, "launches_per_step": len(chunks)},
+                     "algorithmic_flop_per_step": fa_flop, "launches_per_step": len(chunks),
+                     # the lse dispatch repeats QK^T: executed MFMA work is 1.5x the algorithmic
+                     "executed_frac": 1.5 * fa_tflops / BF16_PEAK_TFLOPS,
+                     "mfma_busy_frac_counters": read_mfma_busy()},
         "stages": {
             "full_attn_ms": fa_ms, "select_ms": sel_ms, "sparse_ms_per_layer": sp_ms,
             "sparse_reuse_queries_per_s": L / (sp_ms * 1e-3),
