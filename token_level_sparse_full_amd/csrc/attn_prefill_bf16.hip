@@ -204,8 +204,9 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
     // tile the buffer resource is empty and the DMA writes zeros, so that every
     // tile issues the same instructions).  K(kt+1) may still be in flight at
     // the wait: each wave keeps its last batch of DMA instructions (5 for wave
-    // 0, 4 for the others) outstanding.  The batch is spread over the MFMA
-    // steps (one instruction every third step).
+    // 0, 4 for the others) outstanding.  The batch is spread over the first
+    // ten MFMA steps (one instruction every second step): issued that early
+    // it has landed by the wait two tiles later.
     auto step1 = [&](int kt, const char* kc, char* kd) __attribute__((always_inline)) {
       if (wv == 0) __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5)
       else __builtin_amdgcn_s_waitcnt(0x0F74);           // vmcnt(4)
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
         st.v[0] = mfma32(kf[s], qf[0][s], s == 0 ? f32x16{} : st.v[0]);
         if (s + PB_AHEAD < 16) kf[s + PB_AHEAD] = kfrag(kc, s + PB_AHEAD);
         st.v[1] = mfma32(kf[s], qf[1][s], s == 0 ? f32x16{} : st.v[1]);
-        if (s % 3 == 0 && s < 15) dma_one(rk, kd, koff, s / 3);
+        if (s % 2 == 0 && s < 10) dma_one(rk, kd, koff, s / 2);
         __builtin_amdgcn_sched_barrier(0);
       }
       lse_update(st, kt, (int64_t)kt * PB_KT + PB_KT - 1 > pos_first);
