@@ -191,8 +191,8 @@ size_t hs2_sparse_workspace_bytes(int B, int n_q, int H, int max_sel);
  *                elements follow contiguously ([n_layers][L][d] when
  *                out_layer_stride == L*d; a larger stride writes into caches
  *                of T >= L rows, e.g. appending decode rows)
- * Requires L >= 1, D a positive multiple of 32, d == 256, 1 <= n_layers <= 64,
- * out_layer_stride >= L * d.
+ * Requires L >= 1, D a multiple of 32 in [32, 65536], d == 256,
+ * 1 <= n_layers <= 64, out_layer_stride >= L * d.
  */
 int hs2_bridge_kv_proj(const void* x, int64_t L, int D,
                        const void* w_k, const void* w_v, int n_layers, int d,

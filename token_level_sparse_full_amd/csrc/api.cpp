@@ -193,7 +193,8 @@ int hs2_bridge_kv_proj(const void* x, int64_t L, int D, const void* w_k, const v
                        void* stream) {
   if (!x || !w_k || !w_v || !k_out || !v_out) return fail(HS2_ERR_NULL, "x, w_k, w_v, k_out and v_out are required");
   if (d != HS2_HEAD_DIM) return fail(HS2_ERR_UNSUPPORTED, "projection width %d unsupported (only %d)", d, HS2_HEAD_DIM);
-  if (L < 1 || D < 32 || D % 32 != 0) return fail(HS2_ERR_SHAPE, "need L >= 1 and D a positive multiple of 32");
+  if (L < 1 || D < 32 || D % 32 != 0 || D > 65536)
+    return fail(HS2_ERR_SHAPE, "need L >= 1 and D a multiple of 32 in [32, 65536]");
   if (n_layers < 1 || n_layers > 64) return fail(HS2_ERR_SHAPE, "n_layers must be in [1, 64]");
   if (out_layer_stride < L * (int64_t)d) return fail(HS2_ERR_SHAPE, "out_layer_stride must be >= L * d");
   if ((L + 255) / 256 * (int64_t)(2 * n_layers) > 0x7FFFFFFF) return fail(HS2_ERR_SHAPE, "L too large");

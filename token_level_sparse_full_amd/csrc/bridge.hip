@@ -9,10 +9,15 @@
 // All projections of all bridged layers are one GEMM x[L, D] . [W_k0 | W_v0 |
 // W_k1 | ...] with N = 2 * n_layers * 256; the epilogue scatters each 256-wide
 // column block to its layer's K or V.  Workgroup tile 256 x 256 (4 waves of
-// 128 x 128, 32x32x16 bf16 MFMA), K chunks of 32 staged through LDS and
-// prefetched one chunk ahead.  The weights are read in their natural [D][d]
-// layout: ds_read_b64_tr_b16 turns the [k][n] LDS tile into the k-contiguous
-// B operand, so no transposed copy of W is needed.
+// 128 x 128 in the AGPRs, 32x32x16 bf16 MFMA), K chunks of 32.  The chunks
+// stream into LDS by buffer loads to LDS (16 B per lane, no register staging)
+// through four stage buffers, three chunks ahead of the MFMAs; each wave's
+// eight DMA instructions of a chunk are spread over the 32 MFMAs of the chunk
+// before.  The swizzled LDS layouts are made by the per-lane source offsets
+// of the DMA.  The weights are read in their natural [D][d] layout:
+// ds_read_b64_tr_b16 turns the [k][n] LDS tile into the k-contiguous B
+// operand, so no transposed copy of W is needed.  Rows past L read as zeros
+// (the buffer resource of the x tile ends at row L).
 #include "hs2_device.hpp"
 #include "hs2_internal.hpp"
 
@@ -23,6 +28,7 @@ constexpr int BR_THREADS = 256;
 constexpr int BM = 256, BN = 256, BK = 32;
 constexpr int A_BYTES = BM * BK * 2;  // 16 KB
 constexpr int B_BYTES = BK * BN * 2;  // 16 KB
+constexpr int ST_BYTES = A_BYTES + B_BYTES;
 
 // A tile [BM][BK] bf16: 4 chunks of 16 B per row, chunk ^ ((row >> 2) & 3)
 __device__ __forceinline__ int a_off(int row, int ch) { return row * 64 + ((ch ^ ((row >> 2) & 3)) << 4); }
@@ -30,45 +36,50 @@ __device__ __forceinline__ int a_off(int row, int ch) { return row * 64 + ((ch ^
 __device__ __forceinline__ int b_off(int row, int ch) { return row * 512 + ((ch ^ (2 * (row & 3))) << 4); }
 
 __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * (A_BYTES + B_BYTES)];
+  // four stage buffers, each its own LDS object so that the compiler can tell
+  // the reads of one from the DMA into another
+  __shared__ __attribute__((aligned(1024))) char st0[ST_BYTES], st1[ST_BYTES], st2[ST_BYTES], st3[ST_BYTES];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int hb = l >> 5, l32 = l & 31, G = l >> 4, s16 = l & 15;
   const int wm = wave >> 1, wn = wave & 1;  // wave tile (128 x 128) inside the workgroup tile
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int n_ntiles = (2 * p.n_layers * 256) / BN;
   const int mt_blk = blockIdx.x / n_ntiles, nt_blk = blockIdx.x % n_ntiles;
   const int64_t m0 = (int64_t)mt_blk * BM;
   const int n0 = nt_blk * BN;                 // global column of the concatenated weights
   const int layer = n0 / 512, which = (n0 / 256) & 1;
-  const bf16* x = (const bf16*)p.x;
   const bf16* w = (const bf16*)(which ? p.w_v : p.w_k) + (int64_t)layer * p.D * 256;
+  const int nk = p.D / BK;
 
-  // staging: A 256 rows x 4 chunks, B 32 rows x 32 chunks -> 4 + 4 loads per thread
-  auto load = [&](int kc, u32x4* r) {
+  // buffer resources: the x rows m0 .. min(L, m0 + 256) - 1 and this weight
+  // matrix; empty ones for the chunks past the last (they load zeros, so every
+  // chunk issues the same instructions)
+  const int rows = (int)min<int64_t>(BM, p.L - m0);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const bf16*)p.x + m0 * p.D), 0, rows * p.D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)w, 0, p.D * 512, 0x00020000);
+  const __amdgpu_buffer_rsrc_t r0 = __builtin_amdgcn_make_buffer_rsrc((void*)w, 0, 0, 0x00020000);
+  // per-lane source offsets of this wave's DMA instructions i = wv + 4t: LDS
+  // chunk 64 i + l holds the source chunk that the swizzle puts there
+  uint32_t oa[4], ob[4];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int c = it * BR_THREADS + tid;
-      const int row = c >> 2, ch = c & 3;
-      const int64_t grow = m0 + row;
-      r[it] = grow < p.L ? *(const u32x4*)(x + grow * p.D + kc * BK + ch * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int c = it * BR_THREADS + tid;
-      const int row = c >> 5, ch = c & 31;
-      r[4 + it] = *(const u32x4*)(w + (int64_t)(kc * BK + row) * 256 + ch * 8);
-    }
-  };
-  auto store = [&](char* buf, const u32x4* r) {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int c = it * BR_THREADS + tid;
-      *(u32x4*)(buf + a_off(c >> 2, c & 3)) = r[it];
-    }
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int c = it * BR_THREADS + tid;
-      *(u32x4*)(buf + A_BYTES + b_off(c >> 5, c & 31)) = r[4 + it];
-    }
+  for (int t = 0; t < 4; ++t) {
+    const int P = 64 * (wv + 4 * t) + l;
+    const int ar = P >> 2, ach = (P & 3) ^ ((ar >> 2) & 3);
+    oa[t] = (uint32_t)(ar * p.D * 2 + ach * 16);
+    const int br = P >> 5, bch = (P & 31) ^ (2 * (br & 3));
+    ob[t] = (uint32_t)(br * 512 + bch * 16);
+  }
+  // DMA instruction j (0..7) of chunk kc into stage buffer sb
+  auto dma_one = [&](int kc, char* sb, int j) __attribute__((always_inline)) {
+    const int t = j & 3, ins = wv + 4 * t;
+    const bool live = kc < nk;
+    if (j < 4)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? ra : r0, (void HS2_LDS*)((char HS2_LDS*)sb + ins * 1024), 16,
+                                               oa[t], kc * (BK * 2), 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rb : r0, (void HS2_LDS*)((char HS2_LDS*)sb + A_BYTES + ins * 1024),
+                                               16, ob[t], kc * (BK * 512), 0, 0);
   };
 
   f32x16 acc[4][4];
@@ -77,14 +88,15 @@ __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParam
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  const int nk = p.D / BK;
-  u32x4 stg[8];
-  load(0, stg);
-  store(smem, stg);
-  __syncthreads();
-  for (int kc = 0; kc < nk; ++kc) {
-    char* buf = smem + (kc & 1) * (A_BYTES + B_BYTES);
-    if (kc + 1 < nk) load(kc + 1, stg);
+  // chunk kc from stage buffer buf; the DMA of chunk kc + 3 into nxt (which
+  // held chunk kc - 1) is spread over its MFMAs, one instruction after every
+  // fourth
+  auto step = [&](int kc, const char* buf, char* nxt) __attribute__((always_inline)) {
+    // chunk kc has landed once at most the 16 DMA instructions of the two
+    // chunks after it are outstanding; the barrier makes every wave's part
+    // visible and ends every wave's reads of chunk kc - 1
+    __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
+    dma_barrier();
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       bf16x8 af[4], bfr[4];
@@ -104,15 +116,28 @@ __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParam
         bfr[j] = cat8(lds_tr16((const bf16*)b0), lds_tr16((const bf16*)b1));
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        dma_one(kc + 3, nxt, 4 * ks + i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    if (kc + 1 < nk) {
-      store(smem + ((kc + 1) & 1) * (A_BYTES + B_BYTES), stg);
-      __syncthreads();
-    }
+  };
+
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dma_one(0, st0, j);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dma_one(1, st1, j);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dma_one(2, st2, j);
+  for (int kc = 0; kc < nk; kc += 4) {
+    step(kc, st0, st3);
+    if (kc + 1 < nk) step(kc + 1, st1, st0);
+    if (kc + 2 < nk) step(kc + 2, st2, st1);
+    if (kc + 3 < nk) step(kc + 3, st3, st2);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the zero-filling DMA past the last chunk
 
   // epilogue: lane holds column wn*128 + 32j + l32, rows wm*128 + 32i + 8(r/4) + 4hb + r%4
   bf16* out = (bf16*)(which ? p.v_out : p.k_out) + (int64_t)layer * p.out_layer_stride;

@@ -99,6 +99,15 @@ __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v,
 // Sum of x over lanes l and l^32, landing in lane l%32 for x and in lane
 // 32+l%32 for y: returns x(l) + x(l+32) on lanes < 32 and y(l-32) + y(l) on
 // lanes >= 32.
+// Workgroup barrier for tiles filled by LDS DMA.  __syncthreads() carries a
+// workgroup-scope fence, and the compiler implements that fence by waiting
+// for every outstanding vector-memory operation (vmcnt(0)), which would also
+// wait for the DMA of tiles further ahead.  This barrier waits only for the
+// wave's own LDS operations; the caller first waits (vmcnt) for the DMA that
+// must have landed.  The "memory" clobber keeps the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void dma_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ float halfwave_pair_sum(float x, float y) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, y), false, false);
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
