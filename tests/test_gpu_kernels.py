@@ -195,7 +195,10 @@ def _bf16_from_f32(x):
     return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("L,D,n_layers", [(300, 256, 2), (1, 2048, 4), (513, 512, 1)])
+# D / 32 chunks of the K dimension: 1, 3, 5, 7 exercise the pipeline's partial rounds of 4 stage
+# buffers and the chunks past the end; L not a multiple of 256 the rows past L
+@pytest.mark.parametrize("L,D,n_layers", [(300, 256, 2), (1, 2048, 4), (513, 512, 1), (257, 32, 1), (100, 96, 3),
+                                          (70, 160, 2), (513, 224, 1)])
 def test_bridge_integer_exact(L, D, n_layers):
     say("bridge int", L, D, n_layers)
     rng = np.random.default_rng(L + D)
