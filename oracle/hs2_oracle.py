@@ -11,6 +11,8 @@ Everything here is the plain definition written out, slowly and in float64:
                          the top-k highest-scoring older tokens
 * ``sparse_attn_reuse``  attention restricted to a selected index set
 * ``bridge_kv_proj``     the KV-Bridging re-projection of hidden states
+* ``bridge_kv_proj_fp8`` the same re-projection stored as an FP8 e4m3 cache
+                         (codes plus one float32 scale per row)
 
 Sources (the pages about "HySparse2: Hybrid Sparse Attention with Two-Level KV
 Sharing"):
@@ -63,6 +65,8 @@ __all__ = [
     "select_topk_window",
     "sparse_attn_reuse",
     "bridge_kv_proj",
+    "f64_to_e4m3_codes",
+    "bridge_kv_proj_fp8",
 ]
 
 
@@ -278,3 +282,61 @@ def bridge_kv_proj(x: np.ndarray, w_k: np.ndarray, w_v: np.ndarray):
     k = np.stack([x @ w_k[m] for m in range(w_k.shape[0])])
     v = np.stack([x @ w_v[m] for m in range(w_v.shape[0])])
     return k, v
+
+
+# ----------------------------------------------------------------------------
+# FP8 cache rows (the pages count the KV cache in FP8: agihunt.info summary,
+# results table and key results)
+# ----------------------------------------------------------------------------
+
+def f64_to_e4m3_codes(y: np.ndarray) -> np.ndarray:
+    """OCP E4M3 codes of float64 values with |y| <= 448, rounded to the nearest
+    representable value, ties to the even code.
+
+    The representable magnitudes are the subnormals M * 2**-9 (M = 0..7) and the
+    normals (1 + M/8) * 2**(E-7) for E = 1..15 (E = 15, M = 7 is NaN).  Inside
+    the binade [2**e, 2**(e+1)) (e >= -6) they are the multiples of 2**(e-3);
+    below 2**-6 the multiples of 2**-9.  Rounding a / step to the nearest
+    integer with ties to even rounds the 3-bit mantissa to even.  The sign bit
+    follows the sign of y (also when the value rounds to zero).
+    """
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    if np.isnan(y).any() or (a > 448.0).any():
+        raise ValueError("e4m3 codes need finite |y| <= 448")
+    _, ex = np.frexp(np.maximum(a, 2.0 ** -6))   # a = m * 2**ex, m in [0.5, 1): binade 2**(ex-1)
+    step = np.ldexp(1.0, ex - 1 - 3)
+    val = np.rint(a / step) * step                # a / step is exact: step is a power of two
+    table = e4m3_decode_table()
+    code_of = {float(table[c]): c for c in range(0x7F)}   # the 127 non-negative finite codes
+    mags = np.vectorize(lambda v: code_of[float(v)], otypes=[np.int64])(val) if val.size else val.astype(np.int64)
+    return (mags | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def bridge_kv_proj_fp8(x: np.ndarray, w_k: np.ndarray, w_v: np.ndarray):
+    """The bridged K and V of every layer as e4m3 cache rows.
+
+    Each output row a (the float32 value of the exact projection x @ w[m])
+    with amax = max|a| gets scale = fl32(amax / 448) (1 for an all-zero row)
+    and, with r = fl32(448 / amax), the codes e4m3(clamp(fl32(a * r), -448,
+    448)); fl32 rounds to the nearest float32 (a quotient or product of two
+    float32 values rounded once from float64 is the correctly rounded float32
+    result).  Returns (k_codes, v_codes) uint8 [n_layers, L, d] and
+    (k_scale, v_scale) float32 [n_layers, L].
+    """
+    k, v = bridge_kv_proj(x, w_k, w_v)
+
+    def quantize(t):
+        a = t.astype(np.float32).astype(np.float64)
+        amax = np.abs(a).max(axis=-1)
+        nz = amax > 0
+        scale = np.where(nz, (amax / 448.0).astype(np.float32), np.float32(1.0)).astype(np.float64)
+        r = np.where(nz, (448.0 / np.where(nz, amax, 1.0)).astype(np.float32), np.float32(0.0)).astype(np.float64)
+        y = (a * r[..., None]).astype(np.float32).astype(np.float64)
+        y = np.clip(y, -448.0, 448.0)
+        return f64_to_e4m3_codes(y), scale.astype(np.float32)
+
+    kc, ks = quantize(k)
+    vc, vs = quantize(v)
+    return kc, vc, ks, vs
+

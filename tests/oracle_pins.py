@@ -420,4 +420,71 @@ def pin_decode_rows(orc):
     np.testing.assert_array_equal(orc.decode_rows(np.array([0x3F80, 0xC000], dtype=np.uint16), "bf16"), [1.0, -2.0])
 
 
+# ---------------------------------------------------------------------------
+# FP8 e4m3 cache rows
+# ---------------------------------------------------------------------------
+
+def pin_e4m3_encode_vs_torch(orc):
+    """Encoding against torch's float8_e4m3fn conversion (round to nearest even):
+    every finite code's own value, every midpoint between neighbours (the ties),
+    and random values over the whole range and near the subnormals."""
+    t = orc.e4m3_decode_table()
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)])
+    np.testing.assert_array_equal(orc.f64_to_e4m3_codes(t[finite]), finite.astype(np.uint8))
+    pos = np.unique(t[:0x7F])
+    mid = (pos[:-1] + pos[1:]) / 2
+    r = _rng(61)
+    y = np.concatenate([mid, -mid, r.uniform(-448, 448, 5000), r.uniform(-0.03, 0.03, 5000)]).astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(orc.f64_to_e4m3_codes(y.astype(np.float64)), ref)
+
+
+def pin_e4m3_encode_hand(orc):
+    # ties go to the even 3-bit mantissa; the sign bit follows the sign (also of zero)
+    cases = [(1.0 + 1 / 16, 0x38), (1.0 + 3 / 16, 0x3A), (-(1.0 + 1 / 16), 0xB8), (448.0, 0x7E), (416.0, 0x7D),
+             (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02), (2.0 ** -6, 0x08), (0.0, 0x00), (-0.0, 0x80),
+             (-2.0 ** -12, 0x80)]
+    for val, want in cases:
+        assert int(orc.f64_to_e4m3_codes(np.array([val]))[0]) == want, val
+
+
+def pin_bridge_fp8_closed_form(orc):
+    """One-hot hidden states select weight rows: a row [4, -2, 1, 0, ...] has
+    amax 4, scale fl32(4/448) and codes for 448, -224, 112, 0; a zero row keeps
+    scale 1 and codes 0."""
+    D, d = 3, 8
+    x = np.array([[1.0, 0.0, 0.0], [0.0, 0.0, 0.0]])
+    wk = np.zeros((1, D, d))
+    wk[0, 0, :4] = [4.0, -2.0, 1.0, 0.0]
+    wv = np.zeros((1, D, d))
+    wv[0, 0, 5] = -3.0
+    kc, vc, ks, vs = orc.bridge_kv_proj_fp8(x, wk, wv)
+    assert ks.dtype == np.float32 and kc.dtype == np.uint8
+    assert ks[0, 0] == np.float32(4.0 / 448.0) and ks[0, 1] == 1.0 and vs[0, 1] == 1.0
+    np.testing.assert_array_equal(kc[0, 0, :4], [0x7E, 0xF6, 0x6E, 0x00])
+    assert (kc[0, 1] == 0).all() and (vc[0, 1] == 0).all()
+    assert vs[0, 0] == np.float32(3.0 / 448.0) and vc[0, 0, 5] == 0xFE and (np.delete(vc[0, 0], 5) == 0).all()
+
+
+def pin_bridge_fp8_dequant_bound(orc):
+    """decode(code) * scale is within half an e4m3 step of the projection: 2**-4
+    relative for normal codes, 2**-10 * scale absolute below them."""
+    r = _rng(62)
+    L, D, d, n = 9, 40, 16, 2
+    x = r.standard_normal((L, D))
+    wk = r.standard_normal((n, D, d)) * 0.02
+    wv = r.standard_normal((n, D, d)) * 0.02
+    k, v = orc.bridge_kv_proj(x, wk, wv)
+    kc, vc, ks, vs = orc.bridge_kv_proj_fp8(x, wk, wv)
+    t = orc.e4m3_decode_table()
+    for ref, codes, sc in ((k, kc, ks), (v, vc, vs)):
+        got = t[codes] * sc.astype(np.float64)[..., None]
+        bound = (2.0 ** -4 * np.abs(ref) + 2.0 ** -10 * sc.astype(np.float64)[..., None]) * (1 + 1e-6)
+        assert (np.abs(got - ref) <= bound).all()
+        # the largest element of each row lands on +-448
+        amax_pos = np.abs(ref).argmax(axis=-1)
+        top = np.take_along_axis(codes, amax_pos[..., None], axis=-1)[..., 0]
+        assert np.isin(top, [0x7E, 0xFE]).all()
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

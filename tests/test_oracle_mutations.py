@@ -49,6 +49,11 @@ MUTATIONS = [
     ("e4m3 bias 8", "(1.0 + M / 8.0) * 2.0 ** (E - 7)", "(1.0 + M / 8.0) * 2.0 ** (E - 8)"),
     ("e4m3 subnormal step", "t[code] = s * M * 2.0 ** -9", "t[code] = s * M * 2.0 ** -10"),
     ("e4m3 scale ignored", "return vals * np.asarray(scale", "return vals + 0 * np.asarray(scale"),
+    ("e4m3 encode truncates", "val = np.rint(a / step) * step", "val = np.floor(a / step) * step"),
+    ("e4m3 encode one mantissa bit short", "step = np.ldexp(1.0, ex - 1 - 3)", "step = np.ldexp(1.0, ex - 1 - 2)"),
+    ("e4m3 encode sign lost", "np.where(np.signbit(y), 0x80, 0)", "np.where(np.signbit(y), 0, 0)"),
+    ("fp8 scale for the fnuz range", "(amax / 448.0).astype(np.float32)", "(amax / 240.0).astype(np.float32)"),
+    ("fp8 V quantized from K", "vc, vs = quantize(v)", "vc, vs = quantize(k)"),
 ]
 
 
