@@ -488,6 +488,33 @@ def other_workloads(dev):
         "bridge_mfma_frac": br_flop / (t_br * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
         "cross_decoder_step_ms": t_cross, "prefill_tokens_per_s": wl.L / ((t_br + t_cross) * 1e-3),
         "note": "bridge warm (inputs resident); the 4 bridged decode steps cold"}
+    del k_all, v_all
+    torch.cuda.empty_cache()
+
+    # the same bridge writing the FP8 e4m3 cache (codes + per-row scales), then the
+    # 4 bridged decode steps reading that cache
+    k8 = torch.empty((wl.n_full, wl.L, 256), dtype=torch.uint8, device=dev)
+    v8 = torch.empty_like(k8)
+    ks8 = torch.empty((wl.n_full, wl.L), dtype=torch.float32, device=dev)
+    vs8 = torch.empty_like(ks8)
+
+    def run_bridge8(mark):
+        hs2.hs2_bridge_kv_proj_fp8(br["x"], br["w_k"], br["w_v"], k_out=k8, v_out=v8, k_scale=ks8, v_scale=vs8)
+        mark()
+    (t_br8,) = _timed(run_bridge8, 1)
+    t_layers = []
+    for m in range(wl.n_full):
+        q = inputs.cast(inputs.normal((1, 1, wl.H, 256), inputs.STD_QKV, wl.seed, inputs.S_QFULL_LAYER + m, dev),
+                        "bf16")
+        qs = [inputs.cast(inputs.normal((1, 1, wl.H, 256), inputs.STD_QKV, wl.seed, inputs.S_QSPARSE + 8 * m + i, dev),
+                          "bf16") for i in range(wl.n_sparse)]
+        t_layers.append(decode_step(q, qs, k8[m:m + 1], v8[m:m + 1], wl.L, wl.L - 1, ks8[m:m + 1], vs8[m:m + 1]))
+    t_cross8 = float(sum(sum(x) for x in t_layers))
+    out[wl.name + "_fp8"] = {
+        "bridge_ms": float(t_br8), "bridge_tflops": br_flop / (t_br8 * 1e-3) / 1e12,
+        "bridge_mfma_frac": br_flop / (t_br8 * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+        "cross_decoder_step_ms": t_cross8, "prefill_tokens_per_s": wl.L / ((t_br8 + t_cross8) * 1e-3),
+        "note": "bridge into the e4m3 cache (per-row scales) and the bridged decode steps on it"}
     del junk
     return out
 

@@ -201,6 +201,36 @@ int hs2_bridge_kv_proj(const void* x, int64_t L, int D,
 
 size_t hs2_bridge_workspace_bytes(int n_layers, int D, int d);
 
+/*
+ * hs2_bridge_kv_proj_fp8 - KV Bridging re-projection into an FP8 e4m3 cache.
+ *
+ * Defines (HySparse2 pages: agihunt.info summary, paragraph on the outer level
+ * -- the re-projected K/V fill the cross-decoder caches; same summary, results
+ * table and key results -- the KV cache at 1M tokens is counted in FP8): the same
+ * projections as hs2_bridge_kv_proj, quantized per output row from the
+ * float32 accumulators a[m, i, :] (for k; likewise for v), with amax =
+ * max_j |a[m, i, j]| and float32 division and product:
+ *   scale[m, i]    = amax / 448   (1 if the row is 0)
+ *   r              = 448 / amax
+ *   k_out[m, i, j] = e4m3(clamp(a[m, i, j] * r, -448, 448))
+ * with e4m3 = OCP E4M3 ("e4m3fn") code, round to nearest even; the value a
+ * code stands for is decode(code) * scale (the cache format hs2_full_attn_scored
+ * and hs2_sparse_attn_reuse take with HS2_FP8E4M3).
+ *
+ *   x                   [L, D] bf16
+ *   w_k, w_v            [n_layers, D, d] bf16
+ *   k_out, v_out        uint8 codes; layer m starts at byte m * out_layer_stride,
+ *                       rows of d bytes follow contiguously
+ *   k_scale, v_scale    float32; layer m starts at element m * scale_layer_stride
+ * Requires what hs2_bridge_kv_proj requires, scale_layer_stride >= L, and
+ * 4-byte aligned scale pointers.  Uses the same workspace size.
+ */
+int hs2_bridge_kv_proj_fp8(const void* x, int64_t L, int D,
+                           const void* w_k, const void* w_v, int n_layers, int d,
+                           uint8_t* k_out, uint8_t* v_out, float* k_scale, float* v_scale,
+                           int64_t out_layer_stride, int64_t scale_layer_stride,
+                           void* workspace, size_t ws_bytes, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* hs2_status_str(int status);
 

@@ -19,7 +19,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = hs2.header_symbols()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
 
@@ -162,6 +162,32 @@ def bridge(lib, **kw):
 ])
 def test_bridge_rejects(lib, kw, code):
     assert bridge(lib, **kw) == code
+
+
+def bridge8(lib, **kw):
+    a = dict(x=A, L=4096, D=2048, wk=A, wv=A, n=4, d=256, ko=A, vo=A, ks=A, vs=A, st=4096 * 256, sst=4096, ws=None,
+             wsb=0)
+    a.update(kw)
+    return lib.hs2_bridge_kv_proj_fp8(a["x"], a["L"], a["D"], a["wk"], a["wv"], a["n"], a["d"], a["ko"], a["vo"],
+                                      a["ks"], a["vs"], a["st"], a["sst"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), hs2.HS2_ERR_NULL),
+    (dict(ks=None), hs2.HS2_ERR_NULL),
+    (dict(vs=None), hs2.HS2_ERR_NULL),
+    (dict(d=128), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(D=2047), hs2.HS2_ERR_SHAPE),
+    (dict(D=65536 + 32), hs2.HS2_ERR_SHAPE),
+    (dict(L=0), hs2.HS2_ERR_SHAPE),
+    (dict(n=65), hs2.HS2_ERR_SHAPE),
+    (dict(st=4096 * 256 - 1), hs2.HS2_ERR_SHAPE),
+    (dict(sst=4095), hs2.HS2_ERR_SHAPE),
+    (dict(ko=MIS), hs2.HS2_ERR_ALIGN),
+    (dict(ks=A + 2), hs2.HS2_ERR_ALIGN),
+])
+def test_bridge_fp8_rejects(lib, kw, code):
+    assert bridge8(lib, **kw) == code
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

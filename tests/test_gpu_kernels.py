@@ -232,3 +232,60 @@ def test_bridge_normal_within_one_ulp_and_strided_output():
         assert (np.abs(g - ref) <= ulp + 64 * 2.0 ** -24 * mag).all()
         assert (np.abs(g - ref) <= ulp).mean() > 0.999
     assert (k_cache[:, L:] == 0).all() and (v_cache[:, L:] == 0).all()
+
+# --------------------------------------------------------------------------- bridge into an e4m3 cache
+@pytest.mark.parametrize("L,D,n_layers", [(300, 256, 2), (70, 160, 1), (1, 2048, 4)])
+def test_bridge_fp8_integer_exact(L, D, n_layers):
+    """Integer inputs make the float32 accumulators exact, so codes and scales
+    must equal the oracle's bit for bit (row 0 is all zero: scale 1, codes 0)."""
+    say("bridge fp8 int", L, D, n_layers)
+    rng = np.random.default_rng(L + 3 * D)
+    x = rng.integers(-8, 9, size=(L, D))
+    x[0] = 0
+    wk = rng.integers(-4, 5, size=(n_layers, D, 256))
+    wv = rng.integers(-4, 5, size=(n_layers, D, 256))
+    kc, vc, ks, vs = hs2.hs2_bridge_kv_proj_fp8(_bf16_from_f32(x).to(DEV), _bf16_from_f32(wk).to(DEV),
+                                               _bf16_from_f32(wv).to(DEV))
+    torch.cuda.synchronize()
+    kc_r, vc_r, ks_r, vs_r = oracle.bridge_kv_proj_fp8(x.astype(np.float64), wk.astype(np.float64),
+                                                       wv.astype(np.float64))
+    np.testing.assert_array_equal(ks.cpu().numpy(), ks_r)
+    np.testing.assert_array_equal(vs.cpu().numpy(), vs_r)
+    np.testing.assert_array_equal(kc.cpu().numpy(), kc_r)
+    np.testing.assert_array_equal(vc.cpu().numpy(), vc_r)
+
+
+def test_bridge_fp8_normal_and_strided_output():
+    """Normal data: the float32 accumulation may differ from the exact sum by
+    at most 64 roundings of 2**-24 on the scale of sum |x w|, which bounds the
+    scales and moves a code by at most one step; rows past L stay untouched."""
+    say("bridge fp8 normal")
+    L, D, n_layers, T = 700, 2048, 2, 1024
+    inp = inputs.bridge_inputs(L=L, D=D, n_layers=n_layers, d=256, seed=4, device=DEV)
+    k8 = torch.zeros((n_layers, T, 256), dtype=torch.uint8, device=DEV)
+    v8 = torch.zeros_like(k8)
+    ksc = torch.zeros((n_layers, T), dtype=torch.float32, device=DEV)
+    vsc = torch.zeros_like(ksc)
+    hs2.hs2_bridge_kv_proj_fp8(inp["x"], inp["w_k"], inp["w_v"], k_out=k8, v_out=v8, k_scale=ksc, v_scale=vsc,
+                               out_layer_stride=T * 256, scale_layer_stride=T)
+    torch.cuda.synchronize()
+    x64, wk64, wv64 = parity.decode(inp["x"]), parity.decode(inp["w_k"]), parity.decode(inp["w_v"])
+    k_ref, v_ref = oracle.bridge_kv_proj(x64, wk64, wv64)
+    k_abs, v_abs = oracle.bridge_kv_proj(np.abs(x64), np.abs(wk64), np.abs(wv64))
+    kc_r, vc_r, ks_r, vs_r = oracle.bridge_kv_proj_fp8(x64, wk64, wv64)
+    table = oracle.e4m3_decode_table()
+    for codes, sc, ref, mag, codes_r, sc_r in ((k8, ksc, k_ref, k_abs, kc_r, ks_r), (v8, vsc, v_ref, v_abs, vc_r, vs_r)):
+        c = codes[:, :L].cpu().numpy()
+        s_ = sc[:, :L].cpu().numpy().astype(np.float64)
+        slack = 64 * 2.0 ** -24 * mag                     # float32 accumulation error bound per element
+        row_slack = slack.max(axis=-1) / 448.0
+        assert (np.abs(s_ - sc_r) <= row_slack + 2.0 ** -23 * sc_r).all()
+        got = table[c] * s_[..., None]
+        # half a step of the value's e4m3 binade (2**-4 relative, 2**-10 scale below the normals),
+        # plus one more step where the float32 sum sits on the other side of a rounding boundary
+        step = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref) / s_[..., None], 2.0 ** -6))) - 3),
+                          2.0 ** -9) * s_[..., None]
+        assert (np.abs(got - ref) <= 1.5 * step + 2 * slack).all()
+        assert (c == codes_r).mean() > 0.999
+        assert (codes[:, L:] == 0).all() and (sc[:, L:] == 0).all()
+

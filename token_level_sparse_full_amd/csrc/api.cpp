@@ -208,4 +208,28 @@ int hs2_bridge_kv_proj(const void* x, int64_t L, int D, const void* w_k, const v
   return hip_status(hs2::launch_bridge(p, workspace, ws_bytes, (hipStream_t)stream), "hs2_bridge_kv_proj");
 }
 
+int hs2_bridge_kv_proj_fp8(const void* x, int64_t L, int D, const void* w_k, const void* w_v, int n_layers, int d,
+                           uint8_t* k_out, uint8_t* v_out, float* k_scale, float* v_scale, int64_t out_layer_stride,
+                           int64_t scale_layer_stride, void* workspace, size_t ws_bytes, void* stream) {
+  if (!x || !w_k || !w_v || !k_out || !v_out || !k_scale || !v_scale)
+    return fail(HS2_ERR_NULL, "x, w_k, w_v, k_out, v_out, k_scale and v_scale are required");
+  if (d != HS2_HEAD_DIM) return fail(HS2_ERR_UNSUPPORTED, "projection width %d unsupported (only %d)", d, HS2_HEAD_DIM);
+  if (L < 1 || D < 32 || D % 32 != 0 || D > 65536)
+    return fail(HS2_ERR_SHAPE, "need L >= 1 and D a multiple of 32 in [32, 65536]");
+  if (n_layers < 1 || n_layers > 64) return fail(HS2_ERR_SHAPE, "n_layers must be in [1, 64]");
+  if (out_layer_stride < L * (int64_t)d) return fail(HS2_ERR_SHAPE, "out_layer_stride must be >= L * d");
+  if (scale_layer_stride < L) return fail(HS2_ERR_SHAPE, "scale_layer_stride must be >= L");
+  if ((L + 255) / 256 * (int64_t)(2 * n_layers) > 0x7FFFFFFF) return fail(HS2_ERR_SHAPE, "L too large");
+  if (!aligned(x, 16) || !aligned(w_k, 16) || !aligned(w_v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16))
+    return fail(HS2_ERR_ALIGN, "x, w_k, w_v, k_out and v_out must be 16-byte aligned");
+  if (!aligned(k_scale, 4) || !aligned(v_scale, 4)) return fail(HS2_ERR_ALIGN, "k_scale and v_scale must be 4-byte aligned");
+  const size_t need = hs2::bridge_workspace_bytes(n_layers, D, d);
+  if (need > 0 && (!workspace || ws_bytes < need)) return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+  hs2::BridgeParams p;
+  p.x = x; p.w_k = w_k; p.w_v = w_v; p.k_out = k_out; p.v_out = v_out;
+  p.L = L; p.D = D; p.n_layers = n_layers; p.out_layer_stride = out_layer_stride;
+  p.fp8 = true; p.k_scale = k_scale; p.v_scale = v_scale; p.scale_layer_stride = scale_layer_stride;
+  return hip_status(hs2::launch_bridge(p, workspace, ws_bytes, (hipStream_t)stream), "hs2_bridge_kv_proj_fp8");
+}
+
 }  // extern "C"

@@ -18,6 +18,16 @@
 // ds_read_b64_tr_b16 turns the [k][n] LDS tile into the k-contiguous B
 // operand, so no transposed copy of W is needed.  Rows past L read as zeros
 // (the buffer resource of the x tile ends at row L).
+//
+// The e4m3 form (the pages count the KV cache in FP8: agihunt.info summary,
+// results table) quantizes each 256-wide output row from its float32
+// accumulators: scale = amax / 448 (1 for an all-zero row) and, with
+// r = 448 / amax, code = e4m3(clamp(v * r, -448, 448)) rounded to nearest even
+// (IEEE float32 division and product; the conversion instruction rounds to
+// nearest even): one multiply per element.  A workgroup holds whole rows (its
+// 256 columns are one layer's K or V), so the row maxima need only a
+// reduction across lanes inside each wave (DPP inside 16-lane rows, then one
+// swizzle) and one LDS exchange between the two waves that share a row.
 #include "hs2_device.hpp"
 #include "hs2_internal.hpp"
 
@@ -35,6 +45,23 @@ __device__ __forceinline__ int a_off(int row, int ch) { return row * 64 + ((ch ^
 // B tile [BK][BN] bf16: 32 chunks per row, chunk ^ (2 * (row & 3))
 __device__ __forceinline__ int b_off(int row, int ch) { return row * 512 + ((ch ^ (2 * (row & 3))) << 4); }
 
+// Maximum over the 32 lanes of each half-wave, returned to all of them:
+// quad_perm swaps (xor 1, xor 2), the half-row and row mirrors (which pair
+// each lane with one in the other half of its 8- and 16-lane group), then one
+// swizzle between the two 16-lane rows of the half-wave.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+  return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false)));
+}
+__device__ __forceinline__ float half_wave_max(float v) {
+  v = dpp_max<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = dpp_max<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = dpp_max<0x141>(v);   // row_half_mirror
+  v = dpp_max<0x140>(v);   // row_mirror
+  return fmaxf(v, shfl_xor(v, 16));
+}
+
+template <bool FP8>
 __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParams p) {
   // four stage buffers, each its own LDS object so that the compiler can tell
   // the reads of one from the DMA into another
@@ -140,16 +167,51 @@ __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParam
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the zero-filling DMA past the last chunk
 
   // epilogue: lane holds column wn*128 + 32j + l32, rows wm*128 + 32i + 8(r/4) + 4hb + r%4
-  bf16* out = (bf16*)(which ? p.v_out : p.k_out) + (int64_t)layer * p.out_layer_stride;
+  if constexpr (!FP8) {
+    bf16* out = (bf16*)(which ? p.v_out : p.k_out) + (int64_t)layer * p.out_layer_stride;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t grow = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * hb + (r & 3);
-      if (grow >= p.L) continue;
+      for (int r = 0; r < 16; ++r) {
+        const int64_t grow = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * hb + (r & 3);
+        if (grow >= p.L) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) out[grow * 256 + wn * 128 + 32 * j + l32] = to_bf16(acc[i][j][r]);
-    }
+        for (int j = 0; j < 4; ++j) out[grow * 256 + wn * 128 + 32 * j + l32] = to_bf16(acc[i][j][r]);
+      }
+  } else {
+    // row maxima of |v| over this wave's 128 columns (4 per lane, then the 32
+    // lanes of the half-wave), then over the partner wave's half through LDS
+    float* red = (float*)st0;   // [wm][wn][128 rows]; the DMA has drained
+    dma_barrier();              // every wave is done reading the stage buffers
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float m = fmaxf(fmaxf(fabsf(acc[i][0][r]), fabsf(acc[i][1][r])), fmaxf(fabsf(acc[i][2][r]), fabsf(acc[i][3][r])));
+        m = half_wave_max(m);
+        if (l32 == 0) red[(wm * 2 + wn) * 128 + 32 * i + 8 * (r >> 2) + 4 * hb + (r & 3)] = m;
+      }
+    dma_barrier();
+    uint8_t* out = (uint8_t*)(which ? p.v_out : p.k_out) + (int64_t)layer * p.out_layer_stride;
+    float* sc = (which ? p.v_scale : p.k_scale) + (int64_t)layer * p.scale_layer_stride;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * i + 8 * (r >> 2) + 4 * hb + (r & 3);
+        const int64_t grow = m0 + wm * 128 + row;
+        const float amax = fmaxf(red[(wm * 2) * 128 + row], red[(wm * 2 + 1) * 128 + row]);
+        const float scale = amax > 0.f ? amax / 448.f : 1.f;
+        const float rcp = amax > 0.f ? 448.f / amax : 0.f;
+        if (grow >= p.L) continue;
+        if (wn == 0 && l32 == 0) sc[grow] = scale;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float y = __builtin_amdgcn_fmed3f(acc[i][j][r] * rcp, 448.f, -448.f);
+          out[grow * 256 + wn * 128 + 32 * j + l32] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xFF);
+        }
+      }
+  }
 }
 
 }  // namespace
@@ -159,7 +221,11 @@ size_t bridge_workspace_bytes(int, int, int) { return 0; }
 hipError_t launch_bridge(const BridgeParams& p, void*, size_t, hipStream_t stream) {
   const int64_t mtiles = (p.L + BM - 1) / BM;
   const int ntiles = (2 * p.n_layers * 256) / BN;
-  hipLaunchKernelGGL(bridge_kernel, dim3((unsigned)(mtiles * ntiles)), dim3(BR_THREADS), 0, stream, p);
+  const dim3 grid((unsigned)(mtiles * ntiles)), block(BR_THREADS);
+  if (p.fp8)
+    hipLaunchKernelGGL(bridge_kernel<true>, grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL(bridge_kernel<false>, grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

@@ -71,6 +71,11 @@ struct BridgeParams {
   int64_t L;
   int D, n_layers;
   int64_t out_layer_stride;
+  // e4m3 output (k_out, v_out hold codes): per-row scales, layer m at m * scale_layer_stride
+  bool fp8 = false;
+  float* k_scale = nullptr;
+  float* v_scale = nullptr;
+  int64_t scale_layer_stride = 0;
 };
 size_t bridge_workspace_bytes(int n_layers, int D, int d);
 hipError_t launch_bridge(const BridgeParams& p, void* ws, size_t ws_bytes, hipStream_t stream);

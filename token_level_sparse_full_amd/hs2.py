@@ -35,6 +35,7 @@ _PROTOS = {
     "hs2_sparse_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "hs2_bridge_kv_proj": (_i, [_vp, _i64, _i, _vp, _vp, _i, _i, _vp, _vp, _i64, _vp, _sz, _vp]),
     "hs2_bridge_workspace_bytes": (_sz, [_i, _i, _i]),
+    "hs2_bridge_kv_proj_fp8": (_i, [_vp, _i64, _i, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _sz, _vp]),
     "hs2_status_str": (ctypes.c_char_p, [_i]),
     "hs2_last_error": (ctypes.c_char_p, []),
     "hs2_version": (_i, []),
@@ -184,3 +185,30 @@ def hs2_bridge_kv_proj(x, w_k, w_v, *, k_out=None, v_out=None, out_layer_stride:
                                   out_layer_stride, _ptr(ws), need, _stream(stream))
     check("hs2_bridge_kv_proj", rc)
     return k_out, v_out
+
+
+def hs2_bridge_kv_proj_fp8(x, w_k, w_v, *, k_out=None, v_out=None, k_scale=None, v_scale=None,
+                           out_layer_stride: int | None = None, scale_layer_stride: int | None = None, stream=None):
+    """KV Bridging projection into an e4m3 cache.  x [L,D]; w_k, w_v [n_layers,D,256];
+    returns (k_out, v_out) uint8 codes [n_layers,L,256] and (k_scale, v_scale) float32 [n_layers,L]."""
+    L, D = x.shape
+    n_layers, _, d = w_k.shape
+    if k_out is None:
+        k_out = torch.empty((n_layers, L, d), dtype=torch.uint8, device=x.device)
+    if v_out is None:
+        v_out = torch.empty((n_layers, L, d), dtype=torch.uint8, device=x.device)
+    if k_scale is None:
+        k_scale = torch.empty((n_layers, L), dtype=torch.float32, device=x.device)
+    if v_scale is None:
+        v_scale = torch.empty((n_layers, L), dtype=torch.float32, device=x.device)
+    if out_layer_stride is None:
+        out_layer_stride = k_out.stride(0) if k_out.dim() == 3 else L * d
+    if scale_layer_stride is None:
+        scale_layer_stride = k_scale.stride(0) if k_scale.dim() == 2 else L
+    need = int(lib().hs2_bridge_workspace_bytes(n_layers, D, d))
+    ws = workspace(need, x.device)
+    rc = lib().hs2_bridge_kv_proj_fp8(_ptr(x), L, D, _ptr(w_k), _ptr(w_v), n_layers, d, _ptr(k_out), _ptr(v_out),
+                                      _ptr(k_scale), _ptr(v_scale), out_layer_stride, scale_layer_stride,
+                                      _ptr(ws), need, _stream(stream))
+    check("hs2_bridge_kv_proj_fp8", rc)
+    return k_out, v_out, k_scale, v_scale
