@@ -426,6 +426,61 @@ def other_workloads(dev):
             mark()
         return _timed(run, 3, flush=flush)
 
+    def prefill_over_bridge(wl, kl, vl, ksl=None, vsl=None):
+        """Every prompt position runs the cross-decoder on the bridged cache: per full layer,
+        scored full attention over all L positions (query chunks of 32768), the selection,
+        and the layer's sparse layers on its indices.  Returns (full attention, select,
+        sparse) ms summed over the layers (median of 3 after 1 warm-up; inputs resident)."""
+        L, H, C = wl.L, wl.H, 32768
+        chunks = [(c0, min(L, c0 + C)) for c0 in range(0, L, C)]
+        kvd = hs2._dtype_code(kl)
+        qf = [inputs.cast(inputs.normal((1, L, H, 256), inputs.STD_QKV, wl.seed, inputs.S_QFULL_LAYER + m, dev),
+                          "bf16") for m in range(wl.n_full)]
+        qsp = [[inputs.cast(inputs.normal((1, L, H, 256), inputs.STD_QKV, wl.seed, inputs.S_QSPARSE + 8 * m + i, dev),
+                            "bf16") for i in range(wl.n_sparse)] for m in range(wl.n_full)]
+        sc = torch.empty((1, C, L), dtype=torch.float32, device=dev)
+        idx = torch.empty((1, L, ms), dtype=torch.int32, device=dev)
+        cnt = torch.empty((1, L), dtype=torch.int32, device=dev)
+        o = torch.empty((1, L, H, 256), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((1, L, H), dtype=torch.float32, device=dev)
+        o2, l2 = torch.empty_like(o), torch.empty_like(lse)
+        ws_fa = hs2.workspace(hs2.full_attn_workspace_bytes(1, C, H, L, kvd), dev)
+        ws_sp = hs2.workspace(hs2.sparse_workspace_bytes(1, L, H, ms), dev)
+
+        def run(mark):
+            for m in range(wl.n_full):
+                ks_m = None if ksl is None else ksl[m:m + 1]
+                vs_m = None if vsl is None else vsl[m:m + 1]
+                for c0, c1 in chunks:
+                    hs2.hs2_full_attn_scored(qf[m][:, c0:c1], kl[m:m + 1], vl[m:m + 1], q_pos0=c0, sm_scale=scale,
+                                             k_scale=ks_m, v_scale=vs_m, o=o[:, c0:c1], lse=lse[:, c0:c1],
+                                             scores=sc[:, : c1 - c0], ld_scores=L, ws=ws_fa)
+                    mark()
+                    hs2.hs2_select_topk_window(sc[:, : c1 - c0], q_pos0=c0, T=L, n_q=c1 - c0, window=win, topk=topk,
+                                               idx=idx[:, c0:c1], count=cnt[:, c0:c1])
+                    mark()
+                for x in qsp[m]:
+                    hs2.hs2_sparse_attn_reuse(x, kl[m:m + 1], vl[m:m + 1], idx, cnt, sm_scale=scale, k_scale=ks_m,
+                                              v_scale=vs_m, o=o2, lse=l2, ws=ws_sp)
+                mark()
+        per_layer = 2 * len(chunks) + 1
+        t = _timed(run, wl.n_full * per_layer, reps=3, warm=1)
+        t = t.reshape(wl.n_full, per_layer)
+        t_fa = float(t[:, 0:-1:2].sum())
+        t_sel = float(t[:, 1:-1:2].sum())
+        t_sp = float(t[:, -1].sum())
+        del qf, qsp, sc, idx, cnt, o, lse, o2, l2, ws_fa, ws_sp
+        torch.cuda.empty_cache()
+        return t_fa, t_sel, t_sp
+
+    def reading_b_entry(wl, t_br, t_fa, t_sel, t_sp, note):
+        fa_flop = wl.n_full * 4.0 * wl.H * D * (wl.L * (wl.L + 1) / 2.0)
+        total = t_br + t_fa + t_sel + t_sp
+        return {"ms_per_prompt": total, "prefill_tokens_per_s": wl.L / (total * 1e-3), "bridge_ms": float(t_br),
+                "full_attn_ms_all_layers": t_fa, "full_attn_tflops": fa_flop / (t_fa * 1e-3) / 1e12,
+                "full_attn_mfma_frac": fa_flop / (t_fa * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+                "select_ms_all_layers": t_sel, "sparse_ms_all_layers": t_sp, "note": note}
+
     # batched decode: 16 sequences x 32k keys, 3 sparse layers
     wl = inputs.WORKLOADS["decode_b16_32k"]
     inp = inputs.attention_inputs(B=wl.B, n_q=1, T=wl.T, H=wl.H, d=D, kv="bf16", n_sparse=wl.n_sparse, seed=wl.seed,
@@ -488,6 +543,10 @@ def other_workloads(dev):
         "bridge_mfma_frac": br_flop / (t_br * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
         "cross_decoder_step_ms": t_cross, "prefill_tokens_per_s": wl.L / ((t_br + t_cross) * 1e-3),
         "note": "bridge warm (inputs resident); the 4 bridged decode steps cold"}
+    out[wl.name + "_every_position"] = reading_b_entry(
+        wl, t_br, *prefill_over_bridge(wl, k_all, v_all),
+        "the cross-decoder at every prompt position: 4 full layers x (scored full attention over 65536 "
+        "positions, select, 8 sparse layers) on the bf16 bridged cache")
     del k_all, v_all
     torch.cuda.empty_cache()
 
@@ -515,6 +574,9 @@ def other_workloads(dev):
         "bridge_mfma_frac": br_flop / (t_br8 * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
         "cross_decoder_step_ms": t_cross8, "prefill_tokens_per_s": wl.L / ((t_br8 + t_cross8) * 1e-3),
         "note": "bridge into the e4m3 cache (per-row scales) and the bridged decode steps on it"}
+    out[wl.name + "_fp8_every_position"] = reading_b_entry(
+        wl, t_br8, *prefill_over_bridge(wl, k8, v8, ks8, vs8),
+        "the cross-decoder at every prompt position on the e4m3 bridged cache (many-query e4m3 kernel)")
     del junk
     return out
 

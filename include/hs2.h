@@ -82,8 +82,9 @@ enum hs2_dtype { HS2_F32 = 0, HS2_BF16 = 1, HS2_FP8E4M3 = 2 };
  *                            other columns are left untouched
  * Requires 1 <= n_q, 0 <= q_pos0, q_pos0 + n_q <= T, ld_scores >= q_pos0 + n_q,
  * ld_scores a multiple of 4, sm_scale > 0.
- * FP8 caches are supported when n_q * H <= 16 (decode); larger FP8 calls return
- * HS2_ERR_UNSUPPORTED.
+ * With an FP8 cache the row scales multiply the logits (k_scale) and the
+ * probabilities that weight the V rows (v_scale); the scores are the unscaled
+ * probabilities.
  */
 int hs2_full_attn_scored(const void* q, int q_dtype, int B, int n_q, int H, int d,
                          const void* k, const void* v, int kv_dtype,
@@ -97,7 +98,7 @@ int hs2_full_attn_scored(const void* q, int q_dtype, int B, int n_q, int H, int 
  *     partial softmax states of the key chunks (about B * T * 64 bytes);
  *   bf16 prefill: the lse of every row in log2 units (B * n_q * H * 4 bytes),
  *     written by the lse pass and read by the probability pass;
- *   float32 prefill: none (0).
+ *   float32 and FP8 prefill: none (0).
  * The contents are scratch; calls that share a workspace must not overlap. */
 size_t hs2_full_attn_workspace_bytes(int B, int n_q, int H, int64_t T, int kv_dtype);
 

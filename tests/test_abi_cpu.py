@@ -62,7 +62,8 @@ def full(lib, **kw):
     (dict(ws=None), hs2.HS2_ERR_WORKSPACE),
     (dict(wsb=16), hs2.HS2_ERR_WORKSPACE),
     (dict(ws=A + 16), hs2.HS2_ERR_ALIGN),
-    (dict(kvd=FP8, ks=A, vs=A, n_q=4, q0=96, H=16), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(kvd=FP8, ks=None, vs=A, n_q=4, q0=96, H=16), hs2.HS2_ERR_NULL),
+    (dict(kvd=FP8, ks=A, vs=A + 2, n_q=4, q0=96, H=16), hs2.HS2_ERR_ALIGN),
 ])
 def test_full_attn_rejects(lib, kw, code):
     assert full(lib, **kw) == code

@@ -151,11 +151,17 @@ def _check_full(inp, o, lse, scores, q_pos0, kv):
     ("f32", 16, 64, 40, 104),
     ("bf16", 2, 0, 50, 50),
     ("bf16", 1, 10, 90, 100),
+    ("e4m3", 16, 300, 333, 700),
+    ("e4m3", 16, 0, 70, 70),
+    ("e4m3", 8, 130, 77, 300),
+    ("e4m3", 4, 5, 100, 110),
+    ("e4m3", 1, 10, 90, 100),
 ])
 def test_full_attn_prefill_parity(kv, H, q_pos0, n_q, T):
     say("prefill", kv, H, q_pos0, n_q, T)
     inp = inputs.attention_inputs(B=2, n_q=n_q, T=T, H=H, d=256, kv=kv, n_sparse=0, seed=21, device=DEV)
-    o, lse, scores = hs2.hs2_full_attn_scored(inp["q"], inp["k"], inp["v"], q_pos0=q_pos0, sm_scale=SCALE)
+    o, lse, scores = hs2.hs2_full_attn_scored(inp["q"], inp["k"], inp["v"], q_pos0=q_pos0, sm_scale=SCALE,
+                                              k_scale=inp["k_scale"], v_scale=inp["v_scale"])
     torch.cuda.synchronize()
     _check_full(inp, o, lse, scores, q_pos0, kv)
 

@@ -113,9 +113,6 @@ int hs2_full_attn_scored(const void* q, int q_dtype, int B, int n_q, int H, int 
   if (q_pos0 < 0 || q_pos0 + n_q > T) return fail(HS2_ERR_SHAPE, "need 0 <= q_pos0 and q_pos0 + n_q <= T");
   if (ld_scores < q_pos0 + n_q || ld_scores % 4 != 0)
     return fail(HS2_ERR_SHAPE, "ld_scores must be >= q_pos0 + n_q and a multiple of 4");
-  const bool decode = hs2::attn_uses_decode(n_q, H);
-  if (kv_dtype == HS2_FP8E4M3 && !decode)
-    return fail(HS2_ERR_UNSUPPORTED, "FP8 caches are supported for n_q * H <= 16 only");
   const size_t need = hs2::attn_workspace_bytes(B, n_q, H, T, kv_kind(kv_dtype));
   if (need > 0) {
     if (!workspace) return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes required", need);

@@ -565,7 +565,7 @@ size_t prefill_bf16_workspace_bytes(int B, int n_q, int H);                     
 bool attn_uses_decode(int n_q, int H) { return n_q * H <= 16; }
 
 size_t attn_workspace_bytes(int B, int n_q, int H, int64_t T, int kv_kind) {
-  if (!attn_uses_decode(n_q, H)) return kv_kind == KV_F32 ? 0 : prefill_bf16_workspace_bytes(B, n_q, H);
+  if (!attn_uses_decode(n_q, H)) return kv_kind == KV_BF16 ? prefill_bf16_workspace_bytes(B, n_q, H) : 0;
   return decode_ws_layout(B, T, nullptr, nullptr);
 }
 

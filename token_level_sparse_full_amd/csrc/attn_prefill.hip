@@ -32,16 +32,17 @@ constexpr int PF_THREADS = PF_WAVES * kWave;
 template <int KV>
 struct PfCfg {
   static constexpr bool F32 = (KV == KV_F32);
+  static constexpr bool FP8 = (KV == KV_E4M3);
   static constexpr int KT = F32 ? 32 : 64;          // keys per tile
-  static constexpr int ROWB = F32 ? 1024 : 512;     // bytes per K/V row
-  static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
-  static constexpr int TILE_BYTES = KT * ROWB;      // 32 KB
-  static constexpr int LOADS = TILE_BYTES / 16 / PF_THREADS;  // 16-byte loads per thread per tile
+  static constexpr int ROWB = F32 ? 1024 : 512;     // bytes per K/V row in LDS (e4m3 rows are widened to bf16)
+  static constexpr int GROWB = FP8 ? 256 : ROWB;    // bytes per K/V row in HBM
+  static constexpr int GCPR = GROWB / 16;           // 16-byte chunks per HBM row
+  static constexpr int LOADS = KT * GROWB / 16 / PF_THREADS;  // 16-byte loads per thread per tile
   static constexpr int P_PITCH = F32 ? 144 : 72;    // bytes per key row of the P buffer
   static constexpr int P_BYTES = KT * P_PITCH;
 };
 
-constexpr int kPfSmem = 2 * 32768 + PF_WAVES * 64 * 72 + PF_WAVES * 32 * 4;
+constexpr int kPfSmem = 2 * 32768 + PF_WAVES * 64 * 72 + PF_WAVES * 32 * 4 + 2 * 64 * 4;
 static_assert(PF_WAVES * 32 * 144 <= PF_WAVES * 64 * 72, "f32 P buffer fits");
 
 __device__ __forceinline__ int k_swz(int row, int ch) { return ch ^ (row & 15); }
@@ -59,6 +60,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(const AttnParams
   char* v_lds = smem + 32768;
   char* p_lds_all = smem + 65536;
   float* lse_lds_all = (float*)(p_lds_all + PF_WAVES * 64 * 72);
+  float* ks_lds = lse_lds_all + PF_WAVES * 32;  // e4m3 caches: the tile's K and V row scales
+  float* vs_lds = ks_lds + 64;
 
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int hb = l >> 5, l32 = l & 31;
@@ -101,32 +104,61 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(const AttnParams
   }
 
   // ---- tile staging: global -> registers -> LDS (swizzled)
-  const char* kg = (const char*)p.k + kv_row0 * C::ROWB;
-  const char* vg = (const char*)p.v + kv_row0 * C::ROWB;
+  // An e4m3 chunk of 16 codes becomes two bf16 chunks (exact: every e4m3 value
+  // is a bf16 value); the row scales are applied to the logits and to P.
+  const char* kg = (const char*)p.k + kv_row0 * C::GROWB;
+  const char* vg = (const char*)p.v + kv_row0 * C::GROWB;
   auto load_tile = [&](const char* base, int kt, u32x4* r) {
 #pragma unroll
     for (int it = 0; it < C::LOADS; ++it) {
       const int c = it * PF_THREADS + tid;
-      const int row = c / C::CPR, ch = c % C::CPR;
+      const int row = c / C::GCPR, ch = c % C::GCPR;
       const int64_t key = (int64_t)kt * KT + row;
-      r[it] = key < n_keys ? *(const u32x4*)(base + key * C::ROWB + ch * 16) : u32x4{0u, 0u, 0u, 0u};
+      r[it] = key < n_keys ? *(const u32x4*)(base + key * C::GROWB + ch * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  // e4m3: threads 0-15 fetch 4 K scales each, threads 16-31 4 V scales; absent keys get 0
+  auto load_scales = [&](int kt, float* sr) {
+    if constexpr (C::FP8) {
+      const int i = 4 * (tid & 15);
+      const float* src = (tid < 16 ? p.k_scale : p.v_scale) + kv_row0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t key = (int64_t)kt * KT + i + e;
+        sr[e] = (tid < 32 && key < n_keys) ? src[key] : 0.f;
+      }
+    }
+  };
+  auto store_scales = [&](const float* sr) {
+    if constexpr (C::FP8) {
+      if (tid < 32) {
+        float* dst = (tid < 16 ? ks_lds : vs_lds) + 4 * (tid & 15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[e] = sr[e];
+      }
+    }
+  };
+  auto put_chunk = [&](char* lds, int row, int ch, u32x4 x, bool vlayout) {
+    auto swz = [&](int c) { return vlayout ? (C::F32 ? c : v_swz(row, c)) : k_swz(row, c); };
+    if constexpr (C::FP8) {
+      *(bf16x8*)(lds + row * C::ROWB + swz(2 * ch) * 16) = e4m3x8_to_bf16(x[0], x[1]);
+      *(bf16x8*)(lds + row * C::ROWB + swz(2 * ch + 1) * 16) = e4m3x8_to_bf16(x[2], x[3]);
+    } else {
+      *(u32x4*)(lds + row * C::ROWB + swz(ch) * 16) = x;
     }
   };
   auto store_k = [&](const u32x4* r) {
 #pragma unroll
     for (int it = 0; it < C::LOADS; ++it) {
       const int c = it * PF_THREADS + tid;
-      const int row = c / C::CPR, ch = c % C::CPR;
-      *(u32x4*)(k_lds + row * C::ROWB + k_swz(row, ch) * 16) = r[it];
+      put_chunk(k_lds, c / C::GCPR, c % C::GCPR, r[it], false);
     }
   };
   auto store_v = [&](const u32x4* r) {
 #pragma unroll
     for (int it = 0; it < C::LOADS; ++it) {
       const int c = it * PF_THREADS + tid;
-      const int row = c / C::CPR, ch = c % C::CPR;
-      const int chs = C::F32 ? ch : v_swz(row, ch);
-      *(u32x4*)(v_lds + row * C::ROWB + chs * 16) = r[it];
+      put_chunk(v_lds, c / C::GCPR, c % C::GCPR, r[it], true);
     }
   };
   // K fragment of key row `key` (tile-local) for K-step s (bf16) / chunk-step cs (f32)
@@ -138,12 +170,18 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(const AttnParams
   float m_run = kNegInf, z_run = 0.f;
   const int64_t my_pos = pos_of_row(l32);
   u32x4 stg[2 * C::LOADS];
+  float sst[4];
   load_tile(kg, 0, stg);
+  load_scales(0, sst);
   for (int kt = 0; kt < ntiles; ++kt) {
     __syncthreads();
     store_k(stg);
+    store_scales(sst);
     __syncthreads();
-    if (kt + 1 < ntiles) load_tile(kg, kt + 1, stg);
+    if (kt + 1 < ntiles) {
+      load_tile(kg, kt + 1, stg);
+      load_scales(kt + 1, sst);
+    }
     f32x16 sacc[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -169,7 +207,9 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(const AttnParams
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = sacc[j][r] * p.scale_log2;
+        float c = p.scale_log2;
+        if constexpr (C::FP8) c *= ks_lds[32 * j + 8 * (r >> 2) + 4 * hb + (r & 3)];
+        float x = sacc[j][r] * c;
         if (need_mask) {
           const int64_t key = kbase + 32 * j + 8 * (r >> 2) + 4 * hb + (r & 3);
           x = key <= my_pos ? x : kNegInf;
@@ -214,14 +254,17 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(const AttnParams
 
   load_tile(kg, 0, stg);
   load_tile(vg, 0, stg + C::LOADS);
+  load_scales(0, sst);
   for (int kt = 0; kt < ntiles; ++kt) {
     __syncthreads();
     store_k(stg);
     store_v(stg + C::LOADS);
+    store_scales(sst);
     __syncthreads();
     if (kt + 1 < ntiles) {
       load_tile(kg, kt + 1, stg);
       load_tile(vg, kt + 1, stg + C::LOADS);
+      load_scales(kt + 1, sst);
     }
     const int64_t kbase = (int64_t)kt * KT;
     const bool need_mask = kbase + KT - 1 > pos_first;
@@ -246,9 +289,10 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(const AttnParams
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int64_t key = kbase + 32 * j + l32;
+      const float c = C::FP8 ? p.scale_log2 * ks_lds[32 * j + l32] : p.scale_log2;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(sacc[j][r] * p.scale_log2 - lse2[r]);
+        const float e = fast_exp2(sacc[j][r] * c - lse2[r]);
         sacc[j][r] = (!need_mask || key <= rpos[r]) ? e : 0.f;
       }
     }
@@ -285,10 +329,15 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(const AttnParams
         for (int r = 0; r < 16; ++r) put(8 * (r >> 2) + 4 * hb + (r & 3), sacc[j][r]);
       }
     }
-    // ---- P -> LDS as [key][row]
+    // ---- P -> LDS as [key][row]; an e4m3 cache's V row scale rides on P
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int key = 32 * j + l32;
+      if constexpr (C::FP8) {
+        const float vsc = vs_lds[key];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[j][r] *= vsc;
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int row0 = 8 * q + 4 * hb;
@@ -375,7 +424,11 @@ hipError_t launch_prefill_bf16(const AttnParams& p, void* ws, hipStream_t stream
 
 hipError_t launch_prefill(const AttnParams& p, int kv_kind, void* ws, hipStream_t stream) {
   if (p.B * p.n_q == 0) return hipSuccess;
-  return kv_kind == KV_F32 ? launch_prefill_kv<KV_F32>(p, stream) : launch_prefill_bf16(p, ws, stream);
+  switch (kv_kind) {
+    case KV_F32: return launch_prefill_kv<KV_F32>(p, stream);
+    case KV_E4M3: return launch_prefill_kv<KV_E4M3>(p, stream);
+    default: return launch_prefill_bf16(p, ws, stream);
+  }
 }
 
 }  // namespace hs2
