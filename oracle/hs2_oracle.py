@@ -9,6 +9,9 @@ Everything here is the plain definition written out, slowly and in float64:
 * ``full_attn_scored``   exact causal MQA attention plus the per-token score row
 * ``select_topk_window`` the token-level selection: forced recent window plus
                          the top-k highest-scoring older tokens
+* ``select_blocks_window`` the block-level selection it replaces (kept as an
+                         ablation): the same window plus the best-scoring
+                         aligned blocks of older tokens, same token budget
 * ``sparse_attn_reuse``  attention restricted to a selected index set
 * ``bridge_kv_proj``     the KV-Bridging re-projection of hidden states
 * ``bridge_kv_proj_fp8`` the same re-projection stored as an FP8 e4m3 cache
@@ -63,6 +66,8 @@ __all__ = [
     "decode_rows",
     "full_attn_scored",
     "select_topk_window",
+    "block_score",
+    "select_blocks_window",
     "sparse_attn_reuse",
     "bridge_kv_proj",
     "f64_to_e4m3_codes",
@@ -229,6 +234,67 @@ def select_topk_window(scores: np.ndarray, p: int, window: int = 128, topk: int 
     win = np.arange(n_cand, n, dtype=np.int64)
     sel = np.sort(np.concatenate([top, win]))
     return sel, len(sel), tau
+
+
+def block_score(vals: np.ndarray, dtype=np.float32):
+    """Sum of the scores of one block, as a pairwise tree in ``dtype``.
+
+    The block length must be a power of two.  Adjacent pairs are added first,
+    then adjacent pairs of those sums, and so on; every addition is rounded to
+    ``dtype`` (round to nearest even).  The pages fix no precision for this
+    sum; the decision it feeds is taken in float32 on both sides, in this
+    order (positions past the candidates count as 0, which adds exactly).
+    """
+    t = np.asarray(vals, dtype=dtype)
+    assert t.size >= 1 and t.size & (t.size - 1) == 0, "block length must be a power of two"
+    while t.size > 1:
+        t = (t[0::2] + t[1::2]).astype(dtype)
+    return t[0]
+
+
+def select_blocks_window(scores: np.ndarray, p: int, window: int = 128, topk: int = 1024, block: int = 64,
+                         dtype=np.float32):
+    """Block-level selection with the forced window (the HySparse granularity,
+    kept as an ablation of the token-level selection).
+
+    HySparse2 pages: 10100.com article, section on the first refinement --
+    earlier sparse attention selects fixed blocks of 64 or 128 tokens, so one
+    useful token keeps its whole block; agihunt.info summary, ablation
+    paragraph -- token-level against block-level selection at the same
+    1024-token budget, blocks of 64; evolve.pub review, Table 3 claim.
+
+    Reading of the steps the pages leave open: the window W = [p-window+1, p]
+    and the candidates C = [0, p-window] are those of the token-level
+    selection.  C is cut into aligned blocks B_b = [b*block, (b+1)*block - 1]
+    intersected with C (only the last one can be partial).  A block scores the
+    sum of its candidates' scores (``block_score``).  The topk // block blocks
+    of highest score are selected, ties to the lower block index, and S = W
+    together with the candidates of the selected blocks.  When |C| <= topk
+    every key 0..p is selected.  With block = 1 this is select_topk_window.
+
+    Returns (idx, count, tau) like select_topk_window; tau is the score of the
+    last block admitted (None when no cut was needed).
+    """
+    assert topk % block == 0
+    n = p + 1
+    s = np.asarray(scores, dtype=dtype)[:n]
+    n_cand = max(0, n - window)
+    if n_cand <= topk:
+        return np.arange(n, dtype=np.int64), n, None
+    nb = (n_cand + block - 1) // block
+    sig = []
+    for b in range(nb):
+        vals = np.zeros(block, dtype=dtype)
+        hi = min(n_cand, (b + 1) * block)
+        vals[: hi - b * block] = s[b * block: hi]
+        sig.append(float(block_score(vals, dtype)))
+    order = sorted(range(nb), key=lambda b: (-sig[b], b))
+    nsel = topk // block
+    top = order[:nsel]
+    toks = [np.arange(b * block, min(n_cand, (b + 1) * block), dtype=np.int64) for b in top]
+    win = np.arange(n_cand, n, dtype=np.int64)
+    sel = np.sort(np.concatenate(toks + [win]))
+    return sel, len(sel), sig[order[nsel - 1]]
 
 
 # ----------------------------------------------------------------------------

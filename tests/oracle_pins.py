@@ -283,6 +283,96 @@ def pin_select_window_scores_ignored(orc):
     np.testing.assert_array_equal(a, b)
 
 
+def pin_select_blocks_golden(orc):
+    with open(os.path.join(GOLDEN, "select_blocks_worked_example.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        idx, count, tau = orc.select_blocks_window(np.array(c["scores"], dtype=np.float32), c["p"], c["window"],
+                                                   c["topk"], c["block"])
+        assert list(idx) == c["expected"], c["name"]
+        assert count == len(c["expected"]), c["name"]
+        assert tau == c["tau"], c["name"]
+
+
+def pin_select_blocks_of_one_are_tokens(orc):
+    """Blocks of one token are the token-level selection (pinned on its own above)."""
+    r = _rng(24)
+    for p in [0, 127, 128, 1151, 1152, 1153, 1300, 2500]:
+        s = (r.integers(0, 6, size=p + 1) / 8.0).astype(np.float32)   # many ties
+        a = orc.select_blocks_window(s, p, 128, 1024, 1)
+        b = orc.select_topk_window(s.astype(np.float64), p, 128, 1024)
+        assert list(a[0]) == list(b[0]) and a[1] == b[1], p
+
+
+def _count_rank_blocks(s, p, window, topk, block):
+    """Brute force: exact block sums (math.fsum), block b chosen iff fewer than
+    topk // block blocks beat it (higher sum, or equal sum and lower index)."""
+    n = p + 1
+    n_cand = max(0, n - window)
+    if n_cand <= topk:
+        return list(range(n))
+    nb = -(-n_cand // block)
+    sums = [math.fsum(s[j] for j in range(b * block, min(n_cand, (b + 1) * block))) for b in range(nb)]
+    out = set(range(n_cand, n))
+    for b in range(nb):
+        beat = sum(1 for c in range(nb) if sums[c] > sums[b] or (sums[c] == sums[b] and c < b))
+        if beat < topk // block:
+            out |= set(range(b * block, min(n_cand, (b + 1) * block)))
+    return sorted(out)
+
+
+def pin_select_blocks_brute_force(orc):
+    r = _rng(25)
+    for trial in range(300):
+        block = int(2 ** r.integers(0, 4))
+        topk = block * int(r.integers(1, 4))
+        window = int(r.integers(1, 5))
+        p = int(r.integers(0, 40))
+        s = r.integers(0, 4, size=p + 1).astype(np.float64) / 4.0   # exact sums, many ties
+        idx, count, _ = orc.select_blocks_window(s.astype(np.float32), p, window, topk, block)
+        ref = _count_rank_blocks(s, p, window, topk, block)
+        assert list(idx) == ref, (trial, s, p, window, topk, block)
+        assert count == len(ref)
+
+
+def pin_block_score_pairwise_order(orc):
+    """The float32 tree adds adjacent pairs first: 2^24 + 4 is reached exactly,
+    where a left-to-right sum would lose every 1 to rounding (2^24 + 1 rounds
+    to 2^24).  Exact sums are returned unchanged."""
+    v = np.array([2.0 ** 24, 0, 0, 0, 1, 1, 1, 1], dtype=np.float32)
+    assert float(orc.block_score(v)) == 2.0 ** 24 + 4
+    assert float(orc.block_score(v[::-1].copy())) == 2.0 ** 24 + 4
+    w = np.array([1, 2.0 ** 24, 1, 0], dtype=np.float32)
+    assert float(orc.block_score(w)) == 2.0 ** 24                 # (1 + 2^24) rounds to even, then + 1 again
+    assert float(orc.block_score(w, np.float64)) == 2.0 ** 24 + 2
+    r = _rng(26)
+    x = r.integers(0, 1 << 10, size=64).astype(np.float32) / 1024.0
+    assert float(orc.block_score(x)) == math.fsum(x.astype(np.float64))
+    assert float(orc.block_score(np.array([0.75], dtype=np.float32))) == 0.75
+
+
+def pin_select_blocks_invariants(orc):
+    """Window inside S, ascending, the candidates of S are whole blocks (cut at
+    the last candidate), and exactly topk // block blocks once there is a cut."""
+    r = _rng(27)
+    for p in [0, 1, 127, 128, 1151, 1152, 1153, 1200, 1215, 1216, 1217, 4000]:
+        s = r.random(p + 1).astype(np.float32)
+        idx, count, tau = orc.select_blocks_window(s, p, 128, 1024, 64)
+        assert count == len(idx) <= 1152
+        assert np.all(np.diff(idx) > 0) and idx[-1] == p
+        assert set(range(max(0, p - 127), p + 1)) <= set(idx.tolist())
+        n_cand = max(0, p - 127)
+        chosen = idx[idx < n_cand]
+        if tau is None:
+            assert count == p + 1
+            continue
+        blocks = sorted(set((chosen // 64).tolist()))
+        assert len(blocks) == 16
+        for b in blocks:
+            assert set(range(b * 64, min(n_cand, b * 64 + 64))) <= set(chosen.tolist())
+        assert count == 128 + len(chosen)
+
+
 # ---------------------------------------------------------------------------
 # sparse attention over the selected set
 # ---------------------------------------------------------------------------

@@ -30,10 +30,13 @@ MUTATIONS = [
     ("default scale 1/d", "sm_scale = 1.0 / math.sqrt(d)\n    o = np.zeros", "sm_scale = 1.0 / d\n    o = np.zeros"),
     ("tie to higher index", "key=lambda j: (-s[j], j)", "key=lambda j: (-s[j], -j)"),
     ("ascending scores", "key=lambda j: (-s[j], j)", "key=lambda j: (s[j], j)"),
-    ("window one short", "n_cand = max(0, n - window)", "n_cand = max(0, n - window + 1)"),
-    ("window one long", "n_cand = max(0, n - window)", "n_cand = max(0, n - window - 1)"),
+    ("window one short", "n_cand = max(0, n - window)\n    if n_cand <= topk:\n        sel = np.arange", "n_cand = max(0, n - window + 1)\n    if n_cand <= topk:\n        sel = np.arange"),
+    ("block window one short", "n_cand = max(0, n - window)\n    if n_cand <= topk:\n        return np.arange", "n_cand = max(0, n - window + 1)\n    if n_cand <= topk:\n        return np.arange"),
+    ("window one long", "n_cand = max(0, n - window)\n    if n_cand <= topk:\n        sel = np.arange", "n_cand = max(0, n - window - 1)\n    if n_cand <= topk:\n        sel = np.arange"),
+    ("block window one long", "n_cand = max(0, n - window)\n    if n_cand <= topk:\n        return np.arange", "n_cand = max(0, n - window - 1)\n    if n_cand <= topk:\n        return np.arange"),
     ("top-k one short", "top = np.array(order[:topk]", "top = np.array(order[:topk - 1]"),
-    ("cut test off by one", "if n_cand <= topk:", "if n_cand < topk:"),
+    ("cut test off by one", "n_cand = max(0, n - window)\n    if n_cand <= topk:\n        sel = np.arange", "n_cand = max(0, n - window)\n    if n_cand < topk:\n        sel = np.arange"),
+    ("block cut test off by one", "n_cand = max(0, n - window)\n    if n_cand <= topk:\n        return np.arange", "n_cand = max(0, n - window)\n    if n_cand < topk:\n        return np.arange"),
     ("tau from wrong rank", "tau = float(s[order[topk - 1]])", "tau = float(s[order[topk]])"),
     ("sparse values unsorted", "vals = np.asarray(v, dtype=np.float64)[sel]",
      "vals = np.asarray(v, dtype=np.float64)[np.sort(sel)]"),
@@ -54,6 +57,15 @@ MUTATIONS = [
     ("e4m3 encode sign lost", "np.where(np.signbit(y), 0x80, 0)", "np.where(np.signbit(y), 0, 0)"),
     ("fp8 scale for the fnuz range", "(amax / 448.0).astype(np.float32)", "(amax / 240.0).astype(np.float32)"),
     ("fp8 V quantized from K", "vc, vs = quantize(v)", "vc, vs = quantize(k)"),
+    ("block ties to the higher index", "key=lambda b: (-sig[b], b))", "key=lambda b: (-sig[b], -b))"),
+    ("block tree adds a pair twice", "t = (t[0::2] + t[1::2]).astype(dtype)", "t = (t[0::2] + t[0::2]).astype(dtype)"),
+    ("block sum left to right", "t = (t[0::2] + t[1::2]).astype(dtype)",
+     "t = np.array([np.cumsum(t, dtype=dtype)[-1]], dtype=dtype)"),
+    ("block sum counts the window", "hi = min(n_cand, (b + 1) * block)", "hi = min(n, (b + 1) * block)"),
+    ("block partial block dropped", "nb = (n_cand + block - 1) // block\n    sig", "nb = n_cand // block\n    sig"),
+    ("block one block too many", "nsel = topk // block", "nsel = topk // block + 1"),
+    ("block tokens past the candidates", "toks = [np.arange(b * block, min(n_cand, (b + 1) * block)",
+     "toks = [np.arange(b * block, min(n, (b + 1) * block)"),
 ]
 
 
