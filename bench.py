@@ -355,6 +355,7 @@ def main():
     }
 
     if not args.no_others:
+        result["ablation_block_selection"] = ablation_blocks(hs2, q, k, v, qs, chunks, scale, ld, window, topk)
         result["other_workloads"] = other_workloads(dev)
 
     # ---------------------------------------------------------------- oracle sample (host cores)
@@ -362,6 +363,70 @@ def main():
         result["cpu_baseline"], result["sample_parity"] = cpu_baseline(
             args, inp, needles, step, keep_rows, idx, cnt, o_full, o_sp, L, H, scale, window, topk)
     print(json.dumps(result), flush=True)
+
+
+def ablation_blocks(hs2, q, k, v, qs, chunks, scale, ld, window, topk, block=64):
+    """The block-level selection (aligned 64-token blocks, same 1024-token budget) on the
+    same scores as the token-level one, and the sparse layer on its indices: HIP-event
+    times of both selectors per chunk (second of two runs each) and the median of 3 sparse
+    layers on each index set.  The full-attention launches that produce the scores are
+    not timed."""
+    import numpy as np
+    import torch
+
+    dev = q.device
+    L, H = q.shape[1], q.shape[2]
+    C = chunks[0][1] - chunks[0][0]
+    ms = window + topk
+    scores = torch.empty((1, C, ld), dtype=torch.float32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, L, H), dtype=torch.float32, device=dev)
+    idx_t = torch.empty((1, L, ms), dtype=torch.int32, device=dev)
+    cnt_t = torch.empty((1, L), dtype=torch.int32, device=dev)
+    idx_b, cnt_b = torch.empty_like(idx_t), torch.empty_like(cnt_t)
+    ws_b = hs2.workspace(max(hs2.select_blocks_workspace_bytes(1, c1 - c0, L, c0, window, block)
+                             for c0, c1 in chunks), dev)
+
+    def ev_time(fn, reps):
+        t = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            t.append(a.elapsed_time(b))
+        return t
+
+    t_tok = t_blk = 0.0
+    for c0, c1 in chunks:
+        hs2.hs2_full_attn_scored(q[:, c0:c1], k, v, q_pos0=c0, sm_scale=scale, o=o[:, c0:c1], lse=lse[:, c0:c1],
+                                 scores=scores[:, : c1 - c0], ld_scores=ld)
+        t_tok += ev_time(lambda: hs2.hs2_select_topk_window(scores[:, : c1 - c0], q_pos0=c0, T=L, n_q=c1 - c0,
+                                                            window=window, topk=topk, idx=idx_t[:, c0:c1],
+                                                            count=cnt_t[:, c0:c1]), 2)[-1]
+        t_blk += ev_time(lambda: hs2.hs2_select_blocks_window(scores[:, : c1 - c0], q_pos0=c0, T=L, n_q=c1 - c0,
+                                                              window=window, topk=topk, block=block,
+                                                              idx=idx_b[:, c0:c1], count=cnt_b[:, c0:c1], ws=ws_b),
+                         2)[-1]
+    o2 = torch.empty_like(q)
+    l2 = torch.empty_like(lse)
+    sp_tok = float(np.median(ev_time(lambda: hs2.hs2_sparse_attn_reuse(qs[0], k, v, idx_t, cnt_t, sm_scale=scale,
+                                                                       o=o2, lse=l2), 3)))
+    sp_blk = float(np.median(ev_time(lambda: hs2.hs2_sparse_attn_reuse(qs[0], k, v, idx_b, cnt_b, sm_scale=scale,
+                                                                       o=o2, lse=l2), 3)))
+    rows = np.arange(L, dtype=np.float64) + 1.0
+    cand = np.maximum(rows - window, 0)
+    read_bytes = np.where(cand > topk, cand, 0).sum() * 4
+    n_sel_tok = float(cnt_t.sum().item())
+    n_sel_blk = float(cnt_b.sum().item())
+    del scores, o, lse, idx_t, cnt_t, idx_b, cnt_b, ws_b, o2, l2
+    torch.cuda.empty_cache()
+    return {"block": block, "select_token_ms": t_tok, "select_block_ms": t_blk,
+            "select_block_gbs_of_scores": read_bytes / (t_blk * 1e-3) / 1e9,
+            "sparse_layer_token_ms": sp_tok, "sparse_layer_block_ms": sp_blk,
+            "selected_keys_token": n_sel_tok, "selected_keys_block": n_sel_blk,
+            "note": "same scores, same 1024-token budget; block sums in float32 (pairwise tree)"}
 
 
 def _timed(run, stages: int, reps: int = 10, warm: int = 3, flush=None):

@@ -59,6 +59,7 @@ enum hs2_dtype { HS2_F32 = 0, HS2_BF16 = 1, HS2_FP8E4M3 = 2 };
 #define HS2_HEAD_DIM 256
 #define HS2_MAX_HEADS 16
 #define HS2_MAX_SELECT 4096 /* largest window + topk accepted by the selector */
+#define HS2_MAX_BLOCKS 16384 /* most candidate blocks in one row of the block-level selector */
 
 /*
  * hs2_full_attn_scored - scored full attention (the selector layer).
@@ -139,6 +140,46 @@ int hs2_select_topk_window(const float* scores, int64_t ld_scores, int B, int n_
  * and per-segment counts there.  The contents are scratch: nothing persists
  * between calls, and calls that share a workspace must not overlap. */
 size_t hs2_select_workspace_bytes(int B, int n_q, int64_t T, int64_t q_pos0);
+
+/*
+ * hs2_select_blocks_window - block-level top-k with the forced recent window,
+ * the granularity that the token-level selection replaces (kept to measure
+ * what each costs).
+ *
+ * Defines (HySparse2 pages: agihunt.info summary, ablation paragraph --
+ * token-level against block-level selection at the same 1024-token budget,
+ * blocks of 64; 10100.com article, section on the first refinement -- block
+ * selection keeps fixed blocks of 64 or 128 tokens).  The pages fix neither
+ * the block score nor the window's place; this library takes:
+ *   for query i of sequence b at position p = q_pos0 + i:
+ *     W = [max(0, p-window+1), p], C = [0, p-window]  (as the token-level call)
+ *     if |C| <= topk: S = [0, p]
+ *     else: the blocks B_c = [c*block, (c+1)*block - 1] & C, c = 0 .. ceil(|C|/block)-1;
+ *           sigma_c = float32 sum of the scores of B_c as a pairwise tree
+ *                     (adjacent pairs first, then pairs of those sums, ...);
+ *           S = W + the candidates of the topk/block blocks of largest
+ *               sigma, ties to the lower block
+ *   idx[b,i,:]  the members of S in ascending order, then -1 up to window+topk
+ *   count[b,i]  |S| (<= window + topk; less when the last candidate block is
+ *               partial and selected)
+ *
+ *   scores, idx, count as for hs2_select_topk_window; the output feeds
+ *   hs2_sparse_attn_reuse unchanged.
+ * Requires block a power of two in [4, 256], topk a multiple of block,
+ * window >= 1, window + topk <= HS2_MAX_SELECT, at most HS2_MAX_BLOCKS
+ * candidate blocks in the last row (ceil((q_pos0 + n_q - window) / block)),
+ * and a workspace of hs2_select_blocks_workspace_bytes() bytes (the block
+ * sums; scratch, calls sharing it must not overlap).
+ */
+int hs2_select_blocks_window(const float* scores, int64_t ld_scores, int B, int n_q, int64_t T,
+                             int64_t q_pos0, int window, int topk, int block,
+                             int32_t* idx, int32_t* count,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace of hs2_select_blocks_window: B * n_q * ceil((q_pos0+n_q-window)/block)
+ * float32 block sums, rounded up to 256 bytes (0 when no row has candidates;
+ * 0 also for invalid arguments). */
+size_t hs2_select_blocks_workspace_bytes(int B, int n_q, int64_t T, int64_t q_pos0, int window, int block);
 
 /*
  * hs2_sparse_attn_reuse - a sparse layer over the reused index set.

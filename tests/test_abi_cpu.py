@@ -19,7 +19,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = hs2.header_symbols()
-    assert len(names) == 12
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
 
@@ -196,3 +196,39 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(hs2, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         hs2.lib()
+
+
+def blocks(lib, **kw):
+    a = dict(sc=A, ld=2048, B=1, n_q=4, T=2048, q0=2000, w=128, k=1024, blk=64, idx=A, cnt=A, ws=A, wsb=1 << 40)
+    a.update(kw)
+    return lib.hs2_select_blocks_window(a["sc"], a["ld"], a["B"], a["n_q"], a["T"], a["q0"], a["w"], a["k"],
+                                        a["blk"], a["idx"], a["cnt"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sc=None), hs2.HS2_ERR_NULL),
+    (dict(blk=48), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(blk=2), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(blk=512), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(k=1000), hs2.HS2_ERR_SHAPE),
+    (dict(w=0), hs2.HS2_ERR_SHAPE),
+    (dict(w=128, k=4096), hs2.HS2_ERR_SHAPE),
+    (dict(q0=2045), hs2.HS2_ERR_SHAPE),
+    (dict(ld=2002), hs2.HS2_ERR_SHAPE),
+    (dict(sc=A + 4), hs2.HS2_ERR_ALIGN),
+    (dict(ws=None), hs2.HS2_ERR_WORKSPACE),
+    (dict(wsb=64), hs2.HS2_ERR_WORKSPACE),
+    (dict(ws=A + 16), hs2.HS2_ERR_ALIGN),
+    # 16385 candidate blocks of 4 tokens in the last row
+    (dict(blk=4, T=65800, ld=65800, q0=65668, n_q=4), hs2.HS2_ERR_UNSUPPORTED),
+])
+def test_select_blocks_rejects(lib, kw, code):
+    assert blocks(lib, **kw) == code
+    assert lib.hs2_last_error().decode() != ""
+
+
+def test_select_blocks_workspace_size(lib):
+    # last row p = 2003: 1876 candidates -> 30 blocks of 64, 4 rows of 30 float32 sums
+    assert lib.hs2_select_blocks_workspace_bytes(1, 4, 2048, 2000, 128, 64) == 512
+    assert lib.hs2_select_blocks_workspace_bytes(1, 4, 2048, 0, 128, 64) == 0
+    assert lib.hs2_select_blocks_workspace_bytes(1, 4, 2048, 2000, 128, 48) == 0

@@ -115,6 +115,83 @@ def test_select_parity(q_pos0, n_q, T):
     _select_case(sc, q_pos0, T, 128, 1024)
 
 
+def _score_rows(rng, B, n_q, q_pos0, ld):
+    sc = np.zeros((B, n_q, ld), dtype=np.float32)
+    for b in range(B):
+        for i in range(n_q):
+            n = q_pos0 + i + 1
+            mode = (b * n_q + i) % 5
+            if mode == 0:      # smooth random
+                row = rng.random(n, dtype=np.float32) / n
+            elif mode == 1:    # heavy ties (many equal block sums)
+                row = (rng.integers(0, 3, n) / 64.0).astype(np.float32)
+            elif mode == 2:    # all equal
+                row = np.full(n, 1.0 / n, dtype=np.float32)
+            elif mode == 3:    # zeros with a few spikes
+                row = np.zeros(n, dtype=np.float32)
+                row[rng.integers(0, n, size=min(n, 50))] = 1.0
+            else:              # spread over many octaves: the summation order shows in the sums
+                row = (rng.lognormal(0.0, 3.0, n) / n).astype(np.float32)
+            sc[b, i, :n] = row
+    return sc
+
+
+# block-level selection: the decisions are taken on float32 pairwise-tree block sums on both
+# sides, so indices and counts must match exactly.  Cases: rows below and above the cut,
+# partial last blocks, 2.5k and 9.4k candidate blocks (both LDS capacities), blocks of 4..256.
+@pytest.mark.parametrize("q_pos0,n_q,window,topk,block", [
+    (1100, 200, 128, 1024, 64),
+    (9000, 40, 128, 1024, 64),
+    (40000, 3, 128, 1024, 16),
+    (300000, 2, 128, 1024, 32),
+    (5000, 9, 128, 1024, 256),
+    (0, 70, 2, 8, 4),
+    (700, 33, 5, 24, 8),
+    (2000, 17, 128, 512, 128),
+])
+def test_select_blocks_parity(q_pos0, n_q, window, topk, block):
+    say("select blocks", q_pos0, n_q, window, topk, block)
+    rng = np.random.default_rng(q_pos0 + block)
+    ld = (q_pos0 + n_q + 3) // 4 * 4
+    B = 2
+    sc = _score_rows(rng, B, n_q, q_pos0, ld)
+    T = q_pos0 + n_q
+    idx, cnt = hs2.hs2_select_blocks_window(torch.from_numpy(sc).to(DEV), q_pos0=q_pos0, T=T, window=window,
+                                            topk=topk, block=block)
+    torch.cuda.synchronize()
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(B):
+        for i in range(n_q):
+            p = q_pos0 + i
+            ref, rc, _ = oracle.select_blocks_window(sc[b, i, : p + 1], p, window, topk, block)
+            assert int(cnt[b, i]) == rc, (b, i)
+            assert np.array_equal(idx[b, i, :rc], ref), (b, i)
+            assert (idx[b, i, rc:] == -1).all(), (b, i)
+
+
+def test_select_blocks_feeds_sparse_layer():
+    """The block selection of the GPU's own scores drives the sparse layer unchanged."""
+    say("select blocks -> sparse")
+    inp = inputs.attention_inputs(B=1, n_q=64, T=1600, H=16, d=256, kv="bf16", n_sparse=1, seed=12, device=DEV)
+    q_pos0 = 1536
+    _, _, scores = hs2.hs2_full_attn_scored(inp["q"], inp["k"], inp["v"], q_pos0=q_pos0, sm_scale=SCALE)
+    idx, cnt = hs2.hs2_select_blocks_window(scores, q_pos0=q_pos0, T=1600, block=64)
+    o, lse = hs2.hs2_sparse_attn_reuse(inp["q_sparse"][0], inp["k"], inp["v"], idx, cnt, sm_scale=SCALE)
+    torch.cuda.synchronize()
+    s_np, idx_np, cnt_np = scores.cpu().numpy()[0], idx.cpu().numpy()[0], cnt.cpu().numpy()[0]
+    k64, v64 = parity.kv_f64(inp, 0)
+    q64 = parity.decode(inp["q_sparse"][0][0])
+    o_ref = np.zeros_like(q64)
+    lse_ref = np.zeros(q64.shape[:2])
+    for i in range(64):
+        p = q_pos0 + i
+        ref, rc, _ = oracle.select_blocks_window(s_np[i, : p + 1], p, 128, 1024, 64)
+        assert int(cnt_np[i]) == rc and np.array_equal(idx_np[i, :rc], ref), i
+        o_ref[i], lse_ref[i] = oracle.sparse_attn_reuse(q64[i], k64, v64, ref, SCALE)
+    parity.check_out(o[0], o_ref, "bf16")
+    parity.check_lse(lse[0], lse_ref)
+
+
 def test_select_small_window_topk():
     say("select small")
     rng = np.random.default_rng(3)

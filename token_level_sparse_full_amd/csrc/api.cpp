@@ -154,6 +154,44 @@ int hs2_select_topk_window(const float* scores, int64_t ld_scores, int B, int n_
   return hip_status(hs2::launch_select(p, workspace, ws_bytes, (hipStream_t)stream), "hs2_select_topk_window");
 }
 
+static_assert(HS2_MAX_SELECT == hs2::kMaxSelect && HS2_MAX_BLOCKS == hs2::kMaxBlocks, "limits agree");
+
+static bool block_ok(int block) { return block >= 4 && block <= 256 && (block & (block - 1)) == 0; }
+
+size_t hs2_select_blocks_workspace_bytes(int B, int n_q, int64_t T, int64_t q_pos0, int window, int block) {
+  if (B < 1 || n_q < 1 || T < 1 || q_pos0 < 0 || window < 1 || !block_ok(block)) return 0;
+  return hs2::select_blocks_workspace_bytes(B, n_q, q_pos0, window, block);
+}
+
+int hs2_select_blocks_window(const float* scores, int64_t ld_scores, int B, int n_q, int64_t T, int64_t q_pos0,
+                             int window, int topk, int block, int32_t* idx, int32_t* count, void* workspace,
+                             size_t ws_bytes, void* stream) {
+  if (!scores || !idx || !count) return fail(HS2_ERR_NULL, "scores, idx and count are required");
+  if (B < 1 || n_q < 1 || T < 1) return fail(HS2_ERR_SHAPE, "B, n_q and T must be >= 1");
+  if ((int64_t)B * n_q > 0x7FFFFFFF || T > 0x7FFFFFFF) return fail(HS2_ERR_SHAPE, "B*n_q and T must fit in int32");
+  if (window < 1 || topk < 1 || window + topk > HS2_MAX_SELECT)
+    return fail(HS2_ERR_SHAPE, "need window >= 1, topk >= 1, window + topk <= %d", HS2_MAX_SELECT);
+  if (!block_ok(block)) return fail(HS2_ERR_UNSUPPORTED, "block must be a power of two in [4, 256]");
+  if (topk % block != 0) return fail(HS2_ERR_SHAPE, "topk must be a multiple of block");
+  if (q_pos0 < 0 || q_pos0 + n_q > T) return fail(HS2_ERR_SHAPE, "need 0 <= q_pos0 and q_pos0 + n_q <= T");
+  if (ld_scores < q_pos0 + n_q || ld_scores % 4 != 0)
+    return fail(HS2_ERR_SHAPE, "ld_scores must be >= q_pos0 + n_q and a multiple of 4");
+  if (hs2::select_blocks_nb_max(q_pos0, n_q, window, block) > HS2_MAX_BLOCKS)
+    return fail(HS2_ERR_UNSUPPORTED, "more than %d candidate blocks in a row", HS2_MAX_BLOCKS);
+  if (!aligned(scores, 16)) return fail(HS2_ERR_ALIGN, "scores must be 16-byte aligned");
+  if (!aligned(idx, 4) || !aligned(count, 4)) return fail(HS2_ERR_ALIGN, "idx and count must be 4-byte aligned");
+  const size_t need = hs2::select_blocks_workspace_bytes(B, n_q, q_pos0, window, block);
+  if (need > 0) {
+    if (!workspace) return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if (!aligned(workspace, 256)) return fail(HS2_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (ws_bytes < need) return fail(HS2_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  }
+  hs2::SelectParams p;
+  p.scores = scores; p.ld_scores = ld_scores; p.B = B; p.n_q = n_q; p.q_pos0 = q_pos0;
+  p.window = window; p.topk = topk; p.idx = idx; p.count = count;
+  return hip_status(hs2::launch_select_blocks(p, block, workspace, (hipStream_t)stream), "hs2_select_blocks_window");
+}
+
 size_t hs2_sparse_workspace_bytes(int B, int n_q, int H, int max_sel) {
   if (B < 1 || n_q < 1 || !heads_ok(H) || max_sel < 1 || max_sel > HS2_MAX_SELECT) return 0;
   return hs2::sparse_workspace_bytes(B, n_q, max_sel);

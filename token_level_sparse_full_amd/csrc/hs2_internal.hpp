@@ -43,6 +43,15 @@ struct SelectParams {
 size_t select_workspace_bytes(int B, int n_q, int64_t T, int64_t q_pos0);
 hipError_t launch_select(const SelectParams& p, void* ws, size_t ws_bytes, hipStream_t stream);
 
+// block-level selection: block in {4, 8, ..., 256}, topk a multiple of block,
+// at most kMaxBlocks candidate blocks per row; the workspace holds the block
+// sums [B * n_q, nb_max] float32
+constexpr int kMaxSelect = 4096;   // largest window + topk
+constexpr int kMaxBlocks = 16384;  // candidate blocks of one row held in LDS
+int64_t select_blocks_nb_max(int64_t q_pos0, int n_q, int window, int block);
+size_t select_blocks_workspace_bytes(int B, int n_q, int64_t q_pos0, int window, int block);
+hipError_t launch_select_blocks(const SelectParams& p, int block, void* ws, hipStream_t stream);
+
 struct AttnParams {
   const void* q;
   const void* k;

@@ -766,6 +766,128 @@ size_t mb_layout(int rows, int64_t max_cand, char* base, MbWs* ws) {
   return hist_bytes + cnt_bytes;
 }
 
+// ---- block-level selection (the granularity token-level selection replaces) ----
+// HySparse2 pages: agihunt.info summary, ablation paragraph (token-level against
+// block-level selection at the same 1024-token budget, blocks of 64); 10100.com
+// article, section on the first refinement.  For the query at position p the
+// candidates C = [0, p-window] are cut into aligned blocks of `block` tokens
+// (the last one may be partial); a block scores the sum of its candidates'
+// scores as a float32 pairwise tree (adjacent pairs first); the topk / block
+// best blocks are kept, ties to the lower block, and the window is added.
+//
+// Two kernels.  block_sum_kernel streams the score rows once: each lane sums
+// its float4 ((x0 + x1) + (x2 + x3)) and the block / 4 lanes of a block
+// combine by xor-shuffles 1, 2, 4, ..., which is exactly the pairwise tree.
+// block_select_kernel (one workgroup per row) loads the row's block sums into
+// LDS, finds the topk / block-th largest with the LDS radix select above and
+// writes the token indices in ascending order.
+constexpr int BK_THREADS = 256;
+constexpr int BK_UNROLL = 8;
+constexpr int BK_FLOATS = BK_THREADS * BK_UNROLL * 4;  // scores per block-sum workgroup
+
+__device__ __forceinline__ int64_t bk_cand(const SelectParams& p, int64_t row) {
+  return p.q_pos0 + row % p.n_q + 1 - p.window;  // |C| (may be <= 0)
+}
+
+template <int LPB>  // lanes per block = block / 4
+__global__ __launch_bounds__(BK_THREADS) void block_sum_kernel(const SelectParams p, int64_t row0, int nchunk,
+                                                               int nb_max, float* __restrict__ bsum) {
+  constexpr int block = 4 * LPB;
+  const int64_t row = row0 + blockIdx.x / nchunk;
+  const int chunk = blockIdx.x % nchunk;
+  const int64_t n_cand = bk_cand(p, row);
+  if (n_cand <= p.topk) return;  // every key is selected: no sums needed
+  const int64_t nb = (n_cand + block - 1) / block;
+  const int64_t f0 = (int64_t)chunk * BK_FLOATS;
+  if (f0 >= n_cand) return;
+  const float* src = p.scores + row * p.ld_scores;
+  const int tid = threadIdx.x;
+  f32x4 x[BK_UNROLL];
+  // f < n_cand <= ld_scores with f and ld_scores multiples of 4: the float4 is inside the row
+#pragma unroll
+  for (int it = 0; it < BK_UNROLL; ++it) {
+    const int64_t f = f0 + 4 * (it * BK_THREADS + tid);
+    x[it] = f < n_cand ? *(const f32x4*)(src + f) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int it = 0; it < BK_UNROLL; ++it) {
+    const int64_t f = f0 + 4 * (it * BK_THREADS + tid);
+    f32x4 v = x[it];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = f + e < n_cand ? v[e] : 0.f;  // scores past C (the window) count 0
+    float t = (v[0] + v[1]) + (v[2] + v[3]);
+#pragma unroll
+    for (int m = 1; m < LPB; m <<= 1) t += shfl_xor(t, m);
+    const int64_t b = f / block;
+    if ((tid % LPB) == 0 && b < nb) bsum[(row - row0) * nb_max + b] = t;
+  }
+}
+
+constexpr int BK_MAX_IDS = kMaxSelect / 4;  // selected blocks: topk / block with block >= 4
+
+template <int CAP>
+__global__ __launch_bounds__(SEL_THREADS) void block_select_kernel(const SelectParams p, int64_t row0, int block,
+                                                                   int nb_max, const float* __restrict__ bsum) {
+  __shared__ SelShared sh;
+  __shared__ uint32_t bv[CAP];
+  __shared__ int sel_ids[BK_MAX_IDS];
+  const int64_t row = row0 + blockIdx.x;
+  const int tid = threadIdx.x;
+  const int max_sel = p.window + p.topk;
+  const int64_t n = p.q_pos0 + row % p.n_q + 1;
+  const int64_t n_cand = n - p.window;
+  int32_t* out = p.idx + row * max_sel;
+  if (n_cand <= p.topk) {
+    for (int j = tid; j < max_sel; j += SEL_THREADS) out[j] = j < n ? j : -1;
+    if (tid == 0) p.count[row] = (int32_t)n;
+    return;
+  }
+  const int nb = (int)((n_cand + block - 1) / block);
+  const int nsel = p.topk / block;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  const float* src = bsum + (row - row0) * nb_max;
+  for (int b = tid; b < nb; b += SEL_THREADS) {
+    const uint32_t u = fbits(src[b]);
+    bv[b] = u;
+    lo = min(lo, u);
+    hi = max(hi, u);
+  }
+  block_min_max(lo, hi, sh);  // ends with a barrier: bv is complete
+  int par = 0;
+  uint32_t tau;
+  int need_eq;
+  lds_radix_select(bv, nb, nsel, lo, hi, 4, sh, par, tau, need_eq);
+  // thread t owns the blocks [t*per, (t+1)*per): two ordered scans give the
+  // equal-to-tau rank and then the output rank of each selected block
+  const int per = (nb + SEL_THREADS - 1) / SEL_THREADS;
+  const int b0 = min(nb, tid * per), b1 = min(nb, b0 + per);
+  int my_eq = 0;
+  for (int b = b0; b < b1; ++b) my_eq += bv[b] == tau;
+  int total;
+  int eq_before = block_excl_scan(my_eq, tid, sh, total);
+  int my_sel = 0;
+  for (int b = b0, e = eq_before; b < b1; ++b) {
+    const uint32_t u = bv[b];
+    if (u > tau || (u == tau && e++ < need_eq)) ++my_sel;
+  }
+  int rank = block_excl_scan(my_sel, tid, sh, total);
+  for (int b = b0, e = eq_before; b < b1; ++b) {
+    const uint32_t u = bv[b];
+    if (u > tau || (u == tau && e++ < need_eq)) sel_ids[rank++] = b;
+  }
+  __syncthreads();
+  const int64_t last = sel_ids[nsel - 1];
+  const int nbt = (nsel - 1) * block + (int)min((int64_t)block, n_cand - last * block);
+  for (int j = tid; j < max_sel; j += SEL_THREADS) {
+    int32_t v;
+    if (j < nbt) v = (int32_t)((int64_t)sel_ids[j / block] * block + j % block);
+    else if (j < nbt + p.window) v = (int32_t)(n_cand + (j - nbt));
+    else v = -1;
+    out[j] = v;
+  }
+  if (tid == 0) p.count[row] = nbt + p.window;
+}
+
 }  // namespace
 
 // Sized for the smallest window (1), which has the most candidates: the launch
@@ -793,6 +915,49 @@ hipError_t launch_select(const SelectParams& p, void* ws_ptr, size_t /*ws_bytes*
   hipLaunchKernelGGL(mb_hist_kernel<2>, grid, dim3(MB_THREADS), 0, stream, p, ws);
   hipLaunchKernelGGL(mb_count_kernel, grid, dim3(MB_THREADS), 0, stream, p, ws);
   hipLaunchKernelGGL(mb_write_kernel, grid, dim3(MB_THREADS), 0, stream, p, ws);
+  return hipGetLastError();
+}
+
+int64_t select_blocks_nb_max(int64_t q_pos0, int n_q, int window, int block) {
+  const int64_t c = q_pos0 + n_q - window;  // candidates of the last row
+  return c > 0 ? (c + block - 1) / block : 0;
+}
+
+size_t select_blocks_workspace_bytes(int B, int n_q, int64_t q_pos0, int window, int block) {
+  return (((size_t)B * n_q * (size_t)select_blocks_nb_max(q_pos0, n_q, window, block) * 4) + 255) & ~(size_t)255;
+}
+
+hipError_t launch_select_blocks(const SelectParams& p, int block, void* ws_ptr, hipStream_t stream) {
+  const int64_t rows = (int64_t)p.B * p.n_q;
+  if (rows == 0) return hipSuccess;
+  const int nb_max = (int)select_blocks_nb_max(p.q_pos0, p.n_q, p.window, block);
+  const int nchunk = nb_max > 0 ? (int)(((int64_t)nb_max * block + BK_FLOATS - 1) / BK_FLOATS) : 0;
+  float* bsum = (float*)ws_ptr;
+  // rows per launch: keep every grid under 2^31 work-items
+  const int64_t step = (int64_t)(1u << 31) / ((int64_t)BK_THREADS * (nchunk > 0 ? nchunk : 1) + SEL_THREADS);
+  for (int64_t r0 = 0; r0 < rows; r0 += step) {
+    const int64_t nr = rows - r0 < step ? rows - r0 : step;
+    if (nchunk > 0) {
+      const dim3 g((unsigned)(nr * nchunk));
+      float* bs = bsum + r0 * nb_max;
+      switch (block) {
+        case 4: hipLaunchKernelGGL(block_sum_kernel<1>, g, dim3(BK_THREADS), 0, stream, p, r0, nchunk, nb_max, bs); break;
+        case 8: hipLaunchKernelGGL(block_sum_kernel<2>, g, dim3(BK_THREADS), 0, stream, p, r0, nchunk, nb_max, bs); break;
+        case 16: hipLaunchKernelGGL(block_sum_kernel<4>, g, dim3(BK_THREADS), 0, stream, p, r0, nchunk, nb_max, bs); break;
+        case 32: hipLaunchKernelGGL(block_sum_kernel<8>, g, dim3(BK_THREADS), 0, stream, p, r0, nchunk, nb_max, bs); break;
+        case 64: hipLaunchKernelGGL(block_sum_kernel<16>, g, dim3(BK_THREADS), 0, stream, p, r0, nchunk, nb_max, bs); break;
+        case 128: hipLaunchKernelGGL(block_sum_kernel<32>, g, dim3(BK_THREADS), 0, stream, p, r0, nchunk, nb_max, bs); break;
+        default: hipLaunchKernelGGL(block_sum_kernel<64>, g, dim3(BK_THREADS), 0, stream, p, r0, nchunk, nb_max, bs); break;
+      }
+    }
+    const float* bs = bsum + r0 * nb_max;
+    if (nb_max <= 4096)
+      hipLaunchKernelGGL(block_select_kernel<4096>, dim3((unsigned)nr), dim3(SEL_THREADS), 0, stream, p, r0, block,
+                         nb_max, bs);
+    else
+      hipLaunchKernelGGL(block_select_kernel<kMaxBlocks>, dim3((unsigned)nr), dim3(SEL_THREADS), 0, stream, p,
+                         r0, block, nb_max, bs);
+  }
   return hipGetLastError();
 }
 

@@ -30,6 +30,8 @@ _PROTOS = {
     "hs2_full_attn_workspace_bytes": (_sz, [_i, _i, _i, _i64, _i]),
     "hs2_select_topk_window": (_i, [_vp, _i64, _i, _i, _i64, _i64, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "hs2_select_workspace_bytes": (_sz, [_i, _i, _i64, _i64]),
+    "hs2_select_blocks_window": (_i, [_vp, _i64, _i, _i, _i64, _i64, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "hs2_select_blocks_workspace_bytes": (_sz, [_i, _i, _i64, _i64, _i, _i]),
     "hs2_sparse_attn_reuse": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp, _i64, _vp, _vp, _i, _f, _vp, _vp,
                                    _vp, _sz, _vp]),
     "hs2_sparse_workspace_bytes": (_sz, [_i, _i, _i, _i]),
@@ -145,6 +147,29 @@ def hs2_select_topk_window(scores, *, q_pos0: int, T: int, n_q: int | None = Non
                                       _ptr(ws), need, _stream(stream))
     check("hs2_select_topk_window", rc)
     return idx, count
+
+
+def hs2_select_blocks_window(scores, *, q_pos0: int, T: int, n_q: int | None = None, window: int = 128,
+                             topk: int = 1024, block: int = 64, idx=None, count=None, ws=None, stream=None):
+    """Block-level top-k with forced window.  scores [B,n_q,ld]; returns (idx, count) in the
+    token-level call's format."""
+    B, nq_s, ld = scores.shape
+    n_q = nq_s if n_q is None else n_q
+    if idx is None:
+        idx = torch.empty((B, n_q, window + topk), dtype=torch.int32, device=scores.device)
+    if count is None:
+        count = torch.empty((B, n_q), dtype=torch.int32, device=scores.device)
+    need = int(lib().hs2_select_blocks_workspace_bytes(B, n_q, T, q_pos0, window, block))
+    if ws is None:
+        ws = workspace(need, scores.device)
+    rc = lib().hs2_select_blocks_window(_ptr(scores), ld, B, n_q, T, q_pos0, window, topk, block, _ptr(idx),
+                                        _ptr(count), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    check("hs2_select_blocks_window", rc)
+    return idx, count
+
+
+def select_blocks_workspace_bytes(B: int, n_q: int, T: int, q_pos0: int, window: int = 128, block: int = 64) -> int:
+    return int(lib().hs2_select_blocks_workspace_bytes(B, n_q, T, q_pos0, window, block))
 
 
 def hs2_sparse_attn_reuse(q, k, v, idx, count, *, sm_scale: float | None = None, k_scale=None, v_scale=None,
