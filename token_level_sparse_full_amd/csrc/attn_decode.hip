@@ -454,21 +454,29 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const AttnParams p, c
   const int g = blockIdx.x, row = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
   const int c0 = g * kMergeFan, c1 = min(io.nin, c0 + kMergeFan);
   const int64_t ib = (int64_t)b * io.in_stride;
-  float mc[kMergeFan];
+  // every load is issued up front (indices past the last state repeat it and
+  // are masked), so the fan-in costs one memory latency, not one per state
+  float mc[kMergeFan], zc[kMergeFan], oc[kMergeFan];
   float M = kNegInf;
 #pragma unroll
   for (int i = 0; i < kMergeFan; ++i) {
-    mc[i] = (c0 + i < c1) ? io.in_m[(ib + c0 + i) * 16 + row] : kNegInf;
+    const int64_t c = ib + min(c0 + i, c1 - 1);
+    mc[i] = io.in_m[c * 16 + row];
+    zc[i] = io.in_z[c * 16 + row];
+    oc[i] = io.in_o[(c * 16 + row) * kHeadDim + d];
+  }
+#pragma unroll
+  for (int i = 0; i < kMergeFan; ++i) {
+    if (c0 + i >= c1) mc[i] = kNegInf;
     M = fmaxf(M, mc[i]);
   }
   float Z = 0.f, acc = 0.f;
 #pragma unroll
   for (int i = 0; i < kMergeFan; ++i) {
-    if (mc[i] != kNegInf) {
-      const float f = fast_exp2(mc[i] - M);
-      Z += io.in_z[(ib + c0 + i) * 16 + row] * f;
-      acc += io.in_o[((ib + c0 + i) * 16 + row) * kHeadDim + d] * f;
-    }
+    const bool ok = mc[i] != kNegInf;   // a selected 0 adds exactly; masked terms may hold any bits
+    const float f = fast_exp2(mc[i] - M);
+    Z += ok ? zc[i] * f : 0.f;
+    acc += ok ? oc[i] * f : 0.f;
   }
   if constexpr (FINAL) {
     const int R = gridDim.y;

@@ -261,13 +261,17 @@ __global__ __launch_bounds__(256) void sparse_merge_kernel(const SparseParams p,
   float M = kNegInf;
   for (int i = 0; i < ws.nsplit; ++i) M = fmaxf(M, ws.m[b0 + i * 16]);
   float Z = 0.f, acc = 0.f;
+  // no branch around the loads, so that several pieces are in flight at once;
+  // a piece without keys is masked by a select (its z and o may hold any bits)
+#pragma unroll 8
   for (int i = 0; i < ws.nsplit; ++i) {
     const float mi = ws.m[b0 + i * 16];
-    if (mi != kNegInf) {
-      const float f = fast_exp2(mi - M);
-      Z += ws.z[b0 + i * 16] * f;
-      acc += ws.o[(b0 + i * 16) * kHeadDim + d] * f;
-    }
+    const float zi = ws.z[b0 + i * 16];
+    const float oi = ws.o[(b0 + i * 16) * kHeadDim + d];
+    const bool ok = mi != kNegInf;
+    const float f = fast_exp2(mi - M);
+    Z += ok ? zi * f : 0.f;
+    acc += ok ? oi * f : 0.f;
   }
   const float out = Z > 0.f ? acc / Z : 0.f;
   const int64_t oi = ((int64_t)qid * gridDim.y + h) * kHeadDim + d;
