@@ -219,3 +219,66 @@ def test_decode_1m_fp8():
         for i, (o2, _) in enumerate(sp):
             o2_ref, _ = oracle.sparse_attn_reuse(parity.decode(qs[i][0, 0]), k64, v64, idx_np[0, : cnt_np[0]], 1 / 16)
             parity.check_out(o2[0, 0], o2_ref, "e4m3", f"step {step} sparse {i}")
+
+
+def test_bridge_64k_fp8_every_position():
+    """The bridge into the e4m3 cache at full size, then one bridged layer's
+    cross-decoder at every prompt position (the many-query e4m3 path in the
+    32768-query chunks bench.py times): sampled projection rows and sampled
+    query rows of the last chunk against the oracle, the selection and a
+    sparse layer of those rows on the GPU's own indices."""
+    wl = inputs.WORKLOADS["bridge_64k"]
+    say(wl.name, "fp8, every position")
+    L, D, nl, H, C = wl.L, wl.D, wl.n_full, wl.H, 32768
+    br = inputs.bridge_inputs(L=L, D=D, n_layers=nl, d=256, seed=wl.seed, device=DEV)
+    k8, v8, ks, vs = hs2.hs2_bridge_kv_proj_fp8(br["x"], br["w_k"], br["w_v"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(44)
+    rows = np.sort(np.concatenate([[0, L - 1], rng.choice(np.arange(1, L - 1), size=126, replace=False)]))
+    x64 = parity.decode(br["x"][torch.from_numpy(rows).to(DEV)])
+    wk64, wv64 = parity.decode(br["w_k"]), parity.decode(br["w_v"])
+    kc_r, vc_r, ks_r, vs_r = oracle.bridge_kv_proj_fp8(x64, wk64, wv64)
+    k_ref, v_ref = oracle.bridge_kv_proj(x64, wk64, wv64)
+    k_abs, v_abs = oracle.bridge_kv_proj(np.abs(x64), np.abs(wk64), np.abs(wv64))
+    table = oracle.e4m3_decode_table()
+    sel_rows = torch.from_numpy(rows).to(DEV)
+    for codes, sc, ref, mag, codes_r, sc_r in ((k8, ks, k_ref, k_abs, kc_r, ks_r), (v8, vs, v_ref, v_abs, vc_r, vs_r)):
+        c = codes[:, sel_rows].cpu().numpy()
+        s_ = sc[:, sel_rows].cpu().numpy().astype(np.float64)
+        slack = 64 * 2.0 ** -24 * mag
+        assert (np.abs(s_ - sc_r) <= slack.max(axis=-1) / 448.0 + 2.0 ** -23 * sc_r).all()
+        got = table[c] * s_[..., None]
+        step = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref) / s_[..., None], 2.0 ** -6))) - 3),
+                          2.0 ** -9) * s_[..., None]
+        assert (np.abs(got - ref) <= 1.5 * step + 2 * slack).all()
+        assert (c == codes_r).mean() > 0.999
+    # layer 0 on its e4m3 cache: the last query chunk, as bench.py launches it
+    m, c0 = 0, L - C
+    q = inputs.cast(inputs.normal((1, L, H, 256), inputs.STD_QKV, wl.seed, inputs.S_QFULL_LAYER + m, DEV), "bf16")
+    q2 = inputs.cast(inputs.normal((1, L, H, 256), inputs.STD_QKV, wl.seed, inputs.S_QSPARSE + 8 * m, DEV), "bf16")
+    k, v, ksm, vsm = k8[m:m + 1], v8[m:m + 1], ks[m:m + 1], vs[m:m + 1]
+    o, lse, scores = hs2.hs2_full_attn_scored(q[:, c0:], k, v, q_pos0=c0, sm_scale=1 / 16, k_scale=ksm, v_scale=vsm,
+                                              ld_scores=L)
+    idx, cnt = hs2.hs2_select_topk_window(scores, q_pos0=c0, T=L)
+    o2, _ = hs2.hs2_sparse_attn_reuse(q2[:, c0:], k, v, idx, cnt, sm_scale=1 / 16, k_scale=ksm, v_scale=vsm)
+    torch.cuda.synchronize()
+    k64 = oracle.decode_rows(inputs.raw_numpy(k[0]), "e4m3", inputs.raw_numpy(ksm[0]))
+    v64 = oracle.decode_rows(inputs.raw_numpy(v[0]), "e4m3", inputs.raw_numpy(vsm[0]))
+    qi = np.sort(np.concatenate([[0, C - 1], rng.choice(np.arange(1, C - 1), size=4, replace=False)]))
+    qsel = torch.from_numpy(qi).to(DEV)
+    q64 = parity.decode(q[0, c0:][qsel])
+    q264 = parity.decode(q2[0, c0:][qsel])
+    s_rows = scores[0, qsel].cpu().numpy()
+    idx_np, cnt_np = idx[0, qsel].cpu().numpy(), cnt[0, qsel].cpu().numpy()
+    s_refs = []
+    for r, i in enumerate(qi):
+        p = c0 + int(i)
+        say("query row", p)
+        o_ref, lse_ref, s_ref = oracle.full_attn_scored(q64[r:r + 1], k64, v64, p, 1 / 16)
+        parity.check_out(o[0, int(i):int(i) + 1], o_ref, "e4m3", f"o row {p}")
+        parity.check_lse(lse[0, int(i):int(i) + 1], lse_ref)
+        parity.check_scores(s_rows[r, : p + 1], s_ref[0], f"scores row {p}")
+        s_refs.append(s_ref[0])
+        o2_ref, _ = oracle.sparse_attn_reuse(q264[r], k64, v64, idx_np[r, : cnt_np[r]], 1 / 16)
+        parity.check_out(o2[0, int(i)], o2_ref, "e4m3", f"sparse row {p}")
+    _check_select_rows(idx_np, cnt_np, s_rows, s_refs, [c0 + int(i) for i in qi])
