@@ -112,6 +112,9 @@ def test_prefill_128k_sampled():
     rows = sorted({0, 1, 127, 128, 129, 1151, 1152, 1153, 4097, 32767, 32768, L // 2, L - 1} |
                   {i for _, i in needles[:12]})
     kept = {}
+    # the block-level selection (ablation) of the same chunks, as bench.py launches it
+    idx_b, cnt_b = torch.empty_like(idx), torch.empty_like(cnt)
+    ws_b = hs2.workspace(hs2.select_blocks_workspace_bytes(1, C, L, L - C, WIN, 64), DEV)
     for c0 in range(0, L, C):
         hs2.hs2_full_attn_scored(inp["q"][:, c0:c0 + C], inp["k"], inp["v"], q_pos0=c0, sm_scale=1 / 16,
                                  o=o[:, c0:c0 + C], lse=lse[:, c0:c0 + C], scores=scores, ld_scores=L)
@@ -119,6 +122,8 @@ def test_prefill_128k_sampled():
             if c0 <= p < c0 + C:
                 kept[p] = scores[0, p - c0, : p + 1].cpu().numpy()
         hs2.hs2_select_topk_window(scores, q_pos0=c0, T=L, n_q=C, idx=idx[:, c0:c0 + C], count=cnt[:, c0:c0 + C])
+        hs2.hs2_select_blocks_window(scores, q_pos0=c0, T=L, n_q=C, block=64, idx=idx_b[:, c0:c0 + C],
+                                     count=cnt_b[:, c0:c0 + C], ws=ws_b)
     sp = _sparse_layers(inp["q_sparse"], inp["k"], inp["v"], idx, cnt, "bf16")
     torch.cuda.synchronize()
     # invariants on every row: count, window inside, strictly ascending, in range
@@ -131,6 +136,12 @@ def test_prefill_128k_sampled():
     assert (d > 0).all()
     # every needle is picked by its target query
     idx_np, cnt_np = idx[0].cpu().numpy(), cnt[0].cpu().numpy()
+    # block-level selection of the sampled rows: bit-exact against the oracle on the GPU's scores
+    idxb_np, cntb_np = idx_b[0].cpu().numpy(), cnt_b[0].cpu().numpy()
+    for p in rows:
+        ref, rc, _ = oracle.select_blocks_window(kept[p], p, WIN, TOPK, 64)
+        assert int(cntb_np[p]) == rc and np.array_equal(idxb_np[p, :rc], ref), p
+        assert (idxb_np[p, rc:] == -1).all(), p
     for j, i in needles:
         assert j in idx_np[i, : cnt_np[i]], (j, i)
     # sampled rows against the oracle
