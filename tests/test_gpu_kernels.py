@@ -372,3 +372,39 @@ def test_bridge_fp8_normal_and_strided_output():
         assert (c == codes_r).mean() > 0.999
         assert (codes[:, L:] == 0).all() and (sc[:, L:] == 0).all()
 
+
+
+# --------------------------------------------------------------------------- maximum selection size
+@pytest.mark.parametrize("n_q", [24, 40])   # B * n_q = 48: split sparse form; 80: one workgroup per query
+def test_max_selection_size(n_q):
+    """window + topk = HS2_MAX_SELECT (4096): the token selection (whose single-read estimate
+    cannot keep that many candidates, so the exact path runs), the block selection with 992
+    blocks of 4, and the sparse layer over 4096-entry index sets."""
+    window, topk, q_pos0 = 128, 3968, 6000
+    T = q_pos0 + n_q
+    say("max selection", n_q)
+    rng = np.random.default_rng(n_q)
+    ld = (T + 3) // 4 * 4
+    sc = _score_rows(rng, 2, n_q, q_pos0, ld)
+    _select_case(sc, q_pos0, T, window, topk)
+    s = torch.from_numpy(sc).to(DEV)
+    idx_b, cnt_b = hs2.hs2_select_blocks_window(s, q_pos0=q_pos0, T=T, window=window, topk=topk, block=4)
+    idx, cnt = hs2.hs2_select_topk_window(s, q_pos0=q_pos0, T=T, window=window, topk=topk)
+    inp = inputs.attention_inputs(B=2, n_q=n_q, T=T, H=16, d=256, kv="bf16", n_sparse=1, seed=n_q, device=DEV)
+    o, lse = hs2.hs2_sparse_attn_reuse(inp["q_sparse"][0], inp["k"], inp["v"], idx, cnt, sm_scale=SCALE)
+    torch.cuda.synchronize()
+    idxb_np, cntb_np = idx_b.cpu().numpy(), cnt_b.cpu().numpy()
+    idx_np, cnt_np = idx.cpu().numpy(), cnt.cpu().numpy()
+    o_ref = np.zeros(tuple(inp["q_sparse"][0].shape))
+    lse_ref = np.zeros(o_ref.shape[:3])
+    for b in range(2):
+        k64, v64 = parity.kv_f64(inp, b)
+        q64 = parity.decode(inp["q_sparse"][0][b])
+        for i in range(n_q):
+            p = q_pos0 + i
+            ref, rc, _ = oracle.select_blocks_window(sc[b, i, : p + 1], p, window, topk, 4)
+            assert int(cntb_np[b, i]) == rc and np.array_equal(idxb_np[b, i, :rc], ref), (b, i)
+            assert int(cnt_np[b, i]) == window + topk
+            o_ref[b, i], lse_ref[b, i] = oracle.sparse_attn_reuse(q64[i], k64, v64, idx_np[b, i, : cnt_np[b, i]], SCALE)
+    parity.check_out(o, o_ref, "bf16")
+    parity.check_lse(lse, lse_ref)
