@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--collect-traffic", action="store_true",
                     help="run rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE over --pmc-probe and record the "
                          "per-launch HBM traffic of the full-attention kernel under profiles/")
+    ap.add_argument("--out-dir", default="profile_runs",
+                    help="directory (relative to the repository root) for the raw counter output of "
+                         "--collect-traffic and a copy of the record")
     return ap.parse_args()
 
 
@@ -108,7 +111,7 @@ def collect_traffic(args):
     import glob
     import subprocess
 
-    out_root = os.path.join(ROOT, "gpurun_out", "traffic")
+    out_root = os.path.join(ROOT, args.out_dir, "traffic")
     res = {}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
         d = os.path.join(out_root, ctr.lower())
@@ -196,8 +199,8 @@ def collect_traffic(args):
         f.write(f"mfma_busy_frac_at_2p4ghz = {mfma_util:.4f}\n")
         f.write(f"kernel_source_sha256_16 = {kernel_source_hash()}\n")
     text = open(TRAFFIC_FILE).read()
-    os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
-    with open(os.path.join(ROOT, "gpurun_out", os.path.basename(TRAFFIC_FILE)), "w") as f:
+    os.makedirs(os.path.join(ROOT, args.out_dir), exist_ok=True)
+    with open(os.path.join(ROOT, args.out_dir, os.path.basename(TRAFFIC_FILE)), "w") as f:
         f.write(text)
     print(text, flush=True)
 
