@@ -213,7 +213,7 @@ def inputs_L(args) -> int:
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        print(json.dumps({"error": "bench.py measures a single GPU; multi-GPU runs are not supported: use --gpus 1"}))
         sys.exit(2)
     if args.collect_traffic:      # orchestration only: this process never touches the GPU
         collect_traffic(args)

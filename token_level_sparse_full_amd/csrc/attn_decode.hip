@@ -263,7 +263,7 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_stream_kernel(const Attn
   // Keys past the wave's range load its last row instead (no branches around
   // the loads, so the compiler can count them): their logits are masked and
   // their probabilities are zero.  The K/V stream is read once: nontemporal
-  // loads (measured on the box: 6.2-6.9 TB/s for a plain stream against
+  // loads (measured on an MI355X: 6.2-6.9 TB/s for a plain stream against
   // 4.4 TB/s with ordinary loads).
   // V: each load instruction reads whole rows (bf16: two rows of 512 B, e4m3:
   // four rows of 256 B), so that every cache line is requested once
