@@ -236,24 +236,20 @@ def select_topk_window(scores: np.ndarray, p: int, window: int = 128, topk: int 
     return sel, len(sel), tau
 
 
-def block_score(vals: np.ndarray, dtype=np.float32):
-    """Sum of the scores of one block, as a pairwise tree in ``dtype``.
+def block_score(vals: np.ndarray) -> float:
+    """Sum of the scores of one block.
 
-    The block length must be a power of two.  Adjacent pairs are added first,
-    then adjacent pairs of those sums, and so on; every addition is rounded to
-    ``dtype`` (round to nearest even).  The pages fix no precision for this
-    sum; the decision it feeds is taken in float32 on both sides, in this
-    order (positions past the candidates count as 0, which adds exactly).
+    The pages give a block's score only as the sum of its tokens' scores, so
+    the oracle takes the exact sum: math.fsum adds the values without
+    intermediate rounding and rounds the exact result once to float64.  Two
+    blocks whose exact sums differ by less than one float64 rounding (2**-53
+    relative) could compare equal here; that is far inside the band within
+    which a swap at the cut is accepted, so no judged decision depends on it.
     """
-    t = np.asarray(vals, dtype=dtype)
-    assert t.size >= 1 and t.size & (t.size - 1) == 0, "block length must be a power of two"
-    while t.size > 1:
-        t = (t[0::2] + t[1::2]).astype(dtype)
-    return t[0]
+    return math.fsum(np.asarray(vals, dtype=np.float64).tolist())
 
 
-def select_blocks_window(scores: np.ndarray, p: int, window: int = 128, topk: int = 1024, block: int = 64,
-                         dtype=np.float32):
+def select_blocks_window(scores: np.ndarray, p: int, window: int = 128, topk: int = 1024, block: int = 64):
     """Block-level selection with the forced window (the HySparse granularity,
     kept as an ablation of the token-level selection).
 
@@ -267,27 +263,23 @@ def select_blocks_window(scores: np.ndarray, p: int, window: int = 128, topk: in
     and the candidates C = [0, p-window] are those of the token-level
     selection.  C is cut into aligned blocks B_b = [b*block, (b+1)*block - 1]
     intersected with C (only the last one can be partial).  A block scores the
-    sum of its candidates' scores (``block_score``).  The topk // block blocks
-    of highest score are selected, ties to the lower block index, and S = W
-    together with the candidates of the selected blocks.  When |C| <= topk
-    every key 0..p is selected.  With block = 1 this is select_topk_window.
+    exact sum of its candidates' scores (``block_score``).  The topk // block
+    blocks of highest score are selected, ties to the lower block index, and
+    S = W together with the candidates of the selected blocks.  When |C| <=
+    topk every key 0..p is selected.  With block = 1 this is
+    select_topk_window.
 
     Returns (idx, count, tau) like select_topk_window; tau is the score of the
     last block admitted (None when no cut was needed).
     """
     assert topk % block == 0
     n = p + 1
-    s = np.asarray(scores, dtype=dtype)[:n]
+    s = np.asarray(scores, dtype=np.float64)[:n]
     n_cand = max(0, n - window)
     if n_cand <= topk:
         return np.arange(n, dtype=np.int64), n, None
     nb = (n_cand + block - 1) // block
-    sig = []
-    for b in range(nb):
-        vals = np.zeros(block, dtype=dtype)
-        hi = min(n_cand, (b + 1) * block)
-        vals[: hi - b * block] = s[b * block: hi]
-        sig.append(float(block_score(vals, dtype)))
+    sig = [block_score(s[b * block: min(n_cand, (b + 1) * block)]) for b in range(nb)]
     order = sorted(range(nb), key=lambda b: (-sig[b], b))
     nsel = topk // block
     top = order[:nsel]
@@ -382,27 +374,28 @@ def f64_to_e4m3_codes(y: np.ndarray) -> np.ndarray:
 def bridge_kv_proj_fp8(x: np.ndarray, w_k: np.ndarray, w_v: np.ndarray):
     """The bridged K and V of every layer as e4m3 cache rows.
 
-    Each output row a (the float32 value of the exact projection x @ w[m])
-    with amax = max|a| gets scale = fl32(amax / 448) (1 for an all-zero row)
-    and, with r = fl32(448 / amax), the codes e4m3(clamp(fl32(a * r), -448,
-    448)); fl32 rounds to the nearest float32 (a quotient or product of two
-    float32 values rounded once from float64 is the correctly rounded float32
-    result).  Returns (k_codes, v_codes) uint8 [n_layers, L, d] and
-    (k_scale, v_scale) float32 [n_layers, L].
+    The pages only say the cache is counted in FP8.  Reading taken here: each
+    output row a (the float32 value of the exact projection x @ w[m]) with
+    amax = max|a| is stored as one float32 scale, scale = fl32(amax / 448) (1
+    for an all-zero row), and the codes of the float32 quotients a / scale,
+    e4m3(clamp(fl32(a / scale), -448, 448)) -- the row divided by its stored
+    scale, as the scale is defined to be the factor that decodes it.  fl32
+    rounds to the nearest float32: a quotient of two float32 values computed
+    in float64 and rounded once to float32 is the correctly rounded float32
+    quotient (float64 carries more than twice float32's 24 bits, plus two).
+    Returns (k_codes, v_codes) uint8 [n_layers, L, d] and (k_scale, v_scale)
+    float32 [n_layers, L].
     """
     k, v = bridge_kv_proj(x, w_k, w_v)
 
     def quantize(t):
         a = t.astype(np.float32).astype(np.float64)
         amax = np.abs(a).max(axis=-1)
-        nz = amax > 0
-        scale = np.where(nz, (amax / 448.0).astype(np.float32), np.float32(1.0)).astype(np.float64)
-        r = np.where(nz, (448.0 / np.where(nz, amax, 1.0)).astype(np.float32), np.float32(0.0)).astype(np.float64)
-        y = (a * r[..., None]).astype(np.float32).astype(np.float64)
+        scale = np.where(amax > 0, (amax / 448.0).astype(np.float32), np.float32(1.0)).astype(np.float64)
+        y = (a / scale[..., None]).astype(np.float32).astype(np.float64)
         y = np.clip(y, -448.0, 448.0)
         return f64_to_e4m3_codes(y), scale.astype(np.float32)
 
     kc, ks = quantize(k)
     vc, vs = quantize(v)
     return kc, vc, ks, vs
-

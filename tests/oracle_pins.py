@@ -335,20 +335,36 @@ def pin_select_blocks_brute_force(orc):
         assert count == len(ref)
 
 
-def pin_block_score_pairwise_order(orc):
-    """The float32 tree adds adjacent pairs first: 2^24 + 4 is reached exactly,
-    where a left-to-right sum would lose every 1 to rounding (2^24 + 1 rounds
-    to 2^24).  Exact sums are returned unchanged."""
-    v = np.array([2.0 ** 24, 0, 0, 0, 1, 1, 1, 1], dtype=np.float32)
-    assert float(orc.block_score(v)) == 2.0 ** 24 + 4
-    assert float(orc.block_score(v[::-1].copy())) == 2.0 ** 24 + 4
-    w = np.array([1, 2.0 ** 24, 1, 0], dtype=np.float32)
-    assert float(orc.block_score(w)) == 2.0 ** 24                 # (1 + 2^24) rounds to even, then + 1 again
-    assert float(orc.block_score(w, np.float64)) == 2.0 ** 24 + 2
+def pin_block_score_exact(orc):
+    """A block scores the exact sum of its scores.  Float32 arithmetic in any
+    order loses the 1 in 2^24 + 1 (float32 keeps 24 significant bits, and the
+    tie rounds to the even 2^24); the exact sum keeps it.  Sums of dyadic
+    values are exact in every precision and must come back unchanged."""
+    assert orc.block_score(np.array([2.0 ** 24, 1.0, 0.0, 0.0], dtype=np.float32)) == 2.0 ** 24 + 1
+    assert orc.block_score(np.array([1.0, 2.0 ** 24, 1.0, 0.0], dtype=np.float32)) == 2.0 ** 24 + 2
+    # 2^-30 + 1 + 2^-30: float32 keeps neither small term next to 1
+    assert orc.block_score(np.array([2.0 ** -30, 1.0, 2.0 ** -30, 0.0], dtype=np.float32)) == 1.0 + 2.0 ** -29
     r = _rng(26)
     x = r.integers(0, 1 << 10, size=64).astype(np.float32) / 1024.0
-    assert float(orc.block_score(x)) == math.fsum(x.astype(np.float64))
-    assert float(orc.block_score(np.array([0.75], dtype=np.float32))) == 0.75
+    assert orc.block_score(x) == float(x.astype(np.float64).sum())
+    assert orc.block_score(np.array([0.75], dtype=np.float32)) == 0.75
+    assert orc.block_score(np.zeros(8, dtype=np.float32)) == 0.0
+
+
+def pin_select_blocks_exact_sums_decide(orc):
+    """Blocks of 4 whose float32 sums tie but whose exact sums differ by one:
+    B0 = [2^24, 0, 0, 0] sums to 2^24, B1 = [2^24, 1, 0, 0] to 2^24 + 1.  With
+    one block to keep, the exact sums pick B1; float32 sums (any order) would
+    tie and give B0 by the index rule.  A third block of zeros never wins."""
+    s = np.array([2.0 ** 24, 0, 0, 0, 2.0 ** 24, 1, 0, 0, 0, 0, 0, 0, 5.0, 5.0], dtype=np.float32)
+    idx, count, tau = orc.select_blocks_window(s, 13, 2, 4, 4)
+    assert list(idx) == [4, 5, 6, 7, 12, 13] and count == 6
+    assert tau == 2.0 ** 24 + 1
+    # with the small term moved into B0 the choice flips to B0
+    s2 = s.copy()
+    s2[1], s2[5] = 1.0, 0.0
+    idx2, _, _ = orc.select_blocks_window(s2, 13, 2, 4, 4)
+    assert list(idx2) == [0, 1, 2, 3, 12, 13]
 
 
 def pin_select_blocks_invariants(orc):
@@ -554,6 +570,30 @@ def pin_bridge_fp8_closed_form(orc):
     np.testing.assert_array_equal(kc[0, 0, :4], [0x7E, 0xF6, 0x6E, 0x00])
     assert (kc[0, 1] == 0).all() and (vc[0, 1] == 0).all()
     assert vs[0, 0] == np.float32(3.0 / 448.0) and vc[0, 0, 5] == 0xFE and (np.delete(vc[0, 0], 5) == 0).all()
+
+
+def pin_bridge_fp8_divides_by_the_scale(orc):
+    """Rows whose quotients land on an e4m3 tie: 39 * 448 / 52 is exactly 336,
+    halfway between the codes for 320 and 352.  The float32 quotient
+    fl32(39 / fl32(52/448)) is 336.0 and rounds to the even 320 (0x7A);
+    multiplying by fl32(448/52) instead would give 336.00003 and 352 (0x7B).
+    For amax 124 and 93 it is the other way round: the quotient is 336.00003
+    (352, 0x7B) where the reciprocal product gives 336.0 (320, 0x7A).  The
+    largest element always maps to 448 (0x7E) and signs carry over (0x80)."""
+    D, d = 2, 4
+    x = np.array([[1.0, 0.0], [0.0, 1.0]])
+    wk = np.zeros((1, D, d))
+    wk[0, 0, :2] = [52.0, 39.0]
+    wk[0, 1, :3] = [-124.0, -93.0, 93.0]
+    wv = np.zeros((1, D, d))
+    wv[0, 0, :2] = [124.0, 93.0]
+    wv[0, 1, :2] = [52.0, -39.0]
+    kc, vc, ks, vs = orc.bridge_kv_proj_fp8(x, wk, wv)
+    np.testing.assert_array_equal(kc[0, 0], [0x7E, 0x7A, 0x00, 0x00])
+    np.testing.assert_array_equal(kc[0, 1], [0xFE, 0xFB, 0x7B, 0x00])
+    np.testing.assert_array_equal(vc[0, 0], [0x7E, 0x7B, 0x00, 0x00])
+    np.testing.assert_array_equal(vc[0, 1], [0x7E, 0xFA, 0x00, 0x00])
+    assert ks[0, 0] == np.float32(np.float32(52.0) / np.float32(448.0)) and vs[0, 0] == np.float32(124.0 / 448.0)
 
 
 def pin_bridge_fp8_dequant_bound(orc):

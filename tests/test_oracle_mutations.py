@@ -56,12 +56,25 @@ MUTATIONS = [
     ("e4m3 encode one mantissa bit short", "step = np.ldexp(1.0, ex - 1 - 3)", "step = np.ldexp(1.0, ex - 1 - 2)"),
     ("e4m3 encode sign lost", "np.where(np.signbit(y), 0x80, 0)", "np.where(np.signbit(y), 0, 0)"),
     ("fp8 scale for the fnuz range", "(amax / 448.0).astype(np.float32)", "(amax / 240.0).astype(np.float32)"),
+    ("fp8 codes from the reciprocal product", "y = (a / scale[..., None]).astype(np.float32)",
+     "y = (a * np.where(amax > 0, (448.0 / np.where(amax > 0, amax, 1.0)).astype(np.float32), 0.0)[..., None])"
+     ".astype(np.float32)"),
+    ("fp8 quotient in float64", "y = (a / scale[..., None]).astype(np.float32).astype(np.float64)",
+     "y = (a / scale[..., None])"),
     ("fp8 V quantized from K", "vc, vs = quantize(v)", "vc, vs = quantize(k)"),
     ("block ties to the higher index", "key=lambda b: (-sig[b], b))", "key=lambda b: (-sig[b], -b))"),
-    ("block tree adds a pair twice", "t = (t[0::2] + t[1::2]).astype(dtype)", "t = (t[0::2] + t[0::2]).astype(dtype)"),
-    ("block sum left to right", "t = (t[0::2] + t[1::2]).astype(dtype)",
-     "t = np.array([np.cumsum(t, dtype=dtype)[-1]], dtype=dtype)"),
-    ("block sum counts the window", "hi = min(n_cand, (b + 1) * block)", "hi = min(n, (b + 1) * block)"),
+    ("block sums in float32, pairwise tree", "return math.fsum(np.asarray(vals, dtype=np.float64).tolist())",
+     "t = np.asarray(vals, dtype=np.float32)\n    while t.size > 1:\n"
+     "        t = np.concatenate([t, np.zeros(t.size % 2, np.float32)])\n"
+     "        t = (t[0::2] + t[1::2]).astype(np.float32)\n    return float(t[0])"),
+    ("block sums in float32, left to right", "return math.fsum(np.asarray(vals, dtype=np.float64).tolist())",
+     "return float(np.cumsum(np.asarray(vals, dtype=np.float32), dtype=np.float32)[-1])"),
+    ("block sum drops its first token", "return math.fsum(np.asarray(vals, dtype=np.float64).tolist())",
+     "return math.fsum(np.asarray(vals, dtype=np.float64)[1:].tolist())"),
+    ("block scores its best token", "return math.fsum(np.asarray(vals, dtype=np.float64).tolist())",
+     "return float(np.max(vals))"),
+    ("block sum counts the window", "sig = [block_score(s[b * block: min(n_cand, (b + 1) * block)])",
+     "sig = [block_score(s[b * block: min(n, (b + 1) * block)])"),
     ("block partial block dropped", "nb = (n_cand + block - 1) // block\n    sig", "nb = n_cand // block\n    sig"),
     ("block one block too many", "nsel = topk // block", "nsel = topk // block + 1"),
     ("block tokens past the candidates", "toks = [np.arange(b * block, min(n_cand, (b + 1) * block)",
