@@ -43,10 +43,10 @@ def _random_sets(rng, B, n_q, T, sizes, max_sel, with_invalid):
     return idx, cnt
 
 
-# B * n_q = 48 takes the split form (128-key pieces merged by a second kernel), 80 one workgroup per query
-@pytest.mark.parametrize("kv,H,n_q", [("bf16", 16, 24), ("bf16", 4, 24), ("e4m3", 16, 24), ("f32", 4, 24),
-                                      ("f32", 16, 24), ("bf16", 1, 24), ("bf16", 16, 40), ("e4m3", 8, 40),
-                                      ("f32", 2, 40)])
+# Every (cache dtype, H) instance in both forms: B * n_q = 48 takes the split form (128-key
+# pieces merged by a second kernel), 80 one workgroup per query.
+@pytest.mark.parametrize("kv,H,n_q", [(kv, H, n_q) for kv in ("bf16", "e4m3", "f32") for H in (1, 2, 4, 8, 16)
+                                      for n_q in (24, 40)])
 def test_sparse_reuse_parity(kv, H, n_q):
     say("sparse", kv, H, n_q)
     B, T, max_sel = 2, 3000, 1152
@@ -115,6 +115,31 @@ def test_select_parity(q_pos0, n_q, T):
     _select_case(sc, q_pos0, T, 128, 1024)
 
 
+# Rows with a sink (a few candidates scoring 2.0 or more, as scores summed over heads can)
+# next to heavy ties and 1-ulp neighbours at the cut: the exact threshold then spans 31 bits
+# of the float32 pattern.  Short rows (kept whole in LDS), sampled long rows, and few long
+# rows (the multi-workgroup form).
+@pytest.mark.parametrize("q_pos0,n_q,T", [(2900, 24, 3000), (9000, 16, 9100), (40000, 3, 40004)])
+def test_select_sink_and_ties(q_pos0, n_q, T):
+    say("select sink", q_pos0, n_q, T)
+    rng = np.random.default_rng(q_pos0 + 3)
+    ld = (q_pos0 + n_q + 3) // 4 * 4
+    B = 2
+    sc = np.zeros((B, n_q, ld), dtype=np.float32)
+    base = np.float32(1e-3)
+    ulp = np.spacing(base)
+    for b in range(B):
+        for i in range(n_q):
+            n = q_pos0 + i + 1
+            row = base + ulp * rng.integers(-2, 3, n).astype(np.float32)
+            row[rng.integers(0, n, size=600)] = base * np.float32(1.5)
+            row[rng.integers(0, n - 128, size=1 + (b * n_q + i) % 3)] = np.float32(3.0 + i % 2)
+            if i % 4 == 1:
+                row[rng.integers(0, n - 128, size=2)] = np.float32(2.0)
+            sc[b, i, :n] = row.astype(np.float32)
+    _select_case(sc, q_pos0, T, 128, 1024)
+
+
 def _score_rows(rng, B, n_q, q_pos0, ld):
     sc = np.zeros((B, n_q, ld), dtype=np.float32)
     for b in range(B):
@@ -136,9 +161,10 @@ def _score_rows(rng, B, n_q, q_pos0, ld):
     return sc
 
 
-# block-level selection: the decisions are taken on float32 pairwise-tree block sums on both
-# sides, so indices and counts must match exactly.  Cases: rows below and above the cut,
-# partial last blocks, 2.5k and 9.4k candidate blocks (both LDS capacities), blocks of 4..256.
+# block-level selection against the oracle's exact block sums, within the band that the
+# kernel's float32 pairwise-tree sums allow (parity.check_block_selection).  Cases: rows below
+# and above the cut, partial last blocks, 2.5k and 9.4k candidate blocks (both LDS
+# capacities), blocks of 4..256.
 @pytest.mark.parametrize("q_pos0,n_q,window,topk,block", [
     (1100, 200, 128, 1024, 64),
     (9000, 40, 128, 1024, 64),
@@ -160,13 +186,12 @@ def test_select_blocks_parity(q_pos0, n_q, window, topk, block):
                                             topk=topk, block=block)
     torch.cuda.synchronize()
     idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    swaps = 0
     for b in range(B):
         for i in range(n_q):
             p = q_pos0 + i
-            ref, rc, _ = oracle.select_blocks_window(sc[b, i, : p + 1], p, window, topk, block)
-            assert int(cnt[b, i]) == rc, (b, i)
-            assert np.array_equal(idx[b, i, :rc], ref), (b, i)
-            assert (idx[b, i, rc:] == -1).all(), (b, i)
+            swaps += parity.check_block_selection(idx[b, i], int(cnt[b, i]), sc[b, i], p, window, topk, block)
+    print("block swaps within the band:", swaps)
 
 
 def test_select_blocks_feeds_sparse_layer():
@@ -185,9 +210,8 @@ def test_select_blocks_feeds_sparse_layer():
     lse_ref = np.zeros(q64.shape[:2])
     for i in range(64):
         p = q_pos0 + i
-        ref, rc, _ = oracle.select_blocks_window(s_np[i, : p + 1], p, 128, 1024, 64)
-        assert int(cnt_np[i]) == rc and np.array_equal(idx_np[i, :rc], ref), i
-        o_ref[i], lse_ref[i] = oracle.sparse_attn_reuse(q64[i], k64, v64, ref, SCALE)
+        parity.check_block_selection(idx_np[i], int(cnt_np[i]), s_np[i], p, 128, 1024, 64)
+        o_ref[i], lse_ref[i] = oracle.sparse_attn_reuse(q64[i], k64, v64, idx_np[i, : cnt_np[i]], SCALE)
     parity.check_out(o[0], o_ref, "bf16")
     parity.check_lse(lse[0], lse_ref)
 
@@ -233,6 +257,10 @@ def _check_full(inp, o, lse, scores, q_pos0, kv):
     ("e4m3", 8, 130, 77, 300),
     ("e4m3", 4, 5, 100, 110),
     ("e4m3", 1, 10, 90, 100),
+    ("e4m3", 2, 33, 60, 93),
+    ("f32", 1, 0, 150, 150),
+    ("f32", 2, 20, 90, 110),
+    ("f32", 8, 100, 70, 170),
 ])
 def test_full_attn_prefill_parity(kv, H, q_pos0, n_q, T):
     say("prefill", kv, H, q_pos0, n_q, T)
@@ -251,6 +279,17 @@ def test_full_attn_prefill_parity(kv, H, q_pos0, n_q, T):
     ("bf16", 8, 2, 2100, 2098),
     ("bf16", 4, 4, 300, 200),
     ("e4m3", 4, 2, 3000, 2998),
+    ("bf16", 1, 16, 2000, 1984),
+    ("bf16", 1, 5, 900, 800),
+    ("bf16", 2, 8, 1500, 1492),
+    ("bf16", 2, 3, 600, 597),
+    ("e4m3", 1, 16, 2500, 2484),
+    ("e4m3", 2, 8, 1200, 1000),
+    ("e4m3", 8, 2, 4100, 4098),
+    ("f32", 1, 16, 700, 684),
+    ("f32", 2, 8, 800, 792),
+    ("f32", 4, 4, 640, 636),
+    ("f32", 8, 2, 900, 898),
 ])
 def test_full_attn_decode_parity(kv, H, n_q, T, q_pos0):
     say("decode", kv, H, n_q, T, q_pos0)
@@ -338,6 +377,32 @@ def test_bridge_fp8_integer_exact(L, D, n_layers):
     np.testing.assert_array_equal(vc.cpu().numpy(), vc_r)
 
 
+def test_bridge_fp8_quotient_ties():
+    """Rows whose quotients v / scale fall exactly on, or one float32 step off, an e4m3
+    tie: the codes must be those of the IEEE float32 quotient (not of the product
+    with the reciprocal of the scale, which lands on the other side of the tie)."""
+    say("bridge fp8 ties")
+    pairs = [(52, 39), (104, 39), (104, 78), (124, 93), (196, 175), (204, 153), (208, 39), (248, 93),
+             (248, 186), (356, 267), (392, 175), (392, 203), (392, 350)]
+    D, L = 32, len(pairs) * 2
+    x = np.zeros((L, D))
+    wk = np.zeros((1, D, 256))
+    wv = np.zeros((1, D, 256))
+    for r, (amax, a) in enumerate(pairs):
+        x[2 * r, r] = 1.0          # row 2r: +amax, +a, -a spread over the columns
+        x[2 * r + 1, r] = -1.0     # row 2r+1: the negated row
+        wk[0, r, :3] = [amax, a, -a]
+        wv[0, r, 5:7] = [a, amax]
+    kc, vc, ks, vs = hs2.hs2_bridge_kv_proj_fp8(_bf16_from_f32(x).to(DEV), _bf16_from_f32(wk).to(DEV),
+                                               _bf16_from_f32(wv).to(DEV))
+    torch.cuda.synchronize()
+    kc_r, vc_r, ks_r, vs_r = oracle.bridge_kv_proj_fp8(x, wk, wv)
+    np.testing.assert_array_equal(ks.cpu().numpy(), ks_r)
+    np.testing.assert_array_equal(vs.cpu().numpy(), vs_r)
+    np.testing.assert_array_equal(kc.cpu().numpy(), kc_r)
+    np.testing.assert_array_equal(vc.cpu().numpy(), vc_r)
+
+
 def test_bridge_fp8_normal_and_strided_output():
     """Normal data: the float32 accumulation may differ from the exact sum by
     at most 64 roundings of 2**-24 on the scale of sum |x w|, which bounds the
@@ -402,8 +467,7 @@ def test_max_selection_size(n_q):
         q64 = parity.decode(inp["q_sparse"][0][b])
         for i in range(n_q):
             p = q_pos0 + i
-            ref, rc, _ = oracle.select_blocks_window(sc[b, i, : p + 1], p, window, topk, 4)
-            assert int(cntb_np[b, i]) == rc and np.array_equal(idxb_np[b, i, :rc], ref), (b, i)
+            parity.check_block_selection(idxb_np[b, i], int(cntb_np[b, i]), sc[b, i], p, window, topk, 4)
             assert int(cnt_np[b, i]) == window + topk
             o_ref[b, i], lse_ref[b, i] = oracle.sparse_attn_reuse(q64[i], k64, v64, idx_np[b, i, : cnt_np[b, i]], SCALE)
     parity.check_out(o, o_ref, "bf16")
