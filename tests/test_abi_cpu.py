@@ -109,6 +109,10 @@ def sel(lib, **kw):
     (dict(scores=MIS), hs2.HS2_ERR_ALIGN),
     (dict(idx=A + 2), hs2.HS2_ERR_ALIGN),
     (dict(B=0), hs2.HS2_ERR_SHAPE),
+    # one long decode row: the multi-workgroup selector needs a workspace
+    (dict(T=70000, ld=70000, q0=69999), hs2.HS2_ERR_WORKSPACE),
+    (dict(T=70000, ld=70000, q0=69999, ws=A, wsb=64), hs2.HS2_ERR_WORKSPACE),
+    (dict(T=70000, ld=70000, q0=69999, ws=A + 64, wsb=1 << 30), hs2.HS2_ERR_ALIGN),
 ])
 def test_select_rejects(lib, kw, code):
     assert sel(lib, **kw) == code

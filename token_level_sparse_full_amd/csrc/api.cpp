@@ -39,6 +39,18 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool heads_ok(int H) { return H == 1 || H == 2 || H == 4 || H == 8 || H == 16; }
 
+// 0 <= q_pos0 and q_pos0 + n_q <= T, for n_q >= 1 and 1 <= T <= 2^31 - 1 (no
+// sum is formed before its operands are bounded)
+bool positions_ok(int64_t q_pos0, int n_q, int64_t T) { return q_pos0 >= 0 && q_pos0 <= T - n_q; }
+
+// B, n_q and T as every entry point requires them (and the workspace queries
+// assume): positive, B * n_q and T inside int32
+bool rows_ok(int B, int n_q, int64_t T) {
+  return B >= 1 && n_q >= 1 && T >= 1 && (int64_t)B * n_q <= 0x7FFFFFFF && T <= 0x7FFFFFFF;
+}
+
+constexpr int64_t kMaxBridgeRows = (int64_t)1 << 40;
+
 // (q, kv) dtype pair check shared by the attention entry points.
 int check_dtypes(int q_dtype, int kv_dtype, const float* k_scale, const float* v_scale) {
   const bool known = (q_dtype == HS2_F32 || q_dtype == HS2_BF16) &&
@@ -98,7 +110,7 @@ const char* hs2_status_str(int status) {
 }
 
 size_t hs2_full_attn_workspace_bytes(int B, int n_q, int H, int64_t T, int kv_dtype) {
-  if (B < 1 || n_q < 1 || T < 1 || !heads_ok(H)) return 0;
+  if (!rows_ok(B, n_q, T) || !heads_ok(H)) return 0;
   return hs2::attn_workspace_bytes(B, n_q, H, T, kv_kind(kv_dtype));
 }
 
@@ -110,7 +122,7 @@ int hs2_full_attn_scored(const void* q, int q_dtype, int B, int n_q, int H, int 
   if (rc != HS2_OK) return rc;
   if (!scores) return fail(HS2_ERR_NULL, "scores is required");
   if (!aligned(scores, 16)) return fail(HS2_ERR_ALIGN, "scores must be 16-byte aligned");
-  if (q_pos0 < 0 || q_pos0 + n_q > T) return fail(HS2_ERR_SHAPE, "need 0 <= q_pos0 and q_pos0 + n_q <= T");
+  if (!positions_ok(q_pos0, n_q, T)) return fail(HS2_ERR_SHAPE, "need 0 <= q_pos0 and q_pos0 + n_q <= T");
   if (ld_scores < q_pos0 + n_q || ld_scores % 4 != 0)
     return fail(HS2_ERR_SHAPE, "ld_scores must be >= q_pos0 + n_q and a multiple of 4");
   const size_t need = hs2::attn_workspace_bytes(B, n_q, H, T, kv_kind(kv_dtype));
@@ -130,6 +142,7 @@ int hs2_full_attn_scored(const void* q, int q_dtype, int B, int n_q, int H, int 
 }
 
 size_t hs2_select_workspace_bytes(int B, int n_q, int64_t T, int64_t q_pos0) {
+  if (!rows_ok(B, n_q, T) || !positions_ok(q_pos0, n_q, T)) return 0;
   return hs2::select_workspace_bytes(B, n_q, T, q_pos0);
 }
 
@@ -139,15 +152,19 @@ int hs2_select_topk_window(const float* scores, int64_t ld_scores, int B, int n_
   if (!scores || !idx || !count) return fail(HS2_ERR_NULL, "scores, idx and count are required");
   if (B < 1 || n_q < 1 || T < 1) return fail(HS2_ERR_SHAPE, "B, n_q and T must be >= 1");
   if ((int64_t)B * n_q > 0x7FFFFFFF || T > 0x7FFFFFFF) return fail(HS2_ERR_SHAPE, "B*n_q and T must fit in int32");
-  if (window < 1 || topk < 1 || window + topk > HS2_MAX_SELECT)
+  if (window < 1 || topk < 1 || window > HS2_MAX_SELECT || topk > HS2_MAX_SELECT - window)
     return fail(HS2_ERR_SHAPE, "need window >= 1, topk >= 1, window + topk <= %d", HS2_MAX_SELECT);
-  if (q_pos0 < 0 || q_pos0 + n_q > T) return fail(HS2_ERR_SHAPE, "need 0 <= q_pos0 and q_pos0 + n_q <= T");
+  if (!positions_ok(q_pos0, n_q, T)) return fail(HS2_ERR_SHAPE, "need 0 <= q_pos0 and q_pos0 + n_q <= T");
   if (ld_scores < q_pos0 + n_q || ld_scores % 4 != 0)
     return fail(HS2_ERR_SHAPE, "ld_scores must be >= q_pos0 + n_q and a multiple of 4");
   if (!aligned(scores, 16)) return fail(HS2_ERR_ALIGN, "scores must be 16-byte aligned");
   if (!aligned(idx, 4) || !aligned(count, 4)) return fail(HS2_ERR_ALIGN, "idx and count must be 4-byte aligned");
   const size_t need = hs2::select_workspace_bytes(B, n_q, T, q_pos0);
-  if (need > 0 && (!workspace || ws_bytes < need)) return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+  if (need > 0) {
+    if (!workspace) return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if (!aligned(workspace, 256)) return fail(HS2_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (ws_bytes < need) return fail(HS2_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  }
   hs2::SelectParams p;
   p.scores = scores; p.ld_scores = ld_scores; p.B = B; p.n_q = n_q; p.q_pos0 = q_pos0;
   p.window = window; p.topk = topk; p.idx = idx; p.count = count;
@@ -159,7 +176,9 @@ static_assert(HS2_MAX_SELECT == hs2::kMaxSelect && HS2_MAX_BLOCKS == hs2::kMaxBl
 static bool block_ok(int block) { return block >= 4 && block <= 256 && (block & (block - 1)) == 0; }
 
 size_t hs2_select_blocks_workspace_bytes(int B, int n_q, int64_t T, int64_t q_pos0, int window, int block) {
-  if (B < 1 || n_q < 1 || T < 1 || q_pos0 < 0 || window < 1 || !block_ok(block)) return 0;
+  if (!rows_ok(B, n_q, T) || !positions_ok(q_pos0, n_q, T) || window < 1 || window > HS2_MAX_SELECT ||
+      !block_ok(block))
+    return 0;
   return hs2::select_blocks_workspace_bytes(B, n_q, q_pos0, window, block);
 }
 
@@ -169,11 +188,11 @@ int hs2_select_blocks_window(const float* scores, int64_t ld_scores, int B, int 
   if (!scores || !idx || !count) return fail(HS2_ERR_NULL, "scores, idx and count are required");
   if (B < 1 || n_q < 1 || T < 1) return fail(HS2_ERR_SHAPE, "B, n_q and T must be >= 1");
   if ((int64_t)B * n_q > 0x7FFFFFFF || T > 0x7FFFFFFF) return fail(HS2_ERR_SHAPE, "B*n_q and T must fit in int32");
-  if (window < 1 || topk < 1 || window + topk > HS2_MAX_SELECT)
+  if (window < 1 || topk < 1 || window > HS2_MAX_SELECT || topk > HS2_MAX_SELECT - window)
     return fail(HS2_ERR_SHAPE, "need window >= 1, topk >= 1, window + topk <= %d", HS2_MAX_SELECT);
   if (!block_ok(block)) return fail(HS2_ERR_UNSUPPORTED, "block must be a power of two in [4, 256]");
   if (topk % block != 0) return fail(HS2_ERR_SHAPE, "topk must be a multiple of block");
-  if (q_pos0 < 0 || q_pos0 + n_q > T) return fail(HS2_ERR_SHAPE, "need 0 <= q_pos0 and q_pos0 + n_q <= T");
+  if (!positions_ok(q_pos0, n_q, T)) return fail(HS2_ERR_SHAPE, "need 0 <= q_pos0 and q_pos0 + n_q <= T");
   if (ld_scores < q_pos0 + n_q || ld_scores % 4 != 0)
     return fail(HS2_ERR_SHAPE, "ld_scores must be >= q_pos0 + n_q and a multiple of 4");
   if (hs2::select_blocks_nb_max(q_pos0, n_q, window, block) > HS2_MAX_BLOCKS)
@@ -193,7 +212,7 @@ int hs2_select_blocks_window(const float* scores, int64_t ld_scores, int B, int 
 }
 
 size_t hs2_sparse_workspace_bytes(int B, int n_q, int H, int max_sel) {
-  if (B < 1 || n_q < 1 || !heads_ok(H) || max_sel < 1 || max_sel > HS2_MAX_SELECT) return 0;
+  if (!rows_ok(B, n_q, 1) || !heads_ok(H) || max_sel < 1 || max_sel > HS2_MAX_SELECT) return 0;
   return hs2::sparse_workspace_bytes(B, n_q, max_sel);
 }
 
@@ -228,8 +247,8 @@ int hs2_bridge_kv_proj(const void* x, int64_t L, int D, const void* w_k, const v
                        void* stream) {
   if (!x || !w_k || !w_v || !k_out || !v_out) return fail(HS2_ERR_NULL, "x, w_k, w_v, k_out and v_out are required");
   if (d != HS2_HEAD_DIM) return fail(HS2_ERR_UNSUPPORTED, "projection width %d unsupported (only %d)", d, HS2_HEAD_DIM);
-  if (L < 1 || D < 32 || D % 32 != 0 || D > 65536)
-    return fail(HS2_ERR_SHAPE, "need L >= 1 and D a multiple of 32 in [32, 65536]");
+  if (L < 1 || L > kMaxBridgeRows || D < 32 || D % 32 != 0 || D > 65536)
+    return fail(HS2_ERR_SHAPE, "need 1 <= L <= 2^40 and D a multiple of 32 in [32, 65536]");
   if (n_layers < 1 || n_layers > 64) return fail(HS2_ERR_SHAPE, "n_layers must be in [1, 64]");
   if (out_layer_stride < L * (int64_t)d) return fail(HS2_ERR_SHAPE, "out_layer_stride must be >= L * d");
   if ((L + 255) / 256 * (int64_t)(2 * n_layers) > 0x7FFFFFFF) return fail(HS2_ERR_SHAPE, "L too large");
@@ -249,8 +268,8 @@ int hs2_bridge_kv_proj_fp8(const void* x, int64_t L, int D, const void* w_k, con
   if (!x || !w_k || !w_v || !k_out || !v_out || !k_scale || !v_scale)
     return fail(HS2_ERR_NULL, "x, w_k, w_v, k_out, v_out, k_scale and v_scale are required");
   if (d != HS2_HEAD_DIM) return fail(HS2_ERR_UNSUPPORTED, "projection width %d unsupported (only %d)", d, HS2_HEAD_DIM);
-  if (L < 1 || D < 32 || D % 32 != 0 || D > 65536)
-    return fail(HS2_ERR_SHAPE, "need L >= 1 and D a multiple of 32 in [32, 65536]");
+  if (L < 1 || L > kMaxBridgeRows || D < 32 || D % 32 != 0 || D > 65536)
+    return fail(HS2_ERR_SHAPE, "need 1 <= L <= 2^40 and D a multiple of 32 in [32, 65536]");
   if (n_layers < 1 || n_layers > 64) return fail(HS2_ERR_SHAPE, "n_layers must be in [1, 64]");
   if (out_layer_stride < L * (int64_t)d) return fail(HS2_ERR_SHAPE, "out_layer_stride must be >= L * d");
   if (scale_layer_stride < L) return fail(HS2_ERR_SHAPE, "scale_layer_stride must be >= L");

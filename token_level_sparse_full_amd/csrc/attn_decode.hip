@@ -570,7 +570,7 @@ hipError_t launch_decode_kv(const AttnParams& p, const DecodeWs& ws, hipStream_t
 hipError_t launch_prefill(const AttnParams& p, int kv_kind, void* ws, hipStream_t stream);  // attn_prefill.hip
 size_t prefill_bf16_workspace_bytes(int B, int n_q, int H);                         // attn_prefill_bf16.hip
 
-bool attn_uses_decode(int n_q, int H) { return n_q * H <= 16; }
+bool attn_uses_decode(int n_q, int H) { return (int64_t)n_q * H <= 16; }
 
 size_t attn_workspace_bytes(int B, int n_q, int H, int64_t T, int kv_kind) {
   if (!attn_uses_decode(n_q, H)) return kv_kind == KV_BF16 ? prefill_bf16_workspace_bytes(B, n_q, H) : 0;

@@ -21,10 +21,14 @@
 //
 // The e4m3 form (the pages count the KV cache in FP8: agihunt.info summary,
 // results table) quantizes each 256-wide output row from its float32
-// accumulators: scale = amax / 448 (1 for an all-zero row) and, with
-// r = 448 / amax, code = e4m3(clamp(v * r, -448, 448)) rounded to nearest even
-// (IEEE float32 division and product; the conversion instruction rounds to
-// nearest even): one multiply per element.  A workgroup holds whole rows (its
+// accumulators: scale = amax / 448 (1 for an all-zero row) and code =
+// e4m3(clamp(v / scale, -448, 448)) rounded to nearest even, with v / scale
+// the IEEE float32 quotient.  The quotient costs a multiply and two fma per
+// element: with y the correctly rounded 1/scale (one division per row) and
+// q0 = v * y, the residual e = fma(-q0, scale, v) is exact and fma(e, y, q0)
+// is the correctly rounded v / scale (Markstein's correction step; no
+// underflow or overflow arises, |v / scale| <= 448).  The conversion
+// instruction rounds to nearest even.  A workgroup holds whole rows (its
 // 256 columns are one layer's K or V), so the row maxima need only a
 // reduction across lanes inside each wave (DPP inside 16-lane rows, then one
 // swizzle) and one LDS exchange between the two waves that share a row.
@@ -202,12 +206,15 @@ __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParam
         const int64_t grow = m0 + wm * 128 + row;
         const float amax = fmaxf(red[(wm * 2) * 128 + row], red[(wm * 2 + 1) * 128 + row]);
         const float scale = amax > 0.f ? amax / 448.f : 1.f;
-        const float rcp = amax > 0.f ? 448.f / amax : 0.f;
+        const float rcp = 1.f / scale;
         if (grow >= p.L) continue;
         if (wn == 0 && l32 == 0) sc[grow] = scale;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float y = __builtin_amdgcn_fmed3f(acc[i][j][r] * rcp, 448.f, -448.f);
+          const float a = acc[i][j][r];
+          const float q0 = a * rcp;
+          const float q = __builtin_fmaf(__builtin_fmaf(-q0, scale, a), rcp, q0);  // fl32(a / scale)
+          const float y = __builtin_amdgcn_fmed3f(q, 448.f, -448.f);
           out[grow * 256 + wn * 128 + 32 * j + l32] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xFF);
         }
       }

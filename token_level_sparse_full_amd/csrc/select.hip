@@ -197,6 +197,9 @@ __device__ __forceinline__ void block_min_max(uint32_t& lo, uint32_t& hi, SelSha
 // keeps the LDS atomics apart).  After max_pass digits the search stops:
 // tau then has its lower bits 0, a lower bound of the k-th largest that only
 // the values sharing all of its higher bits pass.
+// Digits that resolve any 32-bit range (4 x 10 bits >= 32): the search is exact.
+constexpr int kRadixExact = (32 + SEL_DIGIT - 1) / SEL_DIGIT;
+
 __device__ void lds_radix_select(const uint32_t* v, int n, int k, uint32_t lo, uint32_t hi, int max_pass,
                                  SelShared& sh, int& par, uint32_t& tau, int& need_eq) {
   const int tid = threadIdx.x;
@@ -360,10 +363,13 @@ __global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(8))
   block_min_max(kmin, kmax, sh);
   if (kept >= p.topk && kept <= SEL_CAP) {
     // every pick is at or above u_est (at least topk candidates are), so the
-    // exact tau of the row is the topk-th largest of the kept ones
+    // exact tau of the row is the topk-th largest of the kept ones.  The pick
+    // code below needs tau exact: the search runs until every bit below the
+    // common prefix is resolved (a 31-bit range, e.g. scores on both sides of
+    // 2.0 when they are summed over heads, takes 4 digits of 10 bits).
     uint32_t tau;
     int need_eq;
-    lds_radix_select(cval, kept, p.topk, kmin, kmax, 3, sh, par, tau, need_eq);
+    lds_radix_select(cval, kept, p.topk, kmin, kmax, kRadixExact, sh, par, tau, need_eq);
     // a pick's output slot is the number of picks before it: the values above
     // tau before it plus the first need_eq ties.  One scan of the packed
     // counts (above << 16 | ties) per 4 * SEL_THREADS kept values.
@@ -856,7 +862,7 @@ __global__ __launch_bounds__(SEL_THREADS) void block_select_kernel(const SelectP
   int par = 0;
   uint32_t tau;
   int need_eq;
-  lds_radix_select(bv, nb, nsel, lo, hi, 4, sh, par, tau, need_eq);
+  lds_radix_select(bv, nb, nsel, lo, hi, kRadixExact, sh, par, tau, need_eq);
   // thread t owns the blocks [t*per, (t+1)*per): two ordered scans give the
   // equal-to-tau rank and then the output rank of each selected block
   const int per = (nb + SEL_THREADS - 1) / SEL_THREADS;
