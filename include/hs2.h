@@ -217,6 +217,28 @@ int hs2_sparse_attn_reuse(const void* q, int q_dtype, int B, int n_q, int H, int
 size_t hs2_sparse_workspace_bytes(int B, int n_q, int H, int max_sel);
 
 /*
+ * hs2_sparse_attn_reuse_noalloc - hs2_sparse_attn_reuse for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).
+ *
+ * Same arguments, results and kernels as hs2_sparse_attn_reuse, without the
+ * workspace: the scratch of the split form (B * n_q <= 64) lives in a static
+ * device array of the library, 16.9 MB per GPU, held from the first call on a
+ * device until the process ends.  It calls no hipMalloc, hipFree or other
+ * allocating routine.  Limits: when B * n_q <= 64, B * n_q * ceil(max_sel /
+ * 128) must be at most 1024 (e.g. 64 queries with max_sel <= 2048, or 16
+ * queries with max_sel <= 4096), else HS2_ERR_WORKSPACE; larger B * n_q need
+ * no scratch.  Every call on a GPU shares that GPU's scratch: calls that may
+ * overlap on one GPU (several streams, several host threads) race and must
+ * be ordered by the caller.  `stream` must belong to the current device.
+ */
+int hs2_sparse_attn_reuse_noalloc(const void* q, int q_dtype, int B, int n_q, int H, int d,
+                                  const void* k, const void* v, int kv_dtype,
+                                  const float* k_scale, const float* v_scale, int64_t T,
+                                  const int32_t* idx, const int32_t* count, int max_sel, float sm_scale,
+                                  void* o, float* lse, void* stream);
+
+/*
  * hs2_bridge_kv_proj - KV Bridging re-projection.
  *
  * Defines (HySparse2 pages: agihunt.info summary, paragraph on the outer level

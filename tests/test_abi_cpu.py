@@ -19,7 +19,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = hs2.header_symbols()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
 
@@ -144,6 +144,29 @@ def sparse(lib, **kw):
 ])
 def test_sparse_rejects(lib, kw, code):
     assert sparse(lib, **kw) == code
+
+
+def sparse_na(lib, **kw):
+    a = dict(q=A, qd=BF16, B=1, n_q=1, H=16, d=256, k=A, v=A, kvd=BF16, ks=None, vs=None, T=100, idx=A, count=A,
+             ms=1152, sc=0.0625, o=A, lse=None)
+    a.update(kw)
+    return lib.hs2_sparse_attn_reuse_noalloc(a["q"], a["qd"], a["B"], a["n_q"], a["H"], a["d"], a["k"], a["v"],
+                                             a["kvd"], a["ks"], a["vs"], a["T"], a["idx"], a["count"], a["ms"],
+                                             a["sc"], a["o"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(idx=None), hs2.HS2_ERR_NULL),
+    (dict(ms=0), hs2.HS2_ERR_SHAPE),
+    (dict(d=64), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(o=MIS), hs2.HS2_ERR_ALIGN),
+    # 64 queries x 17 pieces of 128 keys: more than the 1024 slots of the static scratch
+    (dict(B=4, n_q=16, ms=2176), hs2.HS2_ERR_WORKSPACE),
+    (dict(B=1, n_q=33, ms=4096), hs2.HS2_ERR_WORKSPACE),
+])
+def test_sparse_noalloc_rejects(lib, kw, code):
+    assert sparse_na(lib, **kw) == code
+    assert lib.hs2_last_error().decode() != ""
 
 
 def bridge(lib, **kw):

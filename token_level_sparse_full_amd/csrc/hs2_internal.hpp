@@ -31,6 +31,18 @@ struct SparseParams {
 size_t sparse_workspace_bytes(int B, int n_q, int max_sel);
 hipError_t launch_sparse_attn(const SparseParams& p, int q_kind, int kv_kind, void* ws, hipStream_t stream);
 
+// The allocation-free form: the same kernels, with the split form's partial
+// states in a static device array of kSparseStaticPieces (query, 128-key piece)
+// slots.  Calls whose sparse_workspace_bytes() exceeds sparse_static_bytes()
+// must be rejected before the launch.
+constexpr int kSparseStaticPieces = 1024;
+constexpr size_t sparse_static_bytes() {
+  // m and z: 16 floats per piece; o: 16 x 256 floats per piece; each rounded up to 256 B
+  return 2 * (((size_t)kSparseStaticPieces * 16 * 4 + 255) & ~(size_t)255) +
+         (((size_t)kSparseStaticPieces * 16 * 256 * 4 + 255) & ~(size_t)255);
+}
+hipError_t launch_sparse_attn_static(const SparseParams& p, int q_kind, int kv_kind, hipStream_t stream);
+
 struct SelectParams {
   const float* scores;
   int64_t ld_scores;

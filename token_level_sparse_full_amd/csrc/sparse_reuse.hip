@@ -20,6 +20,8 @@
 //  * few queries (decode: B * n_q <= 64) would leave most CUs idle, so their
 //    selected sets are also split into 128-key pieces, one workgroup each,
 //    whose partial states (max, sum, unnormalised O) a second kernel merges.
+#include <mutex>
+
 #include "attn_tile.hpp"
 #include "hs2_internal.hpp"
 
@@ -305,9 +307,50 @@ hipError_t launch_kv(const SparseParams& p, const SparseWs& ws, bool split, hipS
   return hipGetLastError();
 }
 
+// ---- scratch of the allocation-free entry point -------------------------
+// The split form's partial states for at most kSparseStaticPieces (query,
+// 128-key piece) pairs live in this file-scope device array (each GPU the
+// library runs on holds its own copy until the process ends).  Host code never
+// uses the array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, and is passed to the kernels like a
+// workspace.  Nothing in it needs to start at zero (every piece writes its own
+// slots before the merge reads them).
+constexpr size_t kSparseStaticBytes = sparse_static_bytes();
+static __device__ __align__(256) char scratch[kSparseStaticBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of `scratch` on the current device
+hipError_t static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 size_t sparse_workspace_bytes(int B, int n_q, int max_sel) { return sparse_ws_layout(B, n_q, max_sel, nullptr, nullptr); }
+
+hipError_t launch_sparse_attn_static(const SparseParams& p, int q_kind, int kv_kind, hipStream_t stream) {
+  void* ws = nullptr;
+  if (sparse_workspace_bytes(p.B, p.n_q, p.max_sel) > 0) {
+    const hipError_t e = static_scratch(&ws);
+    if (e != hipSuccess) return e;
+  }
+  return launch_sparse_attn(p, q_kind, kv_kind, ws, stream);
+}
 
 hipError_t launch_sparse_attn(const SparseParams& p, int /*q_kind*/, int kv_kind, void* ws_ptr, hipStream_t stream) {
   if (p.B * p.n_q == 0) return hipSuccess;

@@ -35,6 +35,8 @@ _PROTOS = {
     "hs2_sparse_attn_reuse": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp, _i64, _vp, _vp, _i, _f, _vp, _vp,
                                    _vp, _sz, _vp]),
     "hs2_sparse_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "hs2_sparse_attn_reuse_noalloc": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp, _i64, _vp, _vp, _i, _f,
+                                           _vp, _vp, _vp]),
     "hs2_bridge_kv_proj": (_i, [_vp, _i64, _i, _vp, _vp, _i, _i, _vp, _vp, _i64, _vp, _sz, _vp]),
     "hs2_bridge_workspace_bytes": (_sz, [_i, _i, _i]),
     "hs2_bridge_kv_proj_fp8": (_i, [_vp, _i64, _i, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _sz, _vp]),
@@ -191,6 +193,25 @@ def hs2_sparse_attn_reuse(q, k, v, idx, count, *, sm_scale: float | None = None,
                                      _ptr(o), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(),
                                      _stream(stream))
     check("hs2_sparse_attn_reuse", rc)
+    return o, lse
+
+
+def hs2_sparse_attn_reuse_noalloc(q, k, v, idx, count, *, sm_scale: float | None = None, k_scale=None, v_scale=None,
+                                  o=None, lse=None, stream=None, want_lse: bool = True):
+    """hs2_sparse_attn_reuse with the library's static scratch instead of a workspace."""
+    B, n_q, H, d = q.shape
+    T = k.shape[1]
+    max_sel = idx.shape[-1]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, n_q, H), dtype=torch.float32, device=q.device)
+    rc = lib().hs2_sparse_attn_reuse_noalloc(_ptr(q), _dtype_code(q), B, n_q, H, d, _ptr(k), _ptr(v),
+                                             _dtype_code(k), _ptr(k_scale), _ptr(v_scale), T, _ptr(idx),
+                                             _ptr(count), max_sel, sm_scale, _ptr(o), _ptr(lse), _stream(stream))
+    check("hs2_sparse_attn_reuse_noalloc", rc)
     return o, lse
 
 
