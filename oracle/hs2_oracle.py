@@ -16,6 +16,9 @@ Everything here is the plain definition written out, slowly and in float64:
 * ``bridge_kv_proj``     the KV-Bridging re-projection of hidden states
 * ``bridge_kv_proj_fp8`` the same re-projection stored as an FP8 e4m3 cache
                          (codes plus one float32 scale per row)
+* ``rope_partial``       rotary position embedding of the leading dimensions
+* ``swa_attn``           the self-decoder's sliding-window attention with
+                         partial rotary embedding (the step before the bridge)
 
 Sources (the pages about "HySparse2: Hybrid Sparse Attention with Two-Level KV
 Sharing"):
@@ -72,6 +75,8 @@ __all__ = [
     "bridge_kv_proj",
     "f64_to_e4m3_codes",
     "bridge_kv_proj_fp8",
+    "rope_partial",
+    "swa_attn",
 ]
 
 
@@ -399,3 +404,77 @@ def bridge_kv_proj_fp8(x: np.ndarray, w_k: np.ndarray, w_v: np.ndarray):
     kc, ks = quantize(k)
     vc, vs = quantize(v)
     return kc, vc, ks, vs
+
+
+# ----------------------------------------------------------------------------
+# Self-decoder sliding-window attention with partial rotary embedding
+# (agihunt.info summary: the self-decoder mixes full attention with SWA, where
+# each query sees only a recent span of tokens; SWA layers use a 64-dim
+# partial RoPE while full and sparse layers use NoPE; MQA, head dims 256)
+# ----------------------------------------------------------------------------
+
+def rope_partial(x: np.ndarray, pos: np.ndarray, rope_dims: int = 64, base: float = 10000.0) -> np.ndarray:
+    """Rotary position embedding of the leading ``rope_dims`` dimensions.
+
+    The pages name a 64-dimensional partial RoPE and nothing else.  Reading
+    taken here: the rotary embedding as first defined (rotation of
+    consecutive pairs), applied to dimensions 0 .. rope_dims-1 and leaving the
+    others unchanged.  For the vector at position t, the pair (x[2m], x[2m+1])
+    with m < rope_dims / 2 is rotated by the angle t * base**(-2m / rope_dims):
+        x'[2m]   = x[2m] cos(angle) - x[2m+1] sin(angle)
+        x'[2m+1] = x[2m] sin(angle) + x[2m+1] cos(angle)
+
+    x: [..., n, d]; pos: [n] positions of the n vectors (broadcast over any
+    leading axes).  Returns a float64 copy.
+    """
+    x = np.array(x, dtype=np.float64)
+    if rope_dims == 0:
+        return x
+    assert rope_dims % 2 == 0 and rope_dims <= x.shape[-1]
+    m = np.arange(rope_dims // 2, dtype=np.float64)
+    freq = base ** (-2.0 * m / rope_dims)                    # [R/2]
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * freq[None, :]   # [n, R/2]
+    c, s = np.cos(ang), np.sin(ang)
+    even = x[..., 0:rope_dims:2].copy()
+    odd = x[..., 1:rope_dims:2].copy()
+    x[..., 0:rope_dims:2] = even * c - odd * s
+    x[..., 1:rope_dims:2] = even * s + odd * c
+    return x
+
+
+def swa_attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos0: int, window: int = 128, rope_dims: int = 64,
+             base: float = 10000.0, sm_scale: float | None = None):
+    """Sliding-window MQA attention of one sequence with partial rotary
+    embedding of queries and keys.
+
+    q: [n_q, H, d]; query i sits at position p = q_pos0 + i.  k, v: [T, d],
+    key j at position j (stored without rotation).  The query attends to the
+    ``window`` most recent keys, its own included: j in [max(0, p-window+1), p]
+    (the same reading of "the most recent tokens" as the forced window of the
+    sparse layers).  Queries and keys are rotated by their positions with
+    ``rope_partial``; values are not.  Per head:
+        l_j = scale <q'_h, k'_j>,  o_h = sum_j softmax(l)_j v_j,  lse_h = log sum_j exp(l_j)
+
+    Returns (o [n_q, H, d], lse [n_q, H]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    n_q, H, d = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    qpos = q_pos0 + np.arange(n_q)
+    qr = rope_partial(np.swapaxes(q, 0, 1), qpos, rope_dims, base)       # [H, n_q, d]
+    last = q_pos0 + n_q - 1
+    kr = rope_partial(np.asarray(k, dtype=np.float64)[: last + 1], np.arange(last + 1), rope_dims, base)
+    v = np.asarray(v, dtype=np.float64)
+    o = np.zeros((n_q, H, d))
+    lse = np.zeros((n_q, H))
+    for i in range(n_q):
+        p = q_pos0 + i
+        lo = max(0, p - window + 1)
+        logits = sm_scale * (qr[:, i] @ kr[lo: p + 1].T)                 # [H, p+1-lo]
+        m = logits.max(axis=1, keepdims=True)
+        e = np.exp(logits - m)
+        z = e.sum(axis=1, keepdims=True)
+        o[i] = (e / z) @ v[lo: p + 1]
+        lse[i] = m[:, 0] + np.log(z[:, 0])
+    return o, lse

@@ -617,4 +617,140 @@ def pin_bridge_fp8_dequant_bound(orc):
         assert np.isin(top, [0x7E, 0xFE]).all()
 
 
+# ---------------------------------------------------------------------------
+# self-decoder sliding-window attention with partial rotary embedding
+# ---------------------------------------------------------------------------
+
+def _rope_complex(x, pos, R, base):
+    """RoPE in its complex form: the pair (x[2m], x[2m+1]) is the complex number
+    x[2m] + i x[2m+1], multiplied by exp(i t base^(-2m/R)); other dims untouched."""
+    x = np.array(x, dtype=np.float64)
+    if R == 0:
+        return x
+    z = x[..., 0:R:2] + 1j * x[..., 1:R:2]
+    w = np.exp(1j * np.outer(np.asarray(pos, dtype=np.float64), base ** (-np.arange(R // 2) * 2.0 / R)))
+    z = z * w
+    x[..., 0:R:2] = z.real
+    x[..., 1:R:2] = z.imag
+    return x
+
+
+def pin_rope_complex_form(orc):
+    """rope_partial against the complex-multiplication form, at small and large positions."""
+    r = _rng(71)
+    for R, base in [(2, 10000.0), (8, 100.0), (64, 10000.0), (256, 500000.0)]:
+        x = r.standard_normal((3, 7, 256))
+        pos = np.array([0, 1, 2, 127, 131071, 1 << 20, 40000])
+        np.testing.assert_allclose(orc.rope_partial(x, pos, R, base), _rope_complex(x, pos, R, base),
+                                   rtol=1e-9, atol=1e-9)
+    x = r.standard_normal((4, 256))
+    np.testing.assert_array_equal(orc.rope_partial(x, np.arange(4), 0), x)
+
+
+def pin_rope_closed_forms(orc):
+    """Exact rotations: position 0 is the identity; with base = (2/pi)^2 and R = 4
+    the second pair turns by pi/2 at position 1 ((a, b) -> (-b, a)) and by pi at
+    position 2; the first pair always turns by t radians; dims >= R stay."""
+    x = np.array([[3.0, 5.0, 7.0, 11.0, 13.0, 17.0]] * 3)
+    base = (2.0 / math.pi) ** 2
+    y = orc.rope_partial(x, np.array([0, 1, 2]), 4, base)
+    np.testing.assert_array_equal(y[0], x[0])
+    np.testing.assert_allclose(y[1, 2:4], [-11.0, 7.0], atol=1e-12)
+    np.testing.assert_allclose(y[2, 2:4], [-7.0, -11.0], atol=1e-12)
+    np.testing.assert_allclose(y[1, 0:2], [3 * math.cos(1) - 5 * math.sin(1), 3 * math.sin(1) + 5 * math.cos(1)],
+                               atol=1e-12)
+    np.testing.assert_array_equal(y[:, 4:], x[:, 4:])
+    # a rotation keeps each pair's length
+    r = _rng(72)
+    z = r.standard_normal((5, 64))
+    w = orc.rope_partial(z, np.arange(5) * 999, 64, 10000.0)
+    np.testing.assert_allclose(w[:, 0::2] ** 2 + w[:, 1::2] ** 2, z[:, 0::2] ** 2 + z[:, 1::2] ** 2, rtol=1e-12)
+
+
+def pin_swa_window_of_one(orc):
+    """window = 1: o = v_p, and lse = scale <q, k_p> (q and k_p are turned by the
+    same angle, which leaves their inner product unchanged)."""
+    r = _rng(73)
+    H, d, T = 3, 16, 20
+    q = r.standard_normal((4, H, d))
+    k = r.standard_normal((T, d))
+    v = r.standard_normal((T, d))
+    o, lse = orc.swa_attn(q, k, v, 9, window=1, rope_dims=8, base=10.0, sm_scale=0.3)
+    for i in range(4):
+        p = 9 + i
+        np.testing.assert_allclose(o[i], np.tile(v[p], (H, 1)), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[i], 0.3 * (q[i] @ k[p]), rtol=1e-10, atol=1e-12)
+
+
+def pin_swa_full_window_is_full_attention(orc):
+    """Without rotation and with a window covering every key, SWA is full attention."""
+    r = _rng(74)
+    q = r.standard_normal((6, 2, 8))
+    k = r.standard_normal((15, 8))
+    v = r.standard_normal((15, 8))
+    o, lse = orc.swa_attn(q, k, v, 9, window=100, rope_dims=0, sm_scale=0.5)
+    o_ref, lse_ref, _ = _sdpa_reference(q, k, v, 9, 0.5)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_swa_vs_torch_band_mask(orc):
+    """torch SDPA with a band mask on queries and keys rotated by the complex form."""
+    r = _rng(75)
+    n_q, H, d, T, q0, W, R, base = 9, 4, 32, 40, 25, 6, 16, 50.0
+    q = r.standard_normal((n_q, H, d))
+    k = r.standard_normal((T, d))
+    v = r.standard_normal((T, d))
+    o, lse = orc.swa_attn(q, k, v, q0, window=W, rope_dims=R, base=base, sm_scale=0.2)
+    pos = q0 + np.arange(n_q)
+    qr = _rope_complex(np.swapaxes(q, 0, 1), pos, R, base)            # [H, n_q, d]
+    kr = _rope_complex(k, np.arange(T), R, base)
+    keys = np.arange(T)
+    mask = torch.from_numpy((keys[None, :] <= pos[:, None]) & (keys[None, :] > pos[:, None] - W))
+    qt = torch.from_numpy(qr)
+    kt = torch.from_numpy(kr)[None].expand(H, T, d)
+    vt = torch.from_numpy(v)[None].expand(H, T, d)
+    o_ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=0.2)
+    lg = (0.2 * (qt @ kt.transpose(1, 2))).masked_fill(~mask[None], float("-inf"))
+    np.testing.assert_allclose(o, o_ref.permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, torch.logsumexp(lg, dim=-1).T.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def pin_swa_window_edges(orc):
+    """Keys before p-W+1 and after p do not matter; the oldest key inside does."""
+    r = _rng(76)
+    H, d, T, W = 2, 16, 30, 5
+    q = r.standard_normal((3, H, d))
+    k = r.standard_normal((T, d))
+    v = r.standard_normal((T, d))
+    a = orc.swa_attn(q, k, v, 12, window=W, rope_dims=8)
+    k2, v2 = k.copy(), v.copy()
+    k2[:8] = 50 * r.standard_normal((8, d))      # before the first window (12 - 5 + 1 = 8)
+    v2[:8] = 50 * r.standard_normal((8, d))
+    k2[15:] = 50 * r.standard_normal((T - 15, d))  # after the last query (14)
+    b = orc.swa_attn(q, k2, v2, 12, window=W, rope_dims=8)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+    k3 = k.copy()
+    k3[8] += 1.0                                  # the oldest key of the first query's window
+    c = orc.swa_attn(q, k3, v, 12, window=W, rope_dims=8)
+    assert not np.allclose(a[1][0], c[1][0])
+
+
+def pin_swa_relative_positions(orc):
+    """Moving the whole sequence c positions later (c unseen keys in front)
+    leaves every result unchanged: rotated logits depend on position differences."""
+    r = _rng(77)
+    H, d, T, W, c = 2, 64, 24, 7, 1000
+    q = r.standard_normal((5, H, d))
+    k = r.standard_normal((T, d))
+    v = r.standard_normal((T, d))
+    a = orc.swa_attn(q, k, v, 15, window=W, rope_dims=64, base=10000.0)
+    pad = r.standard_normal((c, d))
+    b = orc.swa_attn(q, np.concatenate([pad, k]), np.concatenate([pad, v]), 15 + c, window=W, rope_dims=64,
+                     base=10000.0)
+    np.testing.assert_allclose(a[0], b[0], rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(a[1], b[1], rtol=1e-9, atol=1e-11)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

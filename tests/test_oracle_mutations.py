@@ -22,7 +22,10 @@ MUTATIONS = [
      "e = np.exp(logits + m)\n        z = e.sum(axis=1, keepdims=True)\n        prob"),
     ("scale dropped", "logits = sm_scale * (q[i] @ keys.T)", "logits = (q[i] @ keys.T)"),
     ("values used as keys", "logits = sm_scale * (q[i] @ keys.T)", "logits = sm_scale * (q[i] @ vals.T)"),
-    ("lse without max", "lse[i] = m[:, 0] + np.log(z[:, 0])", "lse[i] = np.log(z[:, 0])"),
+    ("lse without max", "lse[i] = m[:, 0] + np.log(z[:, 0])\n        scores.append",
+     "lse[i] = np.log(z[:, 0])\n        scores.append"),
+    ("swa lse without max", "lse[i] = m[:, 0] + np.log(z[:, 0])\n    return o, lse",
+     "lse[i] = np.log(z[:, 0])\n    return o, lse"),
     ("score as mean over heads", "scores.append(prob.sum(axis=0))", "scores.append(prob.mean(axis=0))"),
     ("score from first head only", "scores.append(prob.sum(axis=0))", "scores.append(prob[0])"),
     ("unnormalised probabilities", "prob = e / z                            # softmax",
@@ -77,6 +80,17 @@ MUTATIONS = [
      "sig = [block_score(s[b * block: min(n, (b + 1) * block)])"),
     ("block partial block dropped", "nb = (n_cand + block - 1) // block\n    sig", "nb = n_cand // block\n    sig"),
     ("block one block too many", "nsel = topk // block", "nsel = topk // block + 1"),
+    ("rope rotation sign", "x[..., 0:rope_dims:2] = even * c - odd * s", "x[..., 0:rope_dims:2] = even * c + odd * s"),
+    ("rope pairs are the two halves", "even = x[..., 0:rope_dims:2].copy()\n    odd = x[..., 1:rope_dims:2].copy()",
+     "even = x[..., 0:rope_dims // 2].copy()\n    odd = x[..., rope_dims // 2:rope_dims].copy()"),
+    ("rope frequency exponent halved", "freq = base ** (-2.0 * m / rope_dims)", "freq = base ** (-m / rope_dims)"),
+    ("rope base fixed", "freq = base ** (-2.0 * m / rope_dims)", "freq = 10000.0 ** (-2.0 * m / rope_dims)"),
+    ("swa window one long", "lo = max(0, p - window + 1)", "lo = max(0, p - window)"),
+    ("swa window one short", "lo = max(0, p - window + 1)", "lo = max(0, p - window + 2)"),
+    ("swa keys not rotated", "kr = rope_partial(np.asarray(k, dtype=np.float64)[: last + 1], np.arange(last + 1), "
+     "rope_dims, base)", "kr = np.asarray(k, dtype=np.float64)[: last + 1]"),
+    ("swa queries rotated by index", "qpos = q_pos0 + np.arange(n_q)", "qpos = np.arange(n_q)"),
+    ("swa values from the rotated keys", "o[i] = (e / z) @ v[lo: p + 1]", "o[i] = (e / z) @ kr[lo: p + 1]"),
     ("block tokens past the candidates", "toks = [np.arange(b * block, min(n_cand, (b + 1) * block)",
      "toks = [np.arange(b * block, min(n, (b + 1) * block)"),
 ]
