@@ -46,163 +46,250 @@ def parse():
     ap.add_argument("--no-others", action="store_true",
                     help="skip the decode (16 x 32k, 1M FP8) and bridge (64k) workload lines")
     ap.add_argument("--pmc-probe", action="store_true",
-                    help="run one warm-up step and one step of the full-attention launches, then a 1 GiB "
-                         "copy-calibration kernel (the target of the traffic counter runs)")
+                    help="run the launches the counter passes measure, one phase after another: the 128k "
+                         "scored full attention + select calls, one sparse layer, one step of each decode "
+                         "workload, then a 1 GiB copy-calibration kernel")
     ap.add_argument("--collect-traffic", action="store_true",
-                    help="run rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE over --pmc-probe and record the "
-                         "per-launch HBM traffic of the full-attention kernel under profiles/")
+                    help="run rocprofv3 --pmc FETCH_SIZE, WRITE_SIZE and SQ counter passes over --pmc-probe "
+                         "and record the per-launch traffic of every kernel group under profiles/")
     ap.add_argument("--out-dir", default="profile_runs",
                     help="directory (relative to the repository root) for the raw counter output of "
                          "--collect-traffic and a copy of the record")
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_128k_traffic.txt")
-KERNEL_SOURCES = ["attn_prefill_bf16.hip", "hs2_device.hpp", "hs2_internal.hpp"]
+COUNTER_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.txt")
 CALIB_BYTES = 1 << 30          # the calibration kernel reads and writes exactly this many bytes
+COMMON_SOURCES = ["hs2_device.hpp"]    # device helpers every kernel includes
+# kernel groups measured by the counter probe: (phase, kernel-name substrings, sources, launches per phase)
+GROUPS = {
+    "full_attn_prefill": ("prefill", ["prefill_bf16_kernel"], ["attn_prefill_bf16.hip"], "chunks"),
+    "select_prefill": ("prefill", ["select_kernel"], ["select.hip"], "chunks"),
+    "sparse_prefill": ("prefill_sparse", ["sparse_attn_kernel"], ["sparse_reuse.hip", "attn_tile.hpp"], 1),
+    "full_attn_decode_b16_32k": ("decode_b16_32k", ["decode_stream_kernel", "decode_merge_kernel",
+                                                    "decode_score_kernel"], ["attn_decode.hip", "attn_tile.hpp"], 1),
+    "select_decode_b16_32k": ("decode_b16_32k", ["select_kernel", "mb_"], ["select.hip"], 1),
+    "sparse_decode_b16_32k": ("decode_b16_32k", ["sparse_attn_kernel", "sparse_merge_kernel"],
+                              ["sparse_reuse.hip", "attn_tile.hpp"], 3),
+    "full_attn_decode_1m_fp8": ("decode_1m_fp8", ["decode_stream_kernel", "decode_merge_kernel",
+                                                  "decode_score_kernel"], ["attn_decode.hip", "attn_tile.hpp"], 1),
+    "select_decode_1m_fp8": ("decode_1m_fp8", ["select_kernel", "mb_"], ["select.hip"], 1),
+    "sparse_decode_1m_fp8": ("decode_1m_fp8", ["sparse_attn_kernel", "sparse_merge_kernel"],
+                             ["sparse_reuse.hip", "attn_tile.hpp"], 4),
+}
+# the probe's phases in launch order; the "_setup" phases (input generation, warm-ups, cache
+# flushes) are measured by nobody
+PHASES = ["prefill", "prefill_sparse", "_setup_b16", "decode_b16_32k", "_setup_1m", "decode_1m_fp8",
+          "_setup_calib", "calibration"]
+MARKER = "FillFunctor<double>"   # a float64 fill marks the start of each probe phase and the end
+SQ_CTRS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"]
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the sources the full-attention kernel is compiled from."""
+def source_hash(group: str) -> str:
+    """sha256 over the sources a kernel group is compiled from."""
     import hashlib
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in GROUPS[group][2] + COMMON_SOURCES:
         with open(os.path.join(ROOT, "token_level_sparse_full_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic_record() -> dict:
-    """The counter record written by --collect-traffic, or {} when there is none or the
-    kernel sources changed since it was taken."""
+def read_counter_record() -> dict:
+    """{group: {key: value}} from the record written by --collect-traffic; a group is left
+    out when its kernel sources changed since the counters were taken."""
+    out, cur = {}, None
     try:
-        rec = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(COUNTER_FILE) as f:
             for line in f:
-                if "=" in line and not line.startswith("#"):
+                line = line.strip()
+                if line.startswith("[") and line.endswith("]"):
+                    cur = out.setdefault(line[1:-1], {})
+                elif "=" in line and not line.startswith("#") and cur is not None:
                     key, val = line.split("=", 1)
-                    rec[key.strip()] = val.strip()
-        return rec if rec.get("kernel_source_sha256_16") == kernel_source_hash() else {}
+                    cur[key.strip()] = val.strip()
     except OSError:
         return {}
+    return {g: r for g, r in out.items() if g in GROUPS and r.get("source_sha256_16") == source_hash(g)}
 
 
-def read_traffic():
-    """Per-launch HBM bytes of the full-attention kernel recorded by --collect-traffic,
-    or None when there is no record or the kernel sources changed since it was taken."""
+def _rec_float(rec: dict, group: str, key: str):
     try:
-        return float(read_traffic_record()["traffic_bytes_per_launch"])
+        return float(rec[group][key])
     except (KeyError, ValueError):
         return None
 
 
-def read_mfma_busy():
-    """MFMA busy fraction (counters, against 2.4 GHz) of the same record, or None."""
-    try:
-        return float(read_traffic_record()["mfma_busy_frac_at_2p4ghz"])
-    except (KeyError, ValueError):
-        return None
-
-
-def collect_traffic(args):
-    """Two counter passes (FETCH_SIZE, then WRITE_SIZE) over `bench.py --pmc-probe`, each
-    scaled by what the same counter reads for a copy kernel that moves exactly CALIB_BYTES."""
+def _counter_pass(args, ctrs, tag):
+    """One rocprofv3 --pmc pass over the probe; returns the dispatches in order as
+    (dispatch id, kernel name, {counter: value}, seconds)."""
     import csv
     import glob
     import subprocess
 
-    out_root = os.path.join(ROOT, args.out_dir, "traffic")
+    d = os.path.join(ROOT, args.out_dir, "traffic", tag)
+    cmd = ["rocprofv3", "--pmc", *ctrs, "--output-format", "csv", "-d", d, "-o", "p", "--",
+           sys.executable, os.path.join(ROOT, "bench.py"), "--pmc-probe", "--chunk", str(args.chunk)]
+    print("[traffic] " + " ".join(cmd), flush=True)
+    r = subprocess.run(cmd, cwd="/tmp", env=dict(os.environ, TMPDIR="/tmp"), timeout=600)
+    if r.returncode != 0:
+        raise SystemExit(f"rocprofv3 pass {tag} failed with status {r.returncode}")
+    per = {}
+    for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(fn)):
+            i = int(row["Dispatch_Id"])
+            e = per.setdefault(i, [row["Kernel_Name"], {}, (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-9])
+            e[1][row["Counter_Name"]] = e[1].get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    return [(i, per[i][0], per[i][1], per[i][2]) for i in sorted(per)]
+
+
+def _kernel_short(name: str) -> str:
+    """'void ns::(anonymous namespace)::k<1, 2>(args)' -> 'k<1, 2>'"""
+    import re
+    m = re.search(r"::(\w+(?:<[^()]*>)?)\(", name)
+    return m.group(1) if m else name[:60]
+
+
+def _phases(disp):
+    """Split the probe's dispatches at the marker kernels: {phase: [dispatches]}."""
+    marks = [k for k, x in enumerate(disp) if MARKER in x[1]]
+    if len(marks) != len(PHASES) + 1:
+        raise SystemExit(f"expected {len(PHASES) + 1} phase markers in the probe, found {len(marks)}")
+    return {ph: disp[marks[k] + 1: marks[k + 1]] for k, ph in enumerate(PHASES)}
+
+
+def collect_traffic(args):
+    """Counter passes (FETCH_SIZE, WRITE_SIZE, then SQ counters) over `bench.py --pmc-probe`.
+    Each byte counter is scaled by what it reads for a copy kernel that moves exactly
+    CALIB_BYTES; the per-launch bytes of every kernel group go to profiles/."""
+    n_chunks = len(range(0, inputs_L(args), min(args.chunk, inputs_L(args))))
     res = {}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
-        d = os.path.join(out_root, ctr.lower())
-        cmd = ["rocprofv3", "--pmc", ctr, "--output-format", "csv", "-d", d, "-o", "p", "--",
-               sys.executable, os.path.join(ROOT, "bench.py"), "--pmc-probe", "--workload", args.workload,
-               "--chunk", str(args.chunk)]
-        print("[traffic] " + " ".join(cmd), flush=True)
-        env = dict(os.environ, TMPDIR="/tmp")
-        r = subprocess.run(cmd, cwd="/tmp", env=env, timeout=300)
-        if r.returncode != 0:
-            raise SystemExit(f"rocprofv3 {ctr} pass failed with status {r.returncode}")
-        rows = []
-        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            rows += list(csv.DictReader(open(fn)))
-        per = {}
-        for row in rows:
-            if row["Counter_Name"] != ctr:
-                continue
-            key = (int(row["Dispatch_Id"]), row["Kernel_Name"])
-            per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
-        disp = sorted(per.items())
-        attn = [v for (i, n), v in disp if "prefill_bf16_kernel" in n]
-        calib = [v for (i, n), v in disp if "elementwise" in n]
-        n_launch = len(range(0, inputs_L(args), min(args.chunk, inputs_L(args))))
-        # one full-attention call = the lse dispatch + the P/V dispatch; the
-        # measured step is the last n_launch calls (the warm-up step comes first)
-        attn = attn[-2 * n_launch:]
-        res[ctr] = {"attn_kib_per_launch": sum(attn) / n_launch, "calib_kib": calib[-1], "launches": n_launch}
-    # one more pass: MFMA busy cycles of the same launches (utilisation of the matrix cores)
-    d = os.path.join(out_root, "sq")
-    sq_ctrs = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"]
-    cmd = ["rocprofv3", "--pmc", *sq_ctrs, "--output-format", "csv", "-d", d, "-o", "p", "--",
-           sys.executable, os.path.join(ROOT, "bench.py"), "--pmc-probe", "--workload", args.workload,
-           "--chunk", str(args.chunk)]
-    print("[traffic] " + " ".join(cmd), flush=True)
-    r = subprocess.run(cmd, cwd="/tmp", env=dict(os.environ, TMPDIR="/tmp"), timeout=300)
-    if r.returncode != 0:
-        raise SystemExit(f"rocprofv3 SQ pass failed with status {r.returncode}")
-    rows = []
-    for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-        rows += list(csv.DictReader(open(fn)))
-    sq, dur = {}, {}
-    for row in rows:
-        if "prefill_bf16_kernel" not in row["Kernel_Name"]:
-            continue
-        i = int(row["Dispatch_Id"])
-        sq.setdefault(i, {}).setdefault(row["Counter_Name"], 0.0)
-        sq[i][row["Counter_Name"]] += float(row["Counter_Value"])
-        dur[i] = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-9
-    n_launch = res["FETCH_SIZE"]["launches"]
-    last = sorted(sq)[-2 * n_launch:]            # both dispatches of each call
-    sq_avg = {c: sum(sq[i].get(c, 0.0) for i in last) / n_launch for c in sq_ctrs}
-    dur_avg = sum(dur[i] for i in last) / n_launch
-    # busy cycles of all 1024 SIMDs over the launch at the 2.4 GHz peak clock (a lower bound
-    # on the utilisation when the clock runs below peak)
-    mfma_util = sq_avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * dur_avg * 2.4e9)
-    f_fetch = CALIB_BYTES / (res["FETCH_SIZE"]["calib_kib"] * 1024.0)
-    f_write = CALIB_BYTES / (res["WRITE_SIZE"]["calib_kib"] * 1024.0)
-    fetch_b = res["FETCH_SIZE"]["attn_kib_per_launch"] * 1024.0 * f_fetch
-    write_b = res["WRITE_SIZE"]["attn_kib_per_launch"] * 1024.0 * f_write
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
-        f.write("# HBM traffic of one scored full-attention call (its two dispatches: prefill_bf16_kernel<H,1>,\n")
-        f.write("# the lse pass, and prefill_bf16_kernel<H,2>, the P/V pass), one call of the\n")
-        f.write(f"# {args.workload} step ({res['FETCH_SIZE']['launches']} launches of {args.chunk} queries,"
-                " averaged), from rocprofv3 counter passes.\n")
-        f.write("# command: python bench.py --collect-traffic   (runs, one pass per counter set:)\n")
-        f.write(f"#   rocprofv3 --pmc <FETCH_SIZE | WRITE_SIZE | {' '.join(sq_ctrs)}> --output-format csv -d <dir> -o p"
-                f" -- python bench.py --pmc-probe --workload {args.workload} --chunk {args.chunk}\n")
-        f.write("# calibration: a float32 copy kernel (torch.mul by 1.0) that reads and writes exactly 1 GiB;\n")
-        f.write("# each counter is scaled by (1 GiB / what it reads for that kernel).\n")
-        f.write(f"fetch_kib_per_launch_raw = {res['FETCH_SIZE']['attn_kib_per_launch']:.1f}\n")
-        f.write(f"write_kib_per_launch_raw = {res['WRITE_SIZE']['attn_kib_per_launch']:.1f}\n")
-        f.write(f"calib_fetch_kib = {res['FETCH_SIZE']['calib_kib']:.1f}\n")
-        f.write(f"calib_write_kib = {res['WRITE_SIZE']['calib_kib']:.1f}\n")
-        f.write(f"scale_fetch = {f_fetch:.4f}\n")
-        f.write(f"scale_write = {f_write:.4f}\n")
-        f.write(f"fetch_bytes_per_launch = {fetch_b:.4e}\n")
-        f.write(f"write_bytes_per_launch = {write_b:.4e}\n")
-        f.write(f"traffic_bytes_per_launch = {fetch_b + write_b:.4e}\n")
-        f.write("# MFMA utilisation of the same launches (third pass, SQ counters, per launch):\n")
-        for c in sq_ctrs:
-            f.write(f"{c.lower()} = {sq_avg[c]:.4e}\n")
-        f.write(f"launch_seconds_under_counters = {dur_avg:.4f}\n")
-        f.write(f"mfma_busy_frac_at_2p4ghz = {mfma_util:.4f}\n")
-        f.write(f"kernel_source_sha256_16 = {kernel_source_hash()}\n")
-    text = open(TRAFFIC_FILE).read()
+        ph = _phases(_counter_pass(args, [ctr], ctr.lower()))
+        calib = [x[2][ctr] for x in ph["calibration"] if "elementwise" in x[1]][-1]
+        res[ctr] = (ph, CALIB_BYTES / (calib * 1024.0), calib)
+    sq = _phases(_counter_pass(args, SQ_CTRS, "sq"))
+    lines = [
+        "# HBM-side traffic per launch of each kernel group of the path, from rocprofv3 counter passes",
+        "# over one probe run (bench.py --pmc-probe: one warm-up step of the 128k prefill, then its",
+        f"# {n_chunks} scored full-attention + select calls, one sparse layer, one decode step of each decode",
+        "# workload with K/V pushed out of the caches first, and a 1 GiB copy).",
+        "# command: python bench.py --collect-traffic   (one pass per counter set:)",
+        f"#   rocprofv3 --pmc <FETCH_SIZE | WRITE_SIZE | {' '.join(SQ_CTRS)}> --output-format csv -d <dir> -o p"
+        f" -- python bench.py --pmc-probe --chunk {args.chunk}",
+        "# calibration: a float32 copy kernel (torch.mul by 1.0) that reads and writes exactly 1 GiB;",
+        "# each counter is scaled by (1 GiB / what it reads for that kernel).  The counters count what the",
+        "# L2 caches fetch from and write to the memory fabric, so a fetch served by the 256 MB last-level",
+        "# cache (MALL) counts as well: they bound the HBM bytes from above.",
+        f"calib_fetch_kib = {res['FETCH_SIZE'][2]:.1f}",
+        f"calib_write_kib = {res['WRITE_SIZE'][2]:.1f}",
+        f"scale_fetch = {res['FETCH_SIZE'][1]:.4f}",
+        f"scale_write = {res['WRITE_SIZE'][1]:.4f}",
+    ]
+    for g, (phase, names, _, nl) in GROUPS.items():
+        launches = n_chunks if nl == "chunks" else nl
+        sel = lambda lst: [x for x in lst if any(n in x[1] for n in names)]  # noqa: E731
+        f_disp = sel(res["FETCH_SIZE"][0][phase])
+        w_disp = sel(res["WRITE_SIZE"][0][phase])
+        fetch = sum(x[2]["FETCH_SIZE"] for x in f_disp) * 1024.0 * res["FETCH_SIZE"][1] / launches
+        write = sum(x[2]["WRITE_SIZE"] for x in w_disp) * 1024.0 * res["WRITE_SIZE"][1] / launches
+        kernels = sorted({_kernel_short(x[1]) for x in f_disp})
+        lines += ["", f"[{g}]", f"kernels = {', '.join(kernels)}", f"dispatches = {len(f_disp)}",
+                  f"launches = {launches}", f"fetch_bytes_per_launch = {fetch:.4e}",
+                  f"write_bytes_per_launch = {write:.4e}", f"traffic_bytes_per_launch = {fetch + write:.4e}",
+                  f"seconds_per_launch_under_counters = {sum(x[3] for x in f_disp) / launches:.6f}"]
+        if g == "full_attn_prefill":
+            s_disp = sel(sq[phase])
+            tot = {c: sum(x[2].get(c, 0.0) for x in s_disp) / launches for c in SQ_CTRS}
+            dur = sum(x[3] for x in s_disp) / launches
+            lines += [f"{c.lower()} = {tot[c]:.4e}" for c in SQ_CTRS]
+            # busy cycles of all 1024 SIMDs over the launch at the 2.4 GHz peak clock
+            lines += [f"mfma_busy_frac_at_2p4ghz = {tot['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * dur * 2.4e9):.4f}",
+                      f"mean_clock_ghz_from_grbm = {tot['GRBM_GUI_ACTIVE'] / 8 / dur / 1e9:.3f}"]
+        lines.append(f"source_sha256_16 = {source_hash(g)}")
+    text = "\n".join(lines) + "\n"
+    os.makedirs(os.path.dirname(COUNTER_FILE), exist_ok=True)
+    with open(COUNTER_FILE, "w") as f:
+        f.write(text)
     os.makedirs(os.path.join(ROOT, args.out_dir), exist_ok=True)
-    with open(os.path.join(ROOT, args.out_dir, os.path.basename(TRAFFIC_FILE)), "w") as f:
+    with open(os.path.join(ROOT, args.out_dir, os.path.basename(COUNTER_FILE)), "w") as f:
         f.write(text)
     print(text, flush=True)
+
+
+def pmc_probe(args):
+    """The launches the counter passes measure, each phase opened by a float64 fill (the
+    marker) and the last one closed by another."""
+    import torch
+
+    from token_level_sparse_full_amd import hs2, inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mark_t = torch.empty(1, dtype=torch.float64, device=dev)   # no kernel: only the markers fill it
+    marker = lambda: mark_t.fill_(1.0)  # noqa: E731
+    wl = inputs.WORKLOADS["prefill_128k"]
+    L, H, scale = wl.L, wl.H, 1.0 / 16
+    inp = inputs.attention_inputs(B=1, n_q=L, T=L, H=H, d=D, kv="bf16", n_sparse=1, seed=wl.seed, device=dev)
+    inputs.plant_needles(inp["q"][0], inp["k"][0], wl.needles, wl.seed)
+    C = min(args.chunk, L)
+    chunks = [(c0, min(L, c0 + C)) for c0 in range(0, L, C)]
+    ld = (L + 3) // 4 * 4
+    scores = torch.empty((1, C, ld), dtype=torch.float32, device=dev)
+    idx = torch.empty((1, L, 1152), dtype=torch.int32, device=dev)
+    cnt = torch.empty((1, L), dtype=torch.int32, device=dev)
+    o = torch.empty_like(inp["q"])
+    lse = torch.empty((1, L, H), dtype=torch.float32, device=dev)
+
+    def fa_select():
+        for c0, c1 in chunks:
+            hs2.hs2_full_attn_scored(inp["q"][:, c0:c1], inp["k"], inp["v"], q_pos0=c0, sm_scale=scale,
+                                     o=o[:, c0:c1], lse=lse[:, c0:c1], scores=scores[:, : c1 - c0], ld_scores=ld)
+            hs2.hs2_select_topk_window(scores[:, : c1 - c0], q_pos0=c0, T=L, n_q=c1 - c0, idx=idx[:, c0:c1],
+                                       count=cnt[:, c0:c1])
+    fa_select()                                   # warm-up
+    hs2.hs2_sparse_attn_reuse(inp["q_sparse"][0], inp["k"], inp["v"], idx, cnt, sm_scale=scale)
+    torch.cuda.synchronize()
+    marker()
+    fa_select()
+    marker()
+    hs2.hs2_sparse_attn_reuse(inp["q_sparse"][0], inp["k"], inp["v"], idx, cnt, sm_scale=scale, o=o, lse=lse)
+    marker()
+    torch.cuda.synchronize()
+    del inp, scores, idx, cnt, o, lse
+    torch.cuda.empty_cache()
+    junk = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for name in ("decode_b16_32k", "decode_1m_fp8"):
+        w = inputs.WORKLOADS[name]
+        if w.kv == "e4m3":
+            k, v, ks, vs = inputs.kv_cache((1, w.T, 256), "e4m3", w.seed, dev)
+        else:
+            k, v, ks, vs = inputs.kv_cache((w.B, w.T, 256), w.kv, w.seed, dev)
+        q = inputs.cast(inputs.normal((w.B, 1, w.H, 256), inputs.STD_QKV, w.seed, inputs.S_Q, dev), "bf16")
+        qs = [inputs.cast(inputs.normal((w.B, 1, w.H, 256), inputs.STD_QKV, w.seed, inputs.S_QSPARSE + i, dev),
+                          "bf16") for i in range(w.n_sparse)]
+        p = w.T - 1
+
+        def step():
+            _, _, sc = hs2.hs2_full_attn_scored(q, k, v, q_pos0=p, sm_scale=scale, k_scale=ks, v_scale=vs)
+            i_, c_ = hs2.hs2_select_topk_window(sc, q_pos0=p, T=w.T)
+            for x in qs:
+                hs2.hs2_sparse_attn_reuse(x, k, v, i_, c_, sm_scale=scale, k_scale=ks, v_scale=vs)
+        step()                                    # warm-up (and the allocations)
+        junk.fill_(1)                             # K/V out of L2 and MALL
+        marker()
+        step()
+        marker()
+        torch.cuda.synchronize()
+        del k, v, ks, vs
+        torch.cuda.empty_cache()
+    a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    marker()
+    torch.mul(a, 1.0, out=b)                      # copy calibration: reads and writes 1 GiB
+    marker()
+    torch.cuda.synchronize()
+    print("pmc probe done", flush=True)
 
 
 def inputs_L(args) -> int:
@@ -217,6 +304,9 @@ def main():
         sys.exit(2)
     if args.collect_traffic:      # orchestration only: this process never touches the GPU
         collect_traffic(args)
+        return
+    if args.pmc_probe:
+        pmc_probe(args)
         return
 
     import numpy as np
@@ -271,20 +361,6 @@ def main():
             hs2.hs2_sparse_attn_reuse(qs[s], k, v, idx, cnt, sm_scale=scale, o=o_sp[s], lse=lse_sp[s])
             mark()
 
-    if args.pmc_probe:
-        step()                                   # warm-up step
-        torch.cuda.synchronize()
-        for c0, c1 in chunks:                    # the measured full-attention launches
-            hs2.hs2_full_attn_scored(q[:, c0:c1], k, v, q_pos0=c0, sm_scale=scale, o=o_full[:, c0:c1],
-                                     lse=lse_full[:, c0:c1], scores=scores[:, : c1 - c0], ld_scores=ld)
-        torch.cuda.synchronize()
-        a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        torch.mul(a, 1.0, out=b)                 # copy calibration: reads and writes 1 GiB
-        torch.cuda.synchronize()
-        print("pmc probe done", flush=True)
-        return
-
     # ---------------------------------------------------------------- warmup + timed steps
     for _ in range(args.warmup):
         step()
@@ -323,6 +399,20 @@ def main():
     cand = np.maximum(npos - window, 0)
     sel_bytes = np.where(cand > topk, cand, 0).sum() * 4 + L * max_sel * 4
     sel_gbs = sel_bytes / (sel_ms * 1e-3) / 1e9
+    rec = read_counter_record()
+    n_ch = len(chunks)
+
+    def traffic(group, seconds_per_launch):
+        """counter bytes per launch, their rate and its fraction of the HBM peak (None without a record)"""
+        t = _rec_float(rec, group, "traffic_bytes_per_launch")
+        if t is None:
+            return {"traffic": None}
+        gbs = t / seconds_per_launch / 1e9
+        return {"traffic": t, "traffic_gbs": gbs, "traffic_hbm_frac": gbs / HBM_PEAK_GBS}
+
+    ceil_ms = gather_l2_ceiling(hs2, qs[0], k, v, idx, L, H, scale, max_sel)
+    ceil_bytes = L * (max_sel * 2 * D * 2 + 2 * H * D * 2 + max_sel * 4 + 4 + H * 4)
+    ceil_gbs = ceil_bytes / (ceil_ms * 1e-3) / 1e9
 
     result = {
         "metric": "sparse-reuse attn queries/s at 128k ctx + prefill tokens/s; % HBM/MFMA peak",
@@ -342,30 +432,73 @@ def main():
                    "global_batch": 1, "parallelism": "single GPU"},
         "roofline": {"kernel": "hs2_full_attn_scored, prefill path (lse dispatch + P/V dispatch)", "bound": "mfma",
                      "achieved": fa_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": fa_tflops / BF16_PEAK_TFLOPS, "traffic": read_traffic(),
-                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "algorithmic_flop_per_step": fa_flop, "launches_per_step": len(chunks),
+                     "frac": fa_tflops / BF16_PEAK_TFLOPS,
+                     "traffic": _rec_float(rec, "full_attn_prefill", "traffic_bytes_per_launch"),
+                     "traffic_unit": "bytes per launch between L2 and the memory fabric (rocprofv3 FETCH_SIZE + "
+                                     "WRITE_SIZE, copy-calibrated)",
+                     "algorithmic_flop_per_step": fa_flop, "launches_per_step": n_ch,
                      # the lse dispatch repeats QK^T: executed MFMA work is 1.5x the algorithmic
                      "executed_frac": 1.5 * fa_tflops / BF16_PEAK_TFLOPS,
-                     "mfma_busy_frac_counters": read_mfma_busy()},
+                     "mfma_busy_frac_counters": _rec_float(rec, "full_attn_prefill", "mfma_busy_frac_at_2p4ghz"),
+                     "clock_ghz_counters": _rec_float(rec, "full_attn_prefill", "mean_clock_ghz_from_grbm")},
+        "rooflines": {
+            "select": {"kernel": "hs2_select_topk_window (select_kernel), per query chunk", "bound": "hbm",
+                       "achieved": sel_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": sel_gbs / HBM_PEAK_GBS,
+                       "algorithmic_bytes_per_launch": sel_bytes / n_ch,
+                       **traffic("select_prefill", sel_ms * 1e-3 / n_ch)},
+            "sparse_reuse_gather": {
+                "kernel": "hs2_sparse_attn_reuse (sparse_attn_kernel), one layer", "bound": "l2",
+                "achieved": sp_gbs, "peak": ceil_gbs, "unit": "GB/s", "frac": sp_gbs / ceil_gbs,
+                "algorithmic_bytes_per_launch": sp_bytes,
+                "peak_source": "measured: the same kernel with every query gathering the same 1152 rows "
+                               "(L2-resident), algorithmic bytes over its time",
+                "l2_resident_ms": ceil_ms,
+                **traffic("sparse_prefill", sp_ms * 1e-3)},
+        },
         "stages": {
             "full_attn_ms": fa_ms, "select_ms": sel_ms, "sparse_ms_per_layer": sp_ms,
             "sparse_reuse_queries_per_s": L / (sp_ms * 1e-3),
-            "sparse_reuse_gbs_algorithmic": sp_gbs, "sparse_reuse_hbm_frac": sp_gbs / HBM_PEAK_GBS,
-            "select_gbs_algorithmic": sel_gbs,
+            "sparse_reuse_gbs_algorithmic": sp_gbs, "select_gbs_algorithmic": sel_gbs,
             "wall_s_timed": wall,
         },
     }
 
     if not args.no_others:
         result["ablation_block_selection"] = ablation_blocks(hs2, q, k, v, qs, chunks, scale, ld, window, topk)
-        result["other_workloads"] = other_workloads(dev)
+        result["other_workloads"] = other_workloads(dev, rec, with_cpu=not args.no_cpu)
+        for name in ("decode_b16_32k", "decode_1m_fp8"):
+            w = result["other_workloads"][name]
+            result["rooflines"][name + "_full_attn"] = w["full_attn_roofline"]
 
     # ---------------------------------------------------------------- oracle sample (host cores)
     if not args.no_cpu:
         result["cpu_baseline"], result["sample_parity"] = cpu_baseline(
             args, inp, needles, step, keep_rows, idx, cnt, o_full, o_sp, L, H, scale, window, topk)
     print(json.dumps(result), flush=True)
+
+
+def gather_l2_ceiling(hs2, q2, k, v, idx, L, H, scale, max_sel):
+    """The sparse layer with every query gathering the last query's 1152 rows (1.2 MB:
+    L2-resident), median of 3 HIP-event times in ms: the rate this kernel reaches when
+    the gathers are served by L2."""
+    import numpy as np
+    import torch
+
+    idx_same = idx[:, L - 1: L].expand(1, L, max_sel).contiguous()
+    cnt_same = torch.full((1, L), max_sel, dtype=torch.int32, device=idx.device)
+    o = torch.empty_like(q2)
+    lse = torch.empty((1, L, H), dtype=torch.float32, device=idx.device)
+    t = []
+    for _ in range(4):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        hs2.hs2_sparse_attn_reuse(q2, k, v, idx_same, cnt_same, sm_scale=scale, o=o, lse=lse)
+        b.record()
+        torch.cuda.synchronize()
+        t.append(a.elapsed_time(b))
+    del idx_same, cnt_same, o, lse
+    torch.cuda.empty_cache()
+    return float(np.median(t[1:]))
 
 
 def ablation_blocks(hs2, q, k, v, qs, chunks, scale, ld, window, topk, block=64):
@@ -429,7 +562,7 @@ def ablation_blocks(hs2, q, k, v, qs, chunks, scale, ld, window, topk, block=64)
             "select_block_gbs_of_scores": read_bytes / (t_blk * 1e-3) / 1e9,
             "sparse_layer_token_ms": sp_tok, "sparse_layer_block_ms": sp_blk,
             "selected_keys_token": n_sel_tok, "selected_keys_block": n_sel_blk,
-            "note": "same scores, same 1024-token budget; block sums in float32 (pairwise tree)"}
+            "note": "same scores, same 1024-token budget; the kernel adds each block in float32 (pairwise tree)"}
 
 
 def _timed(run, stages: int, reps: int = 10, warm: int = 3, flush=None):
@@ -454,13 +587,58 @@ def _timed(run, stages: int, reps: int = 10, warm: int = 3, flush=None):
     return np.median(np.array(per), axis=0)
 
 
-def other_workloads(dev):
+def _traffic(rec, group, seconds_per_launch):
+    """Counter bytes per launch of a kernel group, their rate and its fraction of the HBM
+    peak ({"traffic": None} without a current record)."""
+    t = _rec_float(rec, group, "traffic_bytes_per_launch")
+    if t is None:
+        return {"traffic": None}
+    gbs = t / seconds_per_launch / 1e9
+    return {"traffic": t, "traffic_gbs": gbs, "traffic_hbm_frac": gbs / HBM_PEAK_GBS}
+
+
+def _threads_used() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        return 1
+
+
+def _oracle_decode(q, qs, k, v, T, p, ks=None, vs=None, b=0):
+    """The float64 oracle on one sequence's decode step (full attention, select, every
+    sparse layer), timed on the host; returns seconds (inputs decoded before timing)."""
+    import oracle
+    from token_level_sparse_full_amd import inputs
+
+    kind = inputs.kind_of(k)
+    k64 = oracle.decode_rows(inputs.raw_numpy(k[b]), kind, None if ks is None else inputs.raw_numpy(ks[b]))
+    v64 = oracle.decode_rows(inputs.raw_numpy(v[b]), kind, None if vs is None else inputs.raw_numpy(vs[b]))
+    q64 = oracle.decode_rows(inputs.raw_numpy(q[b]), "bf16")
+    q2 = [oracle.decode_rows(inputs.raw_numpy(x[b, 0]), "bf16") for x in qs]
+    t0 = time.perf_counter()
+    _, _, s = oracle.full_attn_scored(q64, k64, v64, p, 1.0 / 16)
+    sel, _, _ = oracle.select_topk_window(s[0], p)
+    for x in q2:
+        oracle.sparse_attn_reuse(x, k64, v64, sel, 1.0 / 16)
+    return time.perf_counter() - t0
+
+
+def _cpu_entry(value, unit, seconds, sample):
+    return {"value": value, "unit": unit, "cores": _threads_used(), "host_cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle", "sample": sample, "seconds": seconds}
+
+
+def other_workloads(dev, rec=None, with_cpu=True):
     """The decode and bridge workloads at their own sizes: HIP-event times of each stage
     (median of 10 after 3 warm-ups; a 512 MiB buffer write between reps pushes K/V out of
-    L2 and MALL) against the HBM (decode stages) or bf16 MFMA (bridge) roofline."""
+    L2 and MALL) against the HBM (decode stages) or bf16 MFMA (bridge) roofline, with the
+    counter traffic of the decode kernels and the oracle timed on a sample of each."""
     import torch
 
     from token_level_sparse_full_amd import hs2, inputs
+
+    rec = rec or {}
 
     out = {}
     junk = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -556,12 +734,24 @@ def other_workloads(dev):
     t_fa, t_sel, t_sp = decode_step(inp["q"], inp["q_sparse"], inp["k"], inp["v"], wl.T, wl.T - 1)
     kv_bytes = 2.0 * wl.B * wl.T * 512
     sp_bytes = wl.B * (ms * 2 * 512 + 2 * wl.H * D * 2 + ms * 4)
+    fa_gbs = kv_bytes / (t_fa * 1e-3) / 1e9
     out[wl.name] = {
         "ms_per_step": float(t_fa + t_sel + t_sp), "queries_per_s": wl.B / ((t_fa + t_sel + t_sp) * 1e-3),
-        "full_attn_ms": float(t_fa), "full_attn_hbm_frac": kv_bytes / (t_fa * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "full_attn_ms": float(t_fa), "full_attn_hbm_frac": fa_gbs / HBM_PEAK_GBS,
         "select_ms": float(t_sel), "sparse_ms_all_layers": float(t_sp),
-        "sparse_hbm_frac": wl.n_sparse * sp_bytes / (t_sp * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "sparse_gbs_algorithmic": wl.n_sparse * sp_bytes / (t_sp * 1e-3) / 1e9,
+        "full_attn_roofline": {"kernel": "hs2_full_attn_scored, decode path (stream, merge and score dispatches)",
+                               "bound": "hbm", "achieved": fa_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": fa_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": kv_bytes,
+                               **_traffic(rec, "full_attn_" + wl.name, t_fa * 1e-3)},
+        "select_counters": _traffic(rec, "select_" + wl.name, t_sel * 1e-3),
+        "sparse_counters": _traffic(rec, "sparse_" + wl.name, t_sp * 1e-3 / wl.n_sparse),
         "note": "cold: a 512 MiB write between reps; K/V 512 MiB per step"}
+    if with_cpu:
+        t_cpu = _oracle_decode(inp["q"], inp["q_sparse"], inp["k"], inp["v"], wl.T, wl.T - 1)
+        out[wl.name]["cpu_baseline"] = _cpu_entry(1.0 / t_cpu, "queries/s", t_cpu,
+                                                  f"1 of the {wl.B} sequences: full attention over {wl.T} keys, "
+                                                  f"select and {wl.n_sparse} sparse layers in float64")
     del inp
     torch.cuda.empty_cache()
 
@@ -579,11 +769,23 @@ def other_workloads(dev):
     t_sel = sum(x[1] for x in steps) / len(steps)
     t_sp = sum(x[2] for x in steps) / len(steps)
     kv_bytes = 2.0 * wl.T * (256 + 4)
+    fa_gbs = kv_bytes / (t_fa * 1e-3) / 1e9
     out[wl.name] = {
         "ms_per_step": float(t_fa + t_sel + t_sp), "queries_per_s": 1.0 / ((t_fa + t_sel + t_sp) * 1e-3),
-        "full_attn_ms": float(t_fa), "full_attn_hbm_frac": kv_bytes / (t_fa * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "full_attn_ms": float(t_fa), "full_attn_hbm_frac": fa_gbs / HBM_PEAK_GBS,
         "select_ms": float(t_sel), "sparse_ms_all_layers": float(t_sp),
+        "full_attn_roofline": {"kernel": "hs2_full_attn_scored, decode path (stream, merge and score dispatches)",
+                               "bound": "hbm", "achieved": fa_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": fa_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": kv_bytes,
+                               **_traffic(rec, "full_attn_" + wl.name, t_fa * 1e-3)},
+        "select_counters": _traffic(rec, "select_" + wl.name, t_sel * 1e-3),
+        "sparse_counters": _traffic(rec, "sparse_" + wl.name, t_sp * 1e-3 / wl.n_sparse),
         "note": "mean of the 4 steps (p = T-4 .. T-1); cold between reps"}
+    if with_cpu:
+        t_cpu = _oracle_decode(q, qs, k, v, wl.T, wl.T - 1, ks, vs)
+        out[wl.name]["cpu_baseline"] = _cpu_entry(1.0 / t_cpu, "queries/s", t_cpu,
+                                                  f"the last of the {wl.steps} steps: full attention over {wl.T} "
+                                                  f"e4m3 keys, select and {wl.n_sparse} sparse layers in float64")
     del k, v, ks, vs
     torch.cuda.empty_cache()
 
@@ -611,6 +813,24 @@ def other_workloads(dev):
         "bridge_mfma_frac": br_flop / (t_br * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
         "cross_decoder_step_ms": t_cross, "prefill_tokens_per_s": wl.L / ((t_br + t_cross) * 1e-3),
         "note": "bridge warm (inputs resident); the 4 bridged decode steps cold"}
+    if with_cpu:
+        import oracle
+        rows = torch.arange(0, wl.L, wl.L // 256, device=dev)
+        x64 = oracle.decode_rows(inputs.raw_numpy(br["x"][rows]), "bf16")
+        wk64 = oracle.decode_rows(inputs.raw_numpy(br["w_k"]), "bf16")
+        wv64 = oracle.decode_rows(inputs.raw_numpy(br["w_v"]), "bf16")
+        t0 = time.perf_counter()
+        oracle.bridge_kv_proj(x64, wk64, wv64)
+        t_proj = time.perf_counter() - t0
+        q = inputs.cast(inputs.normal((1, 1, wl.H, 256), inputs.STD_QKV, wl.seed, inputs.S_QFULL_LAYER, dev), "bf16")
+        qs = [inputs.cast(inputs.normal((1, 1, wl.H, 256), inputs.STD_QKV, wl.seed, inputs.S_QSPARSE + i, dev),
+                          "bf16") for i in range(wl.n_sparse)]
+        t_step = _oracle_decode(q, qs, k_all[0:1], v_all[0:1], wl.L, wl.L - 1)
+        out[wl.name]["cpu_baseline"] = _cpu_entry(
+            256 / t_proj, "bridged rows/s", t_proj + t_step,
+            f"256 of the {wl.L} rows through the {wl.n_full} layers' K and V projections in float64 "
+            f"({t_proj:.3f} s), and one bridged layer's decode step at p = {wl.L - 1} with its "
+            f"{wl.n_sparse} sparse layers ({t_step:.3f} s, {1.0 / t_step:.2f} steps/s)")
     out[wl.name + "_every_position"] = reading_b_entry(
         wl, t_br, *prefill_over_bridge(wl, k_all, v_all),
         "the cross-decoder at every prompt position: 4 full layers x (scored full attention over 65536 "
@@ -671,14 +891,20 @@ def cpu_baseline(args, inp, needles, step, keep_rows, idx, cnt, o_full, o_sp, L,
     o_np = o_full[0].float().cpu().numpy()
     osp_np = [t[0].float().cpu().numpy() for t in o_sp]
     worst = {"full_o": 0.0, "scores_rel": 0.0, "sparse_o": 0.0, "sel_swaps": 0, "needles_found": 0}
+    q_rows = {p: oracle.decode_rows(q_np[p:p + 1], "bf16") for p in rows}
+    qs_rows = {p: [oracle.decode_rows(qs_np[s][p], "bf16") for s in range(len(qs_np))] for p in rows}
+    # timed: the oracle's own path on each sampled row (full attention, select, every sparse layer)
+    res = {}
     t0 = time.perf_counter()
     for p in rows:
-        qrow = oracle.decode_rows(q_np[p:p + 1], "bf16")
-        o_ref, _, s_ref = oracle.full_attn_scored(qrow, k64, v64, p, scale)
+        o_ref, _, s_ref = oracle.full_attn_scored(q_rows[p], k64, v64, p, scale)
         sel, n, tau = oracle.select_topk_window(s_ref[0], p, window, topk)
-        o2_refs = [oracle.sparse_attn_reuse(oracle.decode_rows(qs_np[s][p], "bf16"), k64, v64, sel, scale)[0]
-                   for s in range(len(qs_np))]
-        # comparisons (not part of the timed oracle work: cheap)
+        o2 = [oracle.sparse_attn_reuse(x, k64, v64, sel, scale)[0] for x in qs_rows[p]]
+        res[p] = (o_ref, s_ref, sel, tau, o2)
+    t_cpu = time.perf_counter() - t0
+    # untimed: the GPU's results of the same rows against the oracle's
+    for p in rows:
+        o_ref, s_ref, sel, tau, _ = res[p]
         worst["full_o"] = max(worst["full_o"], float(np.abs(o_np[p] - o_ref[0]).max()))
         g = keep_rows[p].cpu().numpy().astype(np.float64)
         worst["scores_rel"] = max(worst["scores_rel"], float((np.abs(g - s_ref[0]) / s_ref[0]).max()))
@@ -689,24 +915,15 @@ def cpu_baseline(args, inp, needles, step, keep_rows, idx, cnt, o_full, o_sp, L,
         worst["sel_swaps"] += int(diff.size)
         # the sparse layers are compared on the GPU's own index set (stage-wise inputs)
         for s in range(len(qs_np)):
-            o2_on_gpu_set, _ = oracle.sparse_attn_reuse(oracle.decode_rows(qs_np[s][p], "bf16"), k64, v64, got, scale)
+            o2_on_gpu_set, _ = oracle.sparse_attn_reuse(qs_rows[p][s], k64, v64, got, scale)
             worst["sparse_o"] = max(worst["sparse_o"], float(np.abs(osp_np[s][p] - o2_on_gpu_set).max()))
-        del o2_refs
-    t_cpu = time.perf_counter() - t0
     for j, i in needles:
         worst["needles_found"] += int(np.isin(j, idx_np[i, : cnt_np[i]]))
     worst["needles"] = len(needles)
     worst["rows"] = len(rows)
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        blas_threads = 1
-    cores = min(len(os.sched_getaffinity(0)), blas_threads)
-    base = {"value": len(rows) / t_cpu, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(rows)} query rows of the same 128k sequence (64 needle targets + edge positions), "
-                      f"each through full attention + select + {len(qs_np)} sparse layers in float64",
-            "seconds": t_cpu}
+    base = _cpu_entry(len(rows) / t_cpu, "tokens/s", t_cpu,
+                      f"{len(rows)} query rows of the same 128k sequence (64 needle targets + edge positions), "
+                      f"each through full attention + select + {len(qs_np)} sparse layers in float64")
     return base, worst
 
 
