@@ -634,6 +634,7 @@ def other_workloads(dev, rec=None, with_cpu=True):
     (median of 10 after 3 warm-ups; a 512 MiB buffer write between reps pushes K/V out of
     L2 and MALL) against the HBM (decode stages) or bf16 MFMA (bridge) roofline, with the
     counter traffic of the decode kernels and the oracle timed on a sample of each."""
+    import numpy as np
     import torch
 
     from token_level_sparse_full_amd import hs2, inputs
@@ -787,6 +788,56 @@ def other_workloads(dev, rec=None, with_cpu=True):
                                                   f"the last of the {wl.steps} steps: full attention over {wl.T} "
                                                   f"e4m3 keys, select and {wl.n_sparse} sparse layers in float64")
     del k, v, ks, vs
+    torch.cuda.empty_cache()
+
+    # the self-decoder's sliding-window attention (window 128, 64-dim partial RoPE) over the 128k prompt
+    wl = inputs.WORKLOADS["self_decoder_swa_128k"]
+    inp = inputs.attention_inputs(B=1, n_q=wl.L, T=wl.L, H=wl.H, d=D, kv="bf16", n_sparse=0, seed=wl.seed, device=dev)
+    q_r, k_r = torch.empty_like(inp["q"]), torch.empty_like(inp["k"])
+    o_sw = torch.empty_like(inp["q"])
+    lse_sw = torch.empty((1, wl.L, wl.H), dtype=torch.float32, device=dev)
+
+    # the rotary embedding in place, as a serving cache turns its rows (only the 64 leading dims are
+    # read and written); repeating it across reps turns the rows further, which changes no timing
+    q_r.copy_(inp["q"])
+    k_r.copy_(inp["k"])
+
+    def run_swa(mark):
+        hs2.hs2_rope_partial(k_r[0], pos0=0, rope_dims=wl.rope_dims, rope_base=10000.0, out=k_r[0])
+        hs2.hs2_rope_partial(q_r[0], pos0=0, rope_dims=wl.rope_dims, rope_base=10000.0, out=q_r[0])
+        mark()
+        hs2.hs2_swa_attn(q_r, k_r, inp["v"], q_pos0=0, window=wl.window, sm_scale=scale, o=o_sw, lse=lse_sw)
+        mark()
+    t_rope, t_sw = _timed(run_swa, 2, flush=flush)
+    sw_bytes = wl.L * (2 * wl.H * D * 2 + 2 * D * 2 + wl.H * 4)     # Q and O, K and V rows, lse
+    rope_bytes = wl.L * (wl.H + 1) * wl.rope_dims * 2 * 2           # leading dims of Q and K rows, read and written
+    sw_flop = 4.0 * wl.H * D * sum(min(p + 1, wl.window) for p in range(wl.L))
+    sw_gbs = sw_bytes / (t_sw * 1e-3) / 1e9
+    out[wl.name] = {
+        "ms": float(t_rope + t_sw), "tokens_per_s": wl.L / ((t_rope + t_sw) * 1e-3),
+        "rope_ms": float(t_rope), "rope_gbs": rope_bytes / (t_rope * 1e-3) / 1e9, "attn_ms": float(t_sw),
+        "roofline": {"kernel": "hs2_swa_attn (swa_kernel)", "bound": "hbm", "achieved": sw_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": sw_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": sw_bytes,
+                     "mfma_tflops_algorithmic": sw_flop / (t_sw * 1e-3) / 1e12},
+        "note": "window 128, rope_dims 64, base 10000, H = 16, bf16: the rotary embedding of K and Q (in place), "
+                "then the attention; cold (512 MiB write between reps)"}
+    if with_cpu:
+        import oracle
+        rows = list(range(0, wl.L, wl.L // 64))
+        t_cpu = 0.0
+        for p in rows:
+            lo = max(0, p - wl.window + 1)
+            kk = np.zeros((p + 1, 256))
+            vv = np.zeros((p + 1, 256))
+            kk[lo:] = oracle.decode_rows(inputs.raw_numpy(inp["k"][0, lo: p + 1]), "bf16")
+            vv[lo:] = oracle.decode_rows(inputs.raw_numpy(inp["v"][0, lo: p + 1]), "bf16")
+            qq = oracle.decode_rows(inputs.raw_numpy(inp["q"][0, p: p + 1]), "bf16")
+            t0 = time.perf_counter()
+            oracle.swa_attn(qq, kk, vv, p, wl.window, wl.rope_dims, 10000.0, scale)
+            t_cpu += time.perf_counter() - t0
+        out[wl.name]["cpu_baseline"] = _cpu_entry(len(rows) / t_cpu, "tokens/s", t_cpu,
+                                                  f"{len(rows)} evenly spaced query rows of the 128k prompt in float64")
+    del inp, o_sw, lse_sw, q_r, k_r
     torch.cuda.empty_cache()
 
     # KV bridging: 4 projections of a 64k-token hidden state, then 4 bridged decode steps

@@ -239,6 +239,53 @@ int hs2_sparse_attn_reuse_noalloc(const void* q, int q_dtype, int B, int n_q, in
                                   void* o, float* lse, void* stream);
 
 /*
+ * hs2_rope_partial - rotary position embedding of the leading dims of bf16
+ * rows (the embedding of the self-decoder's SWA layers).
+ *
+ * Defines (HySparse2 pages: agihunt.info summary, model-shapes paragraph --
+ * SWA layers use a 64-dim partial RoPE, full and sparse layers none).  The
+ * pages give neither the base nor which dims rotate; this library takes the
+ * rotary embedding as first defined, on the leading dims: for the row of slot
+ * i (position t = pos0 + i) and m < rope_dims / 2,
+ *   y[2m]   = x[2m] cos a - x[2m+1] sin a
+ *   y[2m+1] = x[2m] sin a + x[2m+1] cos a,     a = t * rope_base^(-2m / rope_dims)
+ * and y[j] = x[j] for j >= rope_dims; results rounded to bf16 (RNE).
+ *
+ *   x, y  [n_pos, heads, d] bf16: every head of slot i sits at position pos0 + i
+ *         (heads = H for queries, 1 for K rows).  y == x turns the rows in place
+ *         (only the leading rope_dims dims are written); otherwise the two
+ *         must not overlap and y receives whole rows.
+ * Requires d == 256, n_pos >= 1, 1 <= heads <= 4096, n_pos * heads <= 2^40,
+ * pos0 >= 0, pos0 + n_pos <= 2^40, rope_dims a multiple of 8 in [0, 256],
+ * rope_base > 0 when rope_dims > 0.  A key is turned once, when it is written
+ * to the cache; hs2_swa_attn reads turned rows.
+ */
+int hs2_rope_partial(const void* x, void* y, int64_t n_pos, int heads, int d, int64_t pos0, int rope_dims,
+                     double rope_base, void* stream);
+
+/*
+ * hs2_swa_attn - the self-decoder's sliding-window attention (the layers that
+ * run before the prefill exits).
+ *
+ * Defines (HySparse2 pages: agihunt.info summary, backbone paragraph -- the
+ * self-decoder mixes full attention with SWA, where each query sees only a
+ * recent span of tokens; MQA, head dim 256).  The window length is not given;
+ * the window is the `window` most recent keys, the query's own included:
+ *   for sequence b, query i at position p = q_pos0 + i, head h:
+ *     l_j = sm_scale * <q[b,i,h,:], k[b,j,:]>,  j = max(0, p-window+1) .. p
+ *     o[b,i,h,:] = sum_j softmax_j(l) v[b,j,:],  lse[b,i,h] = log sum_j exp(l_j)
+ * with queries and keys already turned by hs2_rope_partial (queries at their
+ * positions, key j at position j), as the SWA layers use them.
+ *
+ *   q      [B, n_q, H, d]  bf16;  k, v [B, T, d] bf16
+ *   o      [B, n_q, H, d]  bf16, written;  lse [B, n_q, H] float32, may be NULL
+ * Requires d == 256, H in {1, 2, 4, 8, 16}, 0 <= q_pos0, q_pos0 + n_q <= T,
+ * window >= 1, sm_scale > 0.  No workspace.
+ */
+int hs2_swa_attn(const void* q, int B, int n_q, int H, int d, const void* k, const void* v, int64_t T,
+                 int64_t q_pos0, int window, float sm_scale, void* o, float* lse, void* stream);
+
+/*
  * hs2_bridge_kv_proj - KV Bridging re-projection.
  *
  * Defines (HySparse2 pages: agihunt.info summary, paragraph on the outer level

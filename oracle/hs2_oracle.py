@@ -463,18 +463,18 @@ def swa_attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos0: int, window: i
         sm_scale = 1.0 / math.sqrt(d)
     qpos = q_pos0 + np.arange(n_q)
     qr = rope_partial(np.swapaxes(q, 0, 1), qpos, rope_dims, base)       # [H, n_q, d]
-    last = q_pos0 + n_q - 1
-    kr = rope_partial(np.asarray(k, dtype=np.float64)[: last + 1], np.arange(last + 1), rope_dims, base)
-    v = np.asarray(v, dtype=np.float64)
+    first, last = max(0, q_pos0 - window + 1), q_pos0 + n_q - 1    # the keys some window reaches
+    kr = rope_partial(np.asarray(k, dtype=np.float64)[first: last + 1], np.arange(first, last + 1), rope_dims, base)
+    v = np.asarray(v, dtype=np.float64)[first: last + 1]
     o = np.zeros((n_q, H, d))
     lse = np.zeros((n_q, H))
     for i in range(n_q):
         p = q_pos0 + i
         lo = max(0, p - window + 1)
-        logits = sm_scale * (qr[:, i] @ kr[lo: p + 1].T)                 # [H, p+1-lo]
+        logits = sm_scale * (qr[:, i] @ kr[lo - first: p + 1 - first].T)   # [H, p+1-lo]
         m = logits.max(axis=1, keepdims=True)
         e = np.exp(logits - m)
         z = e.sum(axis=1, keepdims=True)
-        o[i] = (e / z) @ v[lo: p + 1]
+        o[i] = (e / z) @ v[lo - first: p + 1 - first]
         lse[i] = m[:, 0] + np.log(z[:, 0])
     return o, lse

@@ -19,7 +19,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = hs2.header_symbols()
-    assert len(names) == 15
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
 
@@ -259,3 +259,53 @@ def test_select_blocks_workspace_size(lib):
     assert lib.hs2_select_blocks_workspace_bytes(1, 4, 2048, 2000, 128, 64) == 512
     assert lib.hs2_select_blocks_workspace_bytes(1, 4, 2048, 0, 128, 64) == 0
     assert lib.hs2_select_blocks_workspace_bytes(1, 4, 2048, 2000, 128, 48) == 0
+
+
+def swa(lib, **kw):
+    a = dict(q=A, B=1, n_q=4, H=16, d=256, k=A, v=A, T=100, q0=96, w=128, sc=0.0625, o=A, lse=None)
+    a.update(kw)
+    return lib.hs2_swa_attn(a["q"], a["B"], a["n_q"], a["H"], a["d"], a["k"], a["v"], a["T"], a["q0"], a["w"],
+                            a["sc"], a["o"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), hs2.HS2_ERR_NULL),
+    (dict(o=None), hs2.HS2_ERR_NULL),
+    (dict(d=128), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(H=3), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(w=0), hs2.HS2_ERR_SHAPE),
+    (dict(sc=0.0), hs2.HS2_ERR_SHAPE),
+    (dict(q0=97), hs2.HS2_ERR_SHAPE),
+    (dict(q0=-1), hs2.HS2_ERR_SHAPE),
+    (dict(n_q=0), hs2.HS2_ERR_SHAPE),
+    (dict(k=MIS), hs2.HS2_ERR_ALIGN),
+    (dict(lse=A + 2), hs2.HS2_ERR_ALIGN),
+])
+def test_swa_rejects(lib, kw, code):
+    assert swa(lib, **kw) == code
+    assert lib.hs2_last_error().decode() != ""
+
+
+def rope(lib, **kw):
+    a = dict(x=A, y=A, n=4096, heads=16, d=256, pos0=0, rd=64, base=10000.0)
+    a.update(kw)
+    return lib.hs2_rope_partial(a["x"], a["y"], a["n"], a["heads"], a["d"], a["pos0"], a["rd"], a["base"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), hs2.HS2_ERR_NULL),
+    (dict(d=128), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(n=0), hs2.HS2_ERR_SHAPE),
+    (dict(heads=0), hs2.HS2_ERR_SHAPE),
+    (dict(pos0=-1), hs2.HS2_ERR_SHAPE),
+    (dict(pos0=(1 << 40) - 100), hs2.HS2_ERR_SHAPE),
+    (dict(rd=12), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(rd=264), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(base=0.0), hs2.HS2_ERR_SHAPE),
+    (dict(base=float("nan")), hs2.HS2_ERR_SHAPE),
+    (dict(y=A + 512 * 16), hs2.HS2_ERR_SHAPE),        # overlapping, not equal
+    (dict(y=MIS), hs2.HS2_ERR_ALIGN),
+])
+def test_rope_rejects(lib, kw, code):
+    assert rope(lib, **kw) == code
+    assert lib.hs2_last_error().decode() != ""

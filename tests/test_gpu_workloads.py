@@ -291,3 +291,30 @@ def test_bridge_64k_fp8_every_position():
         o2_ref, _ = oracle.sparse_attn_reuse(q264[r], k64, v64, idx_np[r, : cnt_np[r]], 1 / 16)
         parity.check_out(o2[0, int(i)], o2_ref, "e4m3", f"sparse row {p}")
     _check_select_rows(idx_np, cnt_np, s_rows, s_refs, [c0 + int(i) for i in qi])
+
+
+def test_self_decoder_swa_128k_sampled():
+    """The self-decoder's SWA layer over the 128k prompt (window 128, 64-dim
+    partial RoPE, base 10000), as bench.py launches it (the rotary embedding of
+    Q and K, then the attention): sampled query rows (the sequence start, the
+    window edge, the middle and the end) against the oracle."""
+    wl = inputs.WORKLOADS["self_decoder_swa_128k"]
+    say(wl.name)
+    L, H = wl.L, wl.H
+    inp = inputs.attention_inputs(B=1, n_q=L, T=L, H=H, d=256, kv="bf16", n_sparse=0, seed=wl.seed, device=DEV)
+    qr = hs2.hs2_rope_partial(inp["q"][0], pos0=0, rope_dims=wl.rope_dims, rope_base=10000.0)[None]
+    kr = hs2.hs2_rope_partial(inp["k"][0], pos0=0, rope_dims=wl.rope_dims, rope_base=10000.0)[None]
+    o, lse = hs2.hs2_swa_attn(qr, kr, inp["v"], q_pos0=0, window=wl.window, sm_scale=1 / 16)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    rows = sorted({0, 1, 126, 127, 128, 129, 4095, L // 2, L - 2, L - 1} | set(rng.integers(0, L, 22).tolist()))
+    for p in rows:
+        lo = max(0, p - wl.window + 1)
+        k64 = np.zeros((p + 1, 256))
+        v64 = np.zeros((p + 1, 256))
+        k64[lo:] = parity.decode(inp["k"][0, lo: p + 1])
+        v64[lo:] = parity.decode(inp["v"][0, lo: p + 1])
+        o_ref, lse_ref = oracle.swa_attn(parity.decode(inp["q"][0, p: p + 1]), k64, v64, p, wl.window, wl.rope_dims,
+                                         10000.0, 1 / 16)
+        parity.check_out(o[0, p: p + 1], o_ref, "bf16", f"o row {p}")
+        parity.check_lse(lse[0, p: p + 1], lse_ref)

@@ -87,10 +87,13 @@ MUTATIONS = [
     ("rope base fixed", "freq = base ** (-2.0 * m / rope_dims)", "freq = 10000.0 ** (-2.0 * m / rope_dims)"),
     ("swa window one long", "lo = max(0, p - window + 1)", "lo = max(0, p - window)"),
     ("swa window one short", "lo = max(0, p - window + 1)", "lo = max(0, p - window + 2)"),
-    ("swa keys not rotated", "kr = rope_partial(np.asarray(k, dtype=np.float64)[: last + 1], np.arange(last + 1), "
-     "rope_dims, base)", "kr = np.asarray(k, dtype=np.float64)[: last + 1]"),
+    ("swa keys not rotated", "kr = rope_partial(np.asarray(k, dtype=np.float64)[first: last + 1], "
+     "np.arange(first, last + 1), rope_dims, base)", "kr = np.asarray(k, dtype=np.float64)[first: last + 1]"),
+    ("swa keys rotated from position 0", "np.arange(first, last + 1), rope_dims, base)",
+     "np.arange(0, last + 1 - first), rope_dims, base)"),
     ("swa queries rotated by index", "qpos = q_pos0 + np.arange(n_q)", "qpos = np.arange(n_q)"),
-    ("swa values from the rotated keys", "o[i] = (e / z) @ v[lo: p + 1]", "o[i] = (e / z) @ kr[lo: p + 1]"),
+    ("swa values from the rotated keys", "o[i] = (e / z) @ v[lo - first: p + 1 - first]",
+     "o[i] = (e / z) @ kr[lo - first: p + 1 - first]"),
     ("block tokens past the candidates", "toks = [np.arange(b * block, min(n_cand, (b + 1) * block)",
      "toks = [np.arange(b * block, min(n, (b + 1) * block)"),
 ]

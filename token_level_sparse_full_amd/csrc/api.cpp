@@ -264,6 +264,47 @@ int hs2_sparse_attn_reuse_noalloc(const void* q, int q_dtype, int B, int n_q, in
                     "hs2_sparse_attn_reuse_noalloc");
 }
 
+int hs2_rope_partial(const void* x, void* y, int64_t n_pos, int heads, int d, int64_t pos0, int rope_dims,
+                     double rope_base, void* stream) {
+  if (!x || !y) return fail(HS2_ERR_NULL, "x and y are required");
+  if (d != HS2_HEAD_DIM) return fail(HS2_ERR_UNSUPPORTED, "row width %d unsupported (only %d)", d, HS2_HEAD_DIM);
+  constexpr int64_t kMax = (int64_t)1 << 40;
+  if (n_pos < 1 || n_pos > kMax || heads < 1 || heads > 4096 || n_pos * heads > kMax)
+    return fail(HS2_ERR_SHAPE, "need 1 <= n_pos, 1 <= heads <= 4096, n_pos * heads <= 2^40");
+  if (pos0 < 0 || pos0 > kMax - n_pos) return fail(HS2_ERR_SHAPE, "need 0 <= pos0 and pos0 + n_pos <= 2^40");
+  if (rope_dims < 0 || rope_dims > HS2_HEAD_DIM || rope_dims % 8 != 0)
+    return fail(HS2_ERR_UNSUPPORTED, "rope_dims must be a multiple of 8 in [0, %d]", HS2_HEAD_DIM);
+  if (rope_dims > 0 && !(rope_base > 0.0 && std::isfinite(rope_base)))
+    return fail(HS2_ERR_SHAPE, "rope_base must be finite and > 0");
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(HS2_ERR_ALIGN, "x and y must be 16-byte aligned");
+  const uintptr_t bytes = (uintptr_t)(n_pos * heads) * 512;
+  const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)y;
+  if (xa != ya && xa < ya + bytes && ya < xa + bytes)
+    return fail(HS2_ERR_SHAPE, "x and y overlap without being equal");
+  hs2::RopeParams p{};
+  p.x = x; p.y = y; p.n_rows = n_pos * heads; p.heads = heads; p.pos0 = pos0; p.rope_dims = rope_dims;
+  return hip_status(hs2::launch_rope(p, rope_base, (hipStream_t)stream), "hs2_rope_partial");
+}
+
+int hs2_swa_attn(const void* q, int B, int n_q, int H, int d, const void* k, const void* v, int64_t T, int64_t q_pos0,
+                 int window, float sm_scale, void* o, float* lse, void* stream) {
+  if (!q || !k || !v || !o) return fail(HS2_ERR_NULL, "q, k, v and o are required");
+  if (d != HS2_HEAD_DIM) return fail(HS2_ERR_UNSUPPORTED, "head dim %d unsupported (only %d)", d, HS2_HEAD_DIM);
+  if (!heads_ok(H)) return fail(HS2_ERR_UNSUPPORTED, "H=%d unsupported (1, 2, 4, 8 or 16)", H);
+  if (!rows_ok(B, n_q, T)) return fail(HS2_ERR_SHAPE, "need B, n_q, T >= 1, B*n_q and T inside int32");
+  if (!positions_ok(q_pos0, n_q, T)) return fail(HS2_ERR_SHAPE, "need 0 <= q_pos0 and q_pos0 + n_q <= T");
+  if (window < 1) return fail(HS2_ERR_SHAPE, "window must be >= 1");
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(HS2_ERR_SHAPE, "sm_scale must be finite and > 0");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(HS2_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(HS2_ERR_ALIGN, "lse must be 4-byte aligned");
+  hs2::SwaParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.B = B; p.n_q = n_q; p.H = H; p.T = T; p.q_pos0 = q_pos0; p.window = window;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  return hip_status(hs2::launch_swa(p, (hipStream_t)stream), "hs2_swa_attn");
+}
+
 size_t hs2_bridge_workspace_bytes(int n_layers, int D, int d) { return hs2::bridge_workspace_bytes(n_layers, D, d); }
 
 int hs2_bridge_kv_proj(const void* x, int64_t L, int D, const void* w_k, const void* w_v, int n_layers, int d,

@@ -83,6 +83,33 @@ size_t attn_workspace_bytes(int B, int n_q, int H, int64_t T, int kv_kind);
 hipError_t launch_full_attn(const AttnParams& p, int q_kind, int kv_kind, void* ws, size_t ws_bytes,
                             hipStream_t stream);
 
+// self-decoder sliding-window attention (bf16; queries and keys already turned)
+struct SwaParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, n_q, H;
+  int64_t T, q_pos0;
+  int window;
+  float scale_log2;        // sm_scale * log2(e)
+};
+hipError_t launch_swa(const SwaParams& p, hipStream_t stream);
+
+// partial rotary embedding of bf16 rows of 256: row r sits at position
+// pos0 + r / heads; x == y turns the leading dims in place
+struct RopeParams {
+  const void* x;
+  void* y;
+  int64_t n_rows;
+  int heads;
+  int64_t pos0;
+  int rope_dims;           // a multiple of 8 in [0, 256]
+  double rev[128];         // filled by launch_rope: pair m turns rev[m] revolutions per position
+};
+hipError_t launch_rope(RopeParams p, double rope_base, hipStream_t stream);
+
 struct BridgeParams {
   const void* x;
   const void* w_k;

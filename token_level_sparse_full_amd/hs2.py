@@ -40,6 +40,8 @@ _PROTOS = {
     "hs2_bridge_kv_proj": (_i, [_vp, _i64, _i, _vp, _vp, _i, _i, _vp, _vp, _i64, _vp, _sz, _vp]),
     "hs2_bridge_workspace_bytes": (_sz, [_i, _i, _i]),
     "hs2_bridge_kv_proj_fp8": (_i, [_vp, _i64, _i, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _sz, _vp]),
+    "hs2_rope_partial": (_i, [_vp, _vp, _i64, _i, _i, _i64, _i, ctypes.c_double, _vp]),
+    "hs2_swa_attn": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _i64, _i64, _i, _f, _vp, _vp, _vp]),
     "hs2_status_str": (ctypes.c_char_p, [_i]),
     "hs2_last_error": (ctypes.c_char_p, []),
     "hs2_version": (_i, []),
@@ -212,6 +214,37 @@ def hs2_sparse_attn_reuse_noalloc(q, k, v, idx, count, *, sm_scale: float | None
                                              _dtype_code(k), _ptr(k_scale), _ptr(v_scale), T, _ptr(idx),
                                              _ptr(count), max_sel, sm_scale, _ptr(o), _ptr(lse), _stream(stream))
     check("hs2_sparse_attn_reuse_noalloc", rc)
+    return o, lse
+
+
+def hs2_rope_partial(x, *, pos0: int, rope_dims: int = 64, rope_base: float = 10000.0, out=None, stream=None):
+    """Partial rotary embedding of bf16 rows x [n_pos, heads, 256] (or [n_pos, 256]); slot i at position
+    pos0 + i.  out=x turns in place; returns the turned rows."""
+    n_pos = x.shape[0]
+    heads = x.shape[1] if x.dim() == 3 else 1
+    d = x.shape[-1]
+    if out is None:
+        out = torch.empty_like(x)
+    rc = lib().hs2_rope_partial(_ptr(x), _ptr(out), n_pos, heads, d, pos0, rope_dims, rope_base, _stream(stream))
+    check("hs2_rope_partial", rc)
+    return out
+
+
+def hs2_swa_attn(q, k, v, *, q_pos0: int, window: int = 128, sm_scale: float | None = None, o=None, lse=None,
+                 stream=None, want_lse: bool = True):
+    """Sliding-window attention on turned queries and keys.  q [B,n_q,H,256] bf16; k, v [B,T,256] bf16;
+    returns (o, lse)."""
+    B, n_q, H, d = q.shape
+    T = k.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, n_q, H), dtype=torch.float32, device=q.device)
+    rc = lib().hs2_swa_attn(_ptr(q), B, n_q, H, d, _ptr(k), _ptr(v), T, q_pos0, window, sm_scale, _ptr(o), _ptr(lse),
+                            _stream(stream))
+    check("hs2_swa_attn", rc)
     return o, lse
 
 

@@ -42,7 +42,7 @@ S_NEEDLES = 7
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "prefill" | "decode" | "bridge"
+    kind: str            # "prefill" | "decode" | "bridge" | "swa"
     seed: int
     H: int = 16
     d: int = 256
@@ -55,6 +55,8 @@ class Workload:
     steps: int = 1       # decode steps (consecutive positions at the end of the cache)
     D: int = 0           # bridge hidden size
     n_full: int = 0      # bridged full layers
+    window: int = 0      # sliding window (self-decoder SWA layer)
+    rope_dims: int = 0   # leading dims turned by the rotary embedding (SWA layer)
 
 
 WORKLOADS = {
@@ -65,6 +67,7 @@ WORKLOADS = {
         Workload("prefill_128k", "prefill", seed=3, L=131072, n_sparse=2, needles=64),
         Workload("bridge_64k", "bridge", seed=4, L=65536, D=2048, n_full=4, n_sparse=8),
         Workload("decode_1m_fp8", "decode", seed=5, T=1 << 20, kv="e4m3", steps=4, n_sparse=4),
+        Workload("self_decoder_swa_128k", "swa", seed=6, L=131072, n_sparse=0, window=128, rope_dims=64),
     ]
 }
 
