@@ -67,12 +67,12 @@ GROUPS = {
     "select_prefill": ("prefill", ["select_kernel"], ["select.hip"], "chunks"),
     "sparse_prefill": ("prefill_sparse", ["sparse_attn_kernel"], ["sparse_reuse.hip", "attn_tile.hpp"], 1),
     "full_attn_decode_b16_32k": ("decode_b16_32k", ["decode_stream_kernel", "decode_merge_kernel",
-                                                    "decode_score_kernel"], ["attn_decode.hip", "attn_tile.hpp"], 1),
+                                                    "decode_merge_score_kernel"], ["attn_decode.hip", "attn_tile.hpp"], 1),
     "select_decode_b16_32k": ("decode_b16_32k", ["select_kernel", "mb_"], ["select.hip"], 1),
     "sparse_decode_b16_32k": ("decode_b16_32k", ["sparse_attn_kernel", "sparse_merge_kernel"],
                               ["sparse_reuse.hip", "attn_tile.hpp"], 3),
     "full_attn_decode_1m_fp8": ("decode_1m_fp8", ["decode_stream_kernel", "decode_merge_kernel",
-                                                  "decode_score_kernel"], ["attn_decode.hip", "attn_tile.hpp"], 1),
+                                                  "decode_merge_score_kernel"], ["attn_decode.hip", "attn_tile.hpp"], 1),
     "select_decode_1m_fp8": ("decode_1m_fp8", ["select_kernel", "mb_"], ["select.hip"], 1),
     "sparse_decode_1m_fp8": ("decode_1m_fp8", ["sparse_attn_kernel", "sparse_merge_kernel"],
                              ["sparse_reuse.hip", "attn_tile.hpp"], 4),

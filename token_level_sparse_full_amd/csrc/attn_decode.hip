@@ -5,13 +5,16 @@
 // sparse layers), computed as a split over keys because one decode row has
 // little work per key and the K/V stream (512 MiB at 1M FP8 tokens) must run
 // at HBM speed:
-//   split   : grid (key chunks, sequences); each workgroup computes the
-//             float32 logits of its keys (kept in the workspace, log2 units),
-//             and a partial softmax state (max, sum, unnormalised O) per row;
-//   merge   : a tree of workgroups merges the partial states (32 per
-//             workgroup and level) into O, lse (and lse in log2 units for the
-//             next kernel);
-//   score   : one thread per key, s_j = sum_h exp2(x_hj - lse2_h) per query.
+//   split        : grid (key chunks, sequences); each workgroup computes the
+//                  float32 logits of its keys (kept in the workspace, log2
+//                  units), and a partial softmax state (max, sum, unnormalised
+//                  O) per row;
+//   merge        : while more than 32 states per row are left, a tree level of
+//                  workgroups merges them, 32 at a time;
+//   merge+score  : one launch finishes: some workgroups merge the last states
+//                  into O and lse, the others derive the final lse of every row
+//                  from the same states and write the scores of a key range,
+//                  s_j = sum_h exp2(x_hj - lse2_h).
 // No atomics: every partial has its own slot, so results are deterministic.
 #include "attn_tile.hpp"
 #include "hs2_internal.hpp"
@@ -34,7 +37,6 @@ struct DecodeWs {
   float* mid_m;   // [B][nmid][16]       partial states after one merge level
   float* mid_z;   // [B][nmid][16]
   float* mid_o;   // [B][nmid][16][256]
-  float* lse2;    // [B][16]
   int chunk, nch, nmid;
 };
 constexpr int kMergeFan = 32;   // partial states merged per workgroup and level
@@ -66,7 +68,6 @@ size_t decode_ws_layout(int B, int64_t T, char* base, DecodeWs* ws) {
   w.mid_m = take((size_t)B * nmid * 16 * 4);
   w.mid_z = take((size_t)B * nmid * 16 * 4);
   w.mid_o = take((size_t)B * nmid * 16 * 256 * 4);
-  w.lse2 = take((size_t)B * 16 * 4);
   w.chunk = ch;
   w.nch = (int)nch;
   w.nmid = (int)nmid;
@@ -434,10 +435,9 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_stream_kernel(const Attn
   }
 }
 
-// Merge of partial softmax states (m, z, unnormalised O) over key chunks, as
-// a tree: workgroup (g, row, b) merges the states g*F .. g*F+F-1 of one row
-// (thread = head dim).  Intermediate levels write merged states; the last
-// level (one output state) writes O, lse and lse2.  The order of the sums is
+// One level of the merge of partial softmax states (m, z, unnormalised O)
+// over key chunks: workgroup (g, row, b) merges the states g*F .. g*F+F-1 of
+// one row (thread = head dim) into one state.  The order of the sums is
 // fixed, so results are deterministic.
 struct MergeIO {
   const float* in_m;
@@ -449,7 +449,6 @@ struct MergeIO {
   int in_stride, nin, out_stride;   // states per sequence in the layouts; valid inputs
 };
 
-template <int QKIND, bool FINAL>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const AttnParams p, const DecodeWs ws, const MergeIO io) {
   const int g = blockIdx.x, row = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
   const int c0 = g * kMergeFan, c1 = min(io.nin, c0 + kMergeFan);
@@ -478,46 +477,110 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const AttnParams p, c
     Z += ok ? zc[i] * f : 0.f;
     acc += ok ? oc[i] * f : 0.f;
   }
-  if constexpr (FINAL) {
-    const int R = gridDim.y;
+  const int64_t ob = ((int64_t)b * io.out_stride + g) * 16 + row;
+  io.out_o[ob * kHeadDim + d] = acc;
+  if (d == 0) {
+    io.out_m[ob] = M;
+    io.out_z[ob] = Z;
+  }
+}
+
+// The last merge level and the scores in one launch (at most kMergeFan states
+// per row are left).  Workgroups [0, B * R) merge the O of one (sequence, row)
+// (thread = head dim, every load issued up front); the others score a range
+// of keys after deriving the final lse of every row themselves from the same
+// states' (max, sum) pairs, so no workgroup waits for another.  The sums run
+// over the states in order: deterministic.
+constexpr int MS_KEYS = 2048;   // keys scored per workgroup
+
+template <int QKIND, int H>
+__global__ __launch_bounds__(256) void decode_merge_score_kernel(const AttnParams p, const DecodeWs ws,
+                                                                 const MergeIO io) {
+  const int R = p.n_q * H;
+  const int n_merge = p.B * R;
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x < n_merge) {
+    const int b = blockIdx.x / R, row = blockIdx.x % R, d = tid;
+    const int64_t ib = (int64_t)b * io.in_stride;
+    float mc[kMergeFan], zc[kMergeFan], oc[kMergeFan];
+    float M = kNegInf;
+#pragma unroll
+    for (int i = 0; i < kMergeFan; ++i) {
+      const int64_t c = ib + min(i, io.nin - 1);
+      mc[i] = io.in_m[c * 16 + row];
+      zc[i] = io.in_z[c * 16 + row];
+      oc[i] = io.in_o[(c * 16 + row) * kHeadDim + d];
+    }
+#pragma unroll
+    for (int i = 0; i < kMergeFan; ++i) {
+      if (i >= io.nin) mc[i] = kNegInf;
+      M = fmaxf(M, mc[i]);
+    }
+    float Z = 0.f, acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMergeFan; ++i) {
+      const bool ok = mc[i] != kNegInf;   // a selected 0 adds exactly; masked terms may hold any bits
+      const float f = fast_exp2(mc[i] - M);
+      Z += ok ? zc[i] * f : 0.f;
+      acc += ok ? oc[i] * f : 0.f;
+    }
     const int64_t oi = ((int64_t)b * R + row) * kHeadDim + d;
     const float out = acc / Z;
     if constexpr (QKIND == KV_F32)
       ((float*)p.o)[oi] = out;
     else
       ((bf16*)p.o)[oi] = to_bf16(out);
-    if (d == 0) {
-      const float l2 = M + fast_log2(Z);
-      ws.lse2[b * 16 + row] = l2;
-      if (p.lse) p.lse[(int64_t)b * R + row] = l2 * kLn2;
-    }
-  } else {
-    const int64_t ob = ((int64_t)b * io.out_stride + g) * 16 + row;
-    io.out_o[ob * kHeadDim + d] = acc;
-    if (d == 0) {
-      io.out_m[ob] = M;
-      io.out_z[ob] = Z;
-    }
+    if (d == 0 && p.lse) p.lse[(int64_t)b * R + row] = (M + fast_log2(Z)) * kLn2;
+    return;
   }
-}
-
-template <int H>
-__global__ __launch_bounds__(256) void decode_score_kernel(const AttnParams p, const DecodeWs ws) {
-  const int b = blockIdx.y;
-  const int64_t key = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  // ---- scores of keys [key0, key0 + MS_KEYS) of one sequence
   const int64_t n_keys = p.q_pos0 + p.n_q;
-  if (key >= n_keys) return;
-  const float* x = ws.logits + ((int64_t)b * p.T + key) * 16;
-  const f32x4 x0 = *(const f32x4*)x, x1 = *(const f32x4*)(x + 4), x2 = *(const f32x4*)(x + 8), x3 = *(const f32x4*)(x + 12);
-  const float xs[16] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3],
-                        x2[0], x2[1], x2[2], x2[3], x3[0], x3[1], x3[2], x3[3]};
-  const float* l2 = ws.lse2 + b * 16;
-  for (int i = 0; i < p.n_q; ++i) {
-    if (key > p.q_pos0 + i) continue;
-    float s = 0.f;
+  const int nblk = (int)((n_keys + MS_KEYS - 1) / MS_KEYS);
+  const int sb = blockIdx.x - n_merge;
+  const int b = sb / nblk;
+  const int64_t key0 = (int64_t)(sb % nblk) * MS_KEYS;
+  __shared__ float l2s[16];
+  if (tid < 16) {
+    float l2 = 0.f;
+    if (tid < R) {
+      const int64_t ib = (int64_t)b * io.in_stride;
+      float mc[kMergeFan], zc[kMergeFan];
+      float M = kNegInf;
 #pragma unroll
-    for (int h = 0; h < H; ++h) s += fast_exp2(xs[(i * H + h) & 15] - l2[(i * H + h) & 15]);
-    p.scores[((int64_t)b * p.n_q + i) * p.ld_scores + key] = s;
+      for (int i = 0; i < kMergeFan; ++i) {
+        const int64_t c = ib + min(i, io.nin - 1);
+        mc[i] = io.in_m[c * 16 + tid];
+        zc[i] = io.in_z[c * 16 + tid];
+      }
+#pragma unroll
+      for (int i = 0; i < kMergeFan; ++i) {
+        if (i >= io.nin) mc[i] = kNegInf;
+        M = fmaxf(M, mc[i]);
+      }
+      float Z = 0.f;
+#pragma unroll
+      for (int i = 0; i < kMergeFan; ++i) Z += mc[i] != kNegInf ? zc[i] * fast_exp2(mc[i] - M) : 0.f;
+      l2 = M + fast_log2(Z);
+    }
+    l2s[tid] = l2;
+  }
+  __syncthreads();
+  float l2[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) l2[r] = l2s[r];
+  for (int64_t key = key0 + tid; key < min(n_keys, key0 + MS_KEYS); key += 256) {
+    const float* x = ws.logits + ((int64_t)b * p.T + key) * 16;
+    const f32x4 x0 = *(const f32x4*)x, x1 = *(const f32x4*)(x + 4), x2 = *(const f32x4*)(x + 8),
+                x3 = *(const f32x4*)(x + 12);
+    const float xs[16] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3],
+                          x2[0], x2[1], x2[2], x2[3], x3[0], x3[1], x3[2], x3[3]};
+    for (int i = 0; i < p.n_q; ++i) {
+      if (key > p.q_pos0 + i) continue;
+      float s = 0.f;
+#pragma unroll
+      for (int h = 0; h < H; ++h) s += fast_exp2(xs[(i * H + h) & 15] - l2[(i * H + h) & 15]);
+      p.scores[((int64_t)b * p.n_q + i) * p.ld_scores + key] = s;
+    }
   }
 }
 
@@ -530,11 +593,12 @@ hipError_t launch_decode_h(const AttnParams& p, const DecodeWs& ws, hipStream_t 
   else
     hipLaunchKernelGGL((decode_stream_kernel<KV, H>), dim3(nch, p.B), dim3(DC_THREADS), 0, stream, p, ws);
   const int R = p.n_q * p.H;
-  // merge tree over the chunk states: part -> mid -> part -> ... -> final
+  // merge tree over the chunk states while more than kMergeFan are left:
+  // part -> mid -> part -> ...; the last level and the scores share one launch
   MergeIO io{ws.part_m, ws.part_z, ws.part_o, ws.mid_m, ws.mid_z, ws.mid_o, ws.nch, (int)nch, ws.nmid};
   while (io.nin > kMergeFan) {
     const int nout = (io.nin + kMergeFan - 1) / kMergeFan;
-    hipLaunchKernelGGL((decode_merge_kernel<KV_BF16, false>), dim3(nout, R, p.B), dim3(256), 0, stream, p, ws, io);
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(nout, R, p.B), dim3(256), 0, stream, p, ws, io);
     const bool to_mid = io.out_m == ws.mid_m;
     io.in_m = io.out_m;
     io.in_z = io.out_z;
@@ -546,11 +610,12 @@ hipError_t launch_decode_h(const AttnParams& p, const DecodeWs& ws, hipStream_t 
     io.out_o = to_mid ? ws.part_o : ws.mid_o;
     io.out_stride = to_mid ? ws.nch : ws.nmid;
   }
+  const int nblk = (int)((n_keys + MS_KEYS - 1) / MS_KEYS);
+  const dim3 grid((unsigned)(p.B * R + p.B * nblk));
   if (KV == KV_F32)
-    hipLaunchKernelGGL((decode_merge_kernel<KV_F32, true>), dim3(1, R, p.B), dim3(256), 0, stream, p, ws, io);
+    hipLaunchKernelGGL((decode_merge_score_kernel<KV_F32, H>), grid, dim3(256), 0, stream, p, ws, io);
   else
-    hipLaunchKernelGGL((decode_merge_kernel<KV_BF16, true>), dim3(1, R, p.B), dim3(256), 0, stream, p, ws, io);
-  hipLaunchKernelGGL((decode_score_kernel<H>), dim3((unsigned)((n_keys + 255) / 256), p.B), dim3(256), 0, stream, p, ws);
+    hipLaunchKernelGGL((decode_merge_score_kernel<KV_BF16, H>), grid, dim3(256), 0, stream, p, ws, io);
   return hipGetLastError();
 }
 
