@@ -58,21 +58,33 @@ constexpr int PB_AHEAD = 3;                     // operand prefetch distance (MF
 //    result needs before a VALU, LDS or memory instruction may read it.
 // Back-to-back MFMAs on the same accumulator need none.  LDS loads feeding the
 // operands are covered by the compiler's s_waitcnt insertion (it sees asm uses).
+// The other direction matters too: an XDL op keeps reading its A and B
+// registers after it issues, so nothing may overwrite them right away (a VALU
+// write one instruction after the MFMA has been seen to corrupt S).  For the
+// compiler an asm operand is dead once the asm has issued, so each MFMA takes
+// the operands of the MFMA before it as unused inputs (ka, kb): they stay
+// allocated until this one issues, at least one full MFMA (32 cycles) later.
+// tests/test_asm_hazards.py checks the compiled code for both directions.
 __device__ __forceinline__ void mfma32v_first(f32x16& acc, bf16x8 a, bf16x8 b) {
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void mfma32v(f32x16& acc, bf16x8 a, bf16x8 b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+__device__ __forceinline__ void mfma32v_first(f32x16& acc, bf16x8 a, bf16x8 b, bf16x8 ka) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b), "v"(ka));
 }
-// last step of two chains sharing the B operand, then the read-after-write wait
-__device__ __forceinline__ void mfma32v_last2(f32x16& acc0, f32x16& acc1, bf16x8 a0, bf16x8 a1, bf16x8 b) {
+__device__ __forceinline__ void mfma32v(f32x16& acc, bf16x8 a, bf16x8 b, bf16x8 ka, bf16x8 kb) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b), "v"(ka), "v"(kb));
+}
+// last step of two chains sharing the B operand, then the read-after-write
+// wait (which also covers the operand reads of both)
+__device__ __forceinline__ void mfma32v_last2(f32x16& acc0, f32x16& acc1, bf16x8 a0, bf16x8 a1, bf16x8 b, bf16x8 ka,
+                                              bf16x8 kb) {
   asm volatile(
       "s_nop 2\n\t"
       "v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\t"
       "v_mfma_f32_32x32x16_bf16 %1, %3, %4, %1\n\t"
       "s_nop 7\n\ts_nop 7\n\ts_nop 3"
       : "+v"(acc0), "+v"(acc1)
-      : "v"(a0), "v"(a1), "v"(b));
+      : "v"(a0), "v"(a1), "v"(b), "v"(ka), "v"(kb));
 }
 
 template <int H, int PHASE>   // PHASE 1: prefill_lse, PHASE 2: prefill_pv
@@ -308,12 +320,14 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
       __builtin_amdgcn_sched_barrier(0);
   #pragma unroll
       for (int s = 0; s < 16; ++s) {
+        // the A chain keeps the previous step's B-chain operands alive, the B
+        // chain those of the A chain before it
         if (s == 15) {
-          mfma32v_last2(sa.v[0], sa.v[1], qf[s], q1op(s), kf[s]);
+          mfma32v_last2(sa.v[0], sa.v[1], qf[s], q1op(s), kf[s], q1op(s - 1), kf[s - 1]);
         } else {
-          if (s == 0) mfma32v_first(sa.v[0], qf[s], kf[s]); else mfma32v(sa.v[0], qf[s], kf[s]);
+          if (s == 0) mfma32v_first(sa.v[0], qf[s], kf[s]); else mfma32v(sa.v[0], qf[s], kf[s], q1op(s - 1), kf[s - 1]);
           if (s + PB_AHEAD < 16) kf[s + PB_AHEAD] = kfrag(kb, s + PB_AHEAD);
-          if (s == 0) mfma32v_first(sa.v[1], q1op(s), kf[s]); else mfma32v(sa.v[1], q1op(s), kf[s]);
+          if (s == 0) mfma32v_first(sa.v[1], q1op(s), kf[s], qf[s]); else mfma32v(sa.v[1], q1op(s), kf[s], qf[s], kf[s]);
           if constexpr (!QREG) {
             if (s + PB_AHEAD < 16) q1[s + PB_AHEAD] = q1frag(s + PB_AHEAD);
           }
@@ -479,25 +493,22 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
         store_scores(sa, kt, sc);
       }
     };
-    // Start of tile kt: K(kt) and V(kt-1) have landed; P(kt-1) is read into
-    // registers before the DMA of K(kt+1) and V(kt) is issued, so that these
-    // LDS reads need no wait on that DMA.
-    auto sync_tile = [&](bf16x8 (&pa)[2][2], bool read_p) __attribute__((always_inline)) {
+    // Start of tile kt: K(kt) and V(kt-1) have landed.  P(kt-1) is already in
+    // registers: the P buffer is the wave's own, so it is read at the end of
+    // the previous tile, before the barrier, and its read latency stays off
+    // the path from the barrier to the first MFMA.
+    auto sync_tile = [&]() __attribute__((always_inline)) {
       wait_dma();
       __syncthreads();
-      if (read_p) {
-        read_pa(pbuf, pa);
-        __builtin_amdgcn_sched_barrier(0);
-      }
     };
+    bf16x8 pa[2][2];
     // The DMA of K(kt+1) (zeros past the last tile) and of V(kt) both go in
     // the S steps, one instruction of each every third step: a CU moves about
     // 46 bytes per clock into LDS, and a burst would stall the issuing wave.
     // Issued this early, V(kt) has landed by the next wait (issuing it in the
     // PV steps left about 0.4 k cycles of that wait per tile).
     auto iter = [&](int kt, const char* kc, char* kn, const char* vp, char* vn, auto masked) __attribute__((always_inline)) {
-      bf16x8 pa[2][2];
-      sync_tile(pa, true);
+      sync_tile();
       const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kg, kt + 1), rv = tile_rsrc(vg, kt);
       Pair sa = s_rows_keys(kc, [&](int st) __attribute__((always_inline)) {
         if (st % 3 == 0 && st < 15) dma_one(rk, kn, koff, st / 3);
@@ -509,13 +520,14 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
       float sc[2][2];
       pv_probs(pa, vp, sa, kt, pbuf, sc, masked, std::true_type{}, [](int) {});
       finish_scores(sa, kt, sc);
+      read_pa(pbuf, pa);   // P(kt), for the next tile
     };
     // first tile is never preceded by a PV block
     const int t_mask = (int)((pos_first + 1) / PB_KT);   // tiles >= t_mask need the causal mask
     dma(kg, 0, lds_k0, koff);
     {
       bf16x8 none[2][2] = {};
-      sync_tile(none, false);
+      sync_tile();
       if (ntiles > 1) dma(kg, 1, lds_k1, koff);
       dma(vg, 0, lds_v0, voff);
       Pair sa = s_rows_keys(lds_k0, [](int) {});
@@ -525,6 +537,7 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
       else
         pv_probs(none, lds_v0, sa, 0, pbuf, sc, std::false_type{}, std::false_type{}, [](int) {});
       finish_scores(sa, 0, sc);
+      read_pa(pbuf, pa);
     }
     {
       int kt = 1;
@@ -548,11 +561,7 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
     wait_dma();
     __syncthreads();
     if constexpr (H >= 8) store_scores(Pair{}, ntiles - 1, sc_prev);
-    {
-      bf16x8 pa[2][2];
-      read_pa(pbuf, pa);
-      pv_only(pa, ((ntiles - 1) & 1) ? lds_v1 : lds_v0);
-    }
+    pv_only(pa, ((ntiles - 1) & 1) ? lds_v1 : lds_v0);
 
     // ---- outputs: lane holds O[32mt + 8(r/4) + 4hb + r%4][32n + l32]
   #pragma unroll
