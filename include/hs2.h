@@ -99,7 +99,10 @@ int hs2_full_attn_scored(const void* q, int q_dtype, int B, int n_q, int H, int 
  *     partial softmax states of the key chunks (about B * T * 64 bytes);
  *   bf16 prefill: the lse of every row in log2 units (B * n_q * H * 4 bytes),
  *     written by the lse pass and read by the probability pass;
- *   float32 and FP8 prefill: none (0).
+ *   FP8 prefill: the same lse, plus the cache widened to bf16 codes
+ *     (2 * B * T * 512 bytes: every e4m3 value is exact in bf16), on which the
+ *     bf16 kernels then run with the row scales applied per key;
+ *   float32 prefill: none (0).
  * The contents are scratch; calls that share a workspace must not overlap. */
 size_t hs2_full_attn_workspace_bytes(int B, int n_q, int H, int64_t T, int kv_dtype);
 

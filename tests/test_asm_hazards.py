@@ -37,12 +37,13 @@ def prefill_asm(tmp_path_factory):
 
 def test_every_head_count_is_compiled(prefill_asm):
     names = [n for n in prefill_asm if "prefill_bf16_kernel" in n]
-    assert len(names) == 10, names   # H in {1, 2, 4, 8, 16} x two passes
+    assert len(names) == 20, names   # H in {1, 2, 4, 8, 16} x two passes x (bf16, scaled e4m3)
 
 
+@pytest.mark.parametrize("scaled", [0, 1])
 @pytest.mark.parametrize("H", [1, 2, 4, 8, 16])
-def test_pv_pass_asm_mfma_hazards(prefill_asm, H):
-    name = [n for n in prefill_asm if f"prefill_bf16_kernelILi{H}ELi2E" in n]
+def test_pv_pass_asm_mfma_hazards(prefill_asm, H, scaled):
+    name = [n for n in prefill_asm if f"prefill_bf16_kernelILi{H}ELi2ELb{scaled}E" in n]
     assert len(name) == 1
     bad = asm_hazards.violations(prefill_asm[name[0]])
     assert not bad, "\n".join(bad[:10])

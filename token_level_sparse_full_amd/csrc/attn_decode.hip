@@ -214,7 +214,9 @@ constexpr int DS_STEP = 16;
 constexpr int DS_VPITCH = 272;                       // bf16 elements per staged V row (544 B)
 constexpr int DS_VTILE = DS_STEP * DS_VPITCH * 2;    // 8704 B per wave
 constexpr int DS_RED = (DC_WAVES * 16 * kRedPitch + 2 * DC_WAVES * 16) * 4;
-constexpr int DS_SMEM = DC_WAVES * DS_VTILE > DS_RED ? DC_WAVES * DS_VTILE : DS_RED;
+constexpr int DS_LGT = DS_STEP * 16 * 4;               // 1 KB: one step's logits [key][row] per wave
+constexpr int DS_LOOP = DC_WAVES * (DS_VTILE + DS_LGT);  // V tiles, then logits tiles
+constexpr int DS_SMEM = DS_LOOP > DS_RED ? DS_LOOP : DS_RED;
 
 template <int KV>
 struct DsRegs {
@@ -255,6 +257,7 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_stream_kernel(const Attn
   const char* vseq = (const char*)p.v + kv_row0 * ROWB;
   float* lg = ws.logits + kv_row0 * 16;
   bf16* vt = (bf16*)(smem + wave * DS_VTILE);
+  float* lgt = (float*)(smem + DC_WAVES * DS_VTILE + wave * DS_LGT);
 
   QFrag qf;
   load_qfrag<KV>((const char*)p.q + ((int64_t)b * R + c16) * kHeadDim * 2, row_ok, g, qf);
@@ -295,8 +298,13 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_stream_kernel(const Attn
       }
     }
   };
-  // logits of the wave's keys through a buffer resource that ends at its last
-  // key: stores past it are dropped (rows >= R hold unused slots)
+  // Logits of the wave's keys through a buffer resource that ends at its last
+  // key: stores past it are dropped (rows >= R hold unused slots).  A lane
+  // holds 4 keys of one row; written as they are, every 128-byte line of the
+  // [key][16] layout would be half-written by two store instructions, which
+  // cost a plain K/V stream a quarter of its rate on the box (80 -> 108 us at
+  // 16 x 32k keys).  So a step's 16 x 16 logits go through the wave's 1 KB LDS
+  // tile and out as one contiguous 16-byte-per-lane store.
   const __amdgpu_buffer_rsrc_t lg_rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(lg + key0 * 16), 0, (int)(max((int64_t)0, key1 - key0) * 64), 0x00020000);
   // V rows of the step -> the wave's LDS tile (bf16, row pitch DS_VPITCH)
@@ -341,10 +349,13 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_stream_kernel(const Attn
       float v = acc[i] * p.scale_log2;
       if constexpr (KV == KV_E4M3) v *= r.ks[i];
       v = (key < kw1 && key <= row_pos) ? v : kNegInf;
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), lg_rs, (int)(((key - key0) * 16 + c16) * 4), 0, 0);
+      lgt[(4 * g + i) * 16 + c16] = v;
       x[i] = v;
       tmax = fmaxf(tmax, v);
     }
+    // the wave's own tile: LDS keeps its writes and this read in order
+    const u32x4 lg4 = *(const u32x4*)(lgt + 4 * l);
+    __builtin_amdgcn_raw_buffer_store_b128(lg4, lg_rs, (int)((kb - key0) * 64 + 16 * l), 0, 0);
     tmax = fmaxf(tmax, shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, shfl_xor(tmax, 32));
     const float m_new = fmaxf(m_run, tmax);
@@ -376,6 +387,10 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_stream_kernel(const Attn
 
   // K (and the scales) double-buffered in registers; the one set of V
   // registers is refilled with the next step's rows as soon as they are in LDS.
+  // (Deeper buffering -- two V sets, or three K sets and two V sets with e4m3
+  // rows -- measured no faster: the steady state already streams at about
+  // 6.4 TB/s; the time above that goes to the first step's fill and to the
+  // spread of the waves' finishing times.)
   DsRegs<KV> r0, r1;
   DsVRegs<KV> vr;
   if (nst > 0) {
@@ -633,12 +648,13 @@ hipError_t launch_decode_kv(const AttnParams& p, const DecodeWs& ws, hipStream_t
 }  // namespace
 
 hipError_t launch_prefill(const AttnParams& p, int kv_kind, void* ws, hipStream_t stream);  // attn_prefill.hip
-size_t prefill_bf16_workspace_bytes(int B, int n_q, int H);                         // attn_prefill_bf16.hip
+size_t prefill_bf16_workspace_bytes(int B, int n_q, int H, int64_t T, bool e4m3);   // attn_prefill_bf16.hip
 
 bool attn_uses_decode(int n_q, int H) { return (int64_t)n_q * H <= 16; }
 
 size_t attn_workspace_bytes(int B, int n_q, int H, int64_t T, int kv_kind) {
-  if (!attn_uses_decode(n_q, H)) return kv_kind == KV_BF16 ? prefill_bf16_workspace_bytes(B, n_q, H) : 0;
+  if (!attn_uses_decode(n_q, H))
+    return kv_kind == KV_F32 ? 0 : prefill_bf16_workspace_bytes(B, n_q, H, T, kv_kind == KV_E4M3);
   return decode_ws_layout(B, T, nullptr, nullptr);
 }
 

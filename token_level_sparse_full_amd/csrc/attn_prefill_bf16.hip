@@ -23,6 +23,7 @@
 // sees that reads of one buffer do not depend on the DMA into another.  Every
 // K or V fragment read from LDS feeds two 32-row MFMA tiles, which halves the
 // LDS bytes per MFMA flop against 32-row waves.
+#include <algorithm>
 #include <type_traits>
 
 #include "hs2_device.hpp"
@@ -87,8 +88,13 @@ __device__ __forceinline__ void mfma32v_last2(f32x16& acc0, f32x16& acc1, bf16x8
       : "v"(a0), "v"(a1), "v"(b), "v"(ka), "v"(kb));
 }
 
-template <int H, int PHASE>   // PHASE 1: prefill_lse, PHASE 2: prefill_pv
-__global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_kernel(const AttnParams p, float* lse2) {
+// PHASE 1: prefill_lse, PHASE 2: prefill_pv.  SC: the K and V rows come with
+// per-row float32 scales (an e4m3 cache widened to bf16 codes): a logit is
+// S * (scale * k_scale[key]) and P is multiplied by v_scale[key] before it is
+// rounded to bf16 for the PV product, the arithmetic of the e4m3 path of
+// attn_prefill.hip; each tile's scales ride along with its K or V DMA.
+template <int H, int PHASE, bool SC>
+__global__ __launch_bounds__(PB_THREADS, (PHASE == 1 && !SC) ? 2 : 1) void prefill_bf16_kernel(const AttnParams p, float* lse2) {
   constexpr int TPW = PB_RW / H;       // tokens per wave
   constexpr int TPB = PB_WAVES * TPW;  // tokens per workgroup
 
@@ -158,6 +164,15 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
     for (int i = 0; i < 5; ++i) dma_one(rs, buf, off, i);
   };
   auto wait_dma = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+  // the 32 row scales of tile kt (zeros past the last key) -> sc[0..31], by
+  // one DMA instruction of 4 bytes per lane (lanes 32..63 land in sc[32..63],
+  // never read)
+  auto dma_scales = [&](const float* src, int kt, float* sc) __attribute__((always_inline)) {
+    const int64_t rows = max((int64_t)0, min((int64_t)PB_KT, n_keys - (int64_t)kt * PB_KT));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(src + (int64_t)b * p.T + (int64_t)kt * PB_KT), 0, (int)(rows * 4), 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void HS2_LDS*)sc, 4, (uint32_t)(4 * l), 0, 0, 0);
+  };
   // K fragment for K-step s: key l32 of the tile, dims 16s + 8hb .. +7
   const int kofs = l32 * (PB_KC * 16) + 16 * hb;
   auto kfrag = [&](const char* buf, int s) -> bf16x8 { return as_bf16x8(*(const u32x4*)(buf + kofs + 32 * s)); };
@@ -169,6 +184,7 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
   if constexpr (PHASE == 1) {
     // =============================== prefill_lse ===============================
     __shared__ __attribute__((aligned(1024))) char lds_k0[PB_KTILE], lds_k1[PB_KTILE], lds_k2[PB_KTILE];
+    __shared__ __attribute__((aligned(16))) float lds_ks[SC ? 3 : 1][64];   // K row scales of each buffer
     bf16x8 qf[2][16];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -179,8 +195,39 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
     // Online max / sum of one tile (lane: rows l32 and 32 + l32, keys kt*32 +
     // 8(r/4) + 4hb + r%4).  Tiles left of the diagonal need no causal mask:
     // that path is the bulk of the work, so it is kept free of selects.
-    auto lse_update = [&](Pair& st, int kt, bool masked) __attribute__((always_inline)) {
+    auto lse_update = [&](Pair& st, int kt, bool masked, const float* ksc) __attribute__((always_inline)) {
       const int kbase = kt * PB_KT;
+      if constexpr (SC) {
+        // x = S * (scale * k_scale[key]): keys 8q + 4hb + j of the tile, one
+        // group of 4 scales at a time
+        float tmax[2] = {kNegInf, kNegInf};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          __builtin_amdgcn_sched_barrier(0);   // one group of scales live at a time
+          const f32x4 c4 = *(const f32x4*)(ksc + 8 * q + 4 * hb);
+#pragma unroll
+          for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int r = 4 * q + j;
+              float x = st.v[n][r] * (p.scale_log2 * c4[j]);
+              if (masked) x = (kbase + 8 * q + 4 * hb + j <= my_pos[n]) ? x : kNegInf;
+              st.v[n][r] = x;
+              tmax[n] = fmaxf(tmax[n], x);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const float m_new = fmaxf(m_run[n], tmax[n]);
+          const float m_use = m_new == kNegInf ? 0.f : m_new;   // all masked so far: every term is 0
+          float acc = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc += fast_exp2(st.v[n][r] - m_use);
+          z_run[n] = z_run[n] * fast_exp2(m_run[n] - m_use) + acc;
+          m_run[n] = m_new;
+        }
+        return;
+      }
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         if (!masked) {
@@ -219,9 +266,10 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
     // 0, 4 for the others) outstanding.  The batch is spread over the first
     // ten MFMA steps (one instruction every second step): issued that early
     // it has landed by the wait two tiles later.
-    auto step1 = [&](int kt, const char* kc, char* kd) __attribute__((always_inline)) {
-      if (wv == 0) __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5)
-      else __builtin_amdgcn_s_waitcnt(0x0F74);           // vmcnt(4)
+    auto step1 = [&](int kt, const char* kc, char* kd, const float* ksc, float* ksd) __attribute__((always_inline)) {
+      // wave 1 also carries the tile's scale DMA (SC)
+      if (wv == 0 || (SC && wv == 1)) __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5)
+      else __builtin_amdgcn_s_waitcnt(0x0F74);                                // vmcnt(4)
       __syncthreads();
       const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kg, kt + 2);
       Pair st;
@@ -235,21 +283,36 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
         if (s + PB_AHEAD < 16) kf[s + PB_AHEAD] = kfrag(kc, s + PB_AHEAD);
         st.v[1] = mfma32(kf[s], qf[1][s], s == 0 ? f32x16{} : st.v[1]);
         if (s % 2 == 0 && s < 10) dma_one(rk, kd, koff, s / 2);
+        if constexpr (SC) {
+          if (s == 10 && wv == 1) dma_scales(p.k_scale, kt + 2, ksd);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
-      lse_update(st, kt, (int64_t)kt * PB_KT + PB_KT - 1 > pos_first);
+      __builtin_amdgcn_sched_barrier(0);
+      lse_update(st, kt, (int64_t)kt * PB_KT + PB_KT - 1 > pos_first, ksc);
     };
+    float* ks0 = lds_ks[0];
+    float* ks1 = lds_ks[SC ? 1 : 0];
+    float* ks2 = lds_ks[SC ? 2 : 0];
+    // issue order per wave: K(0) [, scales(0)], K(1) [, scales(1)], so that
+    // the first wait (all but the last batch) covers tile 0 and its scales
     dma(kg, 0, lds_k0, koff);
+    if constexpr (SC) {
+      if (wv == 1) dma_scales(p.k_scale, 0, ks0);
+    }
     dma(kg, 1, lds_k1, koff);
+    if constexpr (SC) {
+      if (wv == 1) dma_scales(p.k_scale, 1, ks1);
+    }
     {
       int kt = 0;
       for (; kt + 2 < ntiles; kt += 3) {
-        step1(kt, lds_k0, lds_k2);
-        step1(kt + 1, lds_k1, lds_k0);
-        step1(kt + 2, lds_k2, lds_k1);
+        step1(kt, lds_k0, lds_k2, ks0, ks2);
+        step1(kt + 1, lds_k1, lds_k0, ks1, ks0);
+        step1(kt + 2, lds_k2, lds_k1, ks2, ks1);
       }
-      if (kt < ntiles) step1(kt, lds_k0, lds_k2);
-      if (kt + 1 < ntiles) step1(kt + 1, lds_k1, lds_k0);
+      if (kt < ntiles) step1(kt, lds_k0, lds_k2, ks0, ks2);
+      if (kt + 1 < ntiles) step1(kt + 1, lds_k1, lds_k0, ks1, ks0);
       wait_dma();   // the zero-filling DMA past the last tile
     }
 #pragma unroll
@@ -270,6 +333,7 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
     __shared__ __attribute__((aligned(1024))) char lds_v0[PB_VTILE], lds_v1[PB_VTILE];
     __shared__ __attribute__((aligned(16))) char lds_p[PB_WAVES * PB_KT * PB_PP];
     __shared__ __attribute__((aligned(16))) float lds_lse[PB_WAVES * PB_RW];
+    __shared__ __attribute__((aligned(16))) float lds_ksc[SC ? 2 : 1][64], lds_vsc[SC ? 2 : 1][64];   // by tile parity
     char* const pbuf = lds_p + wave * PB_KT * PB_PP;
     float* const lse_lds = lds_lse + wave * PB_RW;
     // With H = 16 all 64 query rows of the wave stay in registers (128 VGPRs),
@@ -418,6 +482,12 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
       constexpr bool do_pv = decltype(with_pv)::value;
       const int64_t key = (int64_t)kt * PB_KT + l32;
       auto lse4 = [&](int g) { return *(const f32x4*)(lse_lds + 32 * (g >> 2) + 8 * (g & 3) + 4 * hb); };
+      // logit factor of this lane's key, and its V scale (SC)
+      float cl = p.scale_log2, vsl = 1.f;
+      if constexpr (SC) {
+        cl = p.scale_log2 * lds_ksc[kt & 1][l32];
+        vsl = lds_vsc[kt & 1][l32];
+      }
       bf16x8 bv[16];
       if constexpr (do_pv) {
   #pragma unroll
@@ -437,7 +507,7 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
   #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           const int j = 2 * (st & 1) + jj, r = 4 * q + j;
-          const float e = fast_exp2(sa.v[mt][r] * p.scale_log2 - lcur[j]);
+          const float e = fast_exp2(sa.v[mt][r] * cl - lcur[j]);
           if constexpr (need_mask)
             sa.v[mt][r] = key <= pos_of_row(32 * mt + 8 * q + 4 * hb + j) ? e : 0.f;
           else
@@ -445,10 +515,17 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
         }
         if (st & 1) {
           bf16x4 v4;
-          v4[0] = to_bf16(sa.v[mt][4 * q]);
-          v4[1] = to_bf16(sa.v[mt][4 * q + 1]);
-          v4[2] = to_bf16(sa.v[mt][4 * q + 2]);
-          v4[3] = to_bf16(sa.v[mt][4 * q + 3]);
+          if constexpr (SC) {
+            v4[0] = to_bf16(sa.v[mt][4 * q] * vsl);
+            v4[1] = to_bf16(sa.v[mt][4 * q + 1] * vsl);
+            v4[2] = to_bf16(sa.v[mt][4 * q + 2] * vsl);
+            v4[3] = to_bf16(sa.v[mt][4 * q + 3] * vsl);
+          } else {
+            v4[0] = to_bf16(sa.v[mt][4 * q]);
+            v4[1] = to_bf16(sa.v[mt][4 * q + 1]);
+            v4[2] = to_bf16(sa.v[mt][4 * q + 2]);
+            v4[3] = to_bf16(sa.v[mt][4 * q + 3]);
+          }
           *(bf16x4*)(pb + l32 * PB_PP + (32 * mt + 8 * q + 4 * hb) * 2) = v4;
           lcur = lnext;
           if (g + 2 < 8) lnext = lse4(g + 2);
@@ -513,6 +590,12 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
       Pair sa = s_rows_keys(kc, [&](int st) __attribute__((always_inline)) {
         if (st % 3 == 0 && st < 15) dma_one(rk, kn, koff, st / 3);
         if (st % 3 == 1 && st < 14) dma_one(rv, vn, voff, st / 3);
+        if constexpr (SC) {
+          // the scales of tile kt + 1, used by its probabilities in the next
+          // iteration (after that iteration's wait and barrier)
+          if (st == 14 && wv == 1) dma_scales(p.k_scale, kt + 1, lds_ksc[SC ? ((kt + 1) & 1) : 0]);
+          if (st == 14 && wv == 2) dma_scales(p.v_scale, kt + 1, lds_vsc[SC ? ((kt + 1) & 1) : 0]);
+        }
         if constexpr (H >= 8) {
           if (st == 14) store_scores(Pair{}, kt - 1, sc_prev);
         }
@@ -525,11 +608,19 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
     // first tile is never preceded by a PV block
     const int t_mask = (int)((pos_first + 1) / PB_KT);   // tiles >= t_mask need the causal mask
     dma(kg, 0, lds_k0, koff);
+    if constexpr (SC) {
+      if (wv == 1) dma_scales(p.k_scale, 0, lds_ksc[0]);
+      if (wv == 2) dma_scales(p.v_scale, 0, lds_vsc[0]);
+    }
     {
       bf16x8 none[2][2] = {};
       sync_tile();
       if (ntiles > 1) dma(kg, 1, lds_k1, koff);
       dma(vg, 0, lds_v0, voff);
+      if constexpr (SC) {
+        if (wv == 1) dma_scales(p.k_scale, 1, lds_ksc[SC ? 1 : 0]);
+        if (wv == 2) dma_scales(p.v_scale, 1, lds_vsc[SC ? 1 : 0]);
+      }
       Pair sa = s_rows_keys(lds_k0, [](int) {});
       float sc[2][2];
       if (t_mask == 0)
@@ -579,28 +670,57 @@ __global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_k
 
 }  // namespace
 
-size_t prefill_bf16_workspace_bytes(int B, int n_q, int H) {
-  return ((size_t)B * n_q * H * 4 + 255) & ~(size_t)255;   // lse of every row, log2 units
+// workspace: the lse of every row (log2 units); with an e4m3 cache also the
+// cache widened to bf16 codes, K then V, [B][T][256] each
+size_t prefill_bf16_workspace_bytes(int B, int n_q, int H, int64_t T, bool e4m3) {
+  const size_t lse = ((size_t)B * n_q * H * 4 + 255) & ~(size_t)255;
+  return e4m3 ? lse + 2 * (size_t)B * T * 512 : lse;
 }
 
-template <int H>
+// e4m3 codes -> bf16 codes (exact: every e4m3 value is a bf16 value), 16 per thread
+__global__ __launch_bounds__(256) void widen_e4m3_kernel(const uint32_t* src, bf16* dst, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) {
+    const u32x4 c = __builtin_nontemporal_load((const u32x4*)src + i);
+    *(bf16x8*)(dst + 16 * i) = e4m3x8_to_bf16(c[0], c[1]);
+    *(bf16x8*)(dst + 16 * i + 8) = e4m3x8_to_bf16(c[2], c[3]);
+  }
+}
+
+template <int H, bool SC>
 hipError_t launch_prefill_bf16_h(const AttnParams& p, float* lse2, hipStream_t stream) {
   const int tpb = PB_WAVES * PB_RW / H;
   const unsigned nblk = (unsigned)(p.B * ((p.n_q + tpb - 1) / tpb));
-  hipLaunchKernelGGL((prefill_bf16_kernel<H, 1>), dim3(nblk), dim3(PB_THREADS), 0, stream, p, lse2);
-  hipLaunchKernelGGL((prefill_bf16_kernel<H, 2>), dim3(nblk), dim3(PB_THREADS), 0, stream, p, lse2);
+  hipLaunchKernelGGL((prefill_bf16_kernel<H, 1, SC>), dim3(nblk), dim3(PB_THREADS), 0, stream, p, lse2);
+  hipLaunchKernelGGL((prefill_bf16_kernel<H, 2, SC>), dim3(nblk), dim3(PB_THREADS), 0, stream, p, lse2);
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_bf16(const AttnParams& p, void* ws, hipStream_t stream) {
-  float* lse2 = (float*)ws;
+template <bool SC>
+hipError_t launch_prefill_bf16_sc(const AttnParams& p, float* lse2, hipStream_t stream) {
   switch (p.H) {
-    case 1: return launch_prefill_bf16_h<1>(p, lse2, stream);
-    case 2: return launch_prefill_bf16_h<2>(p, lse2, stream);
-    case 4: return launch_prefill_bf16_h<4>(p, lse2, stream);
-    case 8: return launch_prefill_bf16_h<8>(p, lse2, stream);
-    default: return launch_prefill_bf16_h<16>(p, lse2, stream);
+    case 1: return launch_prefill_bf16_h<1, SC>(p, lse2, stream);
+    case 2: return launch_prefill_bf16_h<2, SC>(p, lse2, stream);
+    case 4: return launch_prefill_bf16_h<4, SC>(p, lse2, stream);
+    case 8: return launch_prefill_bf16_h<8, SC>(p, lse2, stream);
+    default: return launch_prefill_bf16_h<16, SC>(p, lse2, stream);
   }
+}
+
+hipError_t launch_prefill_bf16(const AttnParams& p, void* ws, hipStream_t stream, bool e4m3) {
+  float* lse2 = (float*)ws;
+  if (!e4m3) return launch_prefill_bf16_sc<false>(p, lse2, stream);
+  // widen the e4m3 cache into the workspace, then run the bf16 passes on it
+  const size_t lse_bytes = prefill_bf16_workspace_bytes(p.B, p.n_q, p.H, p.T, false);
+  bf16* kw = (bf16*)((char*)ws + lse_bytes);
+  bf16* vw = kw + (size_t)p.B * p.T * 256;
+  const int64_t n16 = (int64_t)p.B * p.T * 16;
+  const unsigned grid = (unsigned)std::min<int64_t>((n16 + 255) / 256, 8192);
+  hipLaunchKernelGGL(widen_e4m3_kernel, dim3(grid), dim3(256), 0, stream, (const uint32_t*)p.k, kw, n16);
+  hipLaunchKernelGGL(widen_e4m3_kernel, dim3(grid), dim3(256), 0, stream, (const uint32_t*)p.v, vw, n16);
+  AttnParams q = p;
+  q.k = kw;
+  q.v = vw;
+  return launch_prefill_bf16_sc<true>(q, lse2, stream);
 }
 
 }  // namespace hs2
