@@ -55,7 +55,6 @@ int main(void) {
     for (int b = 0; b < NI; ++b)
       for (int c = 0; c < NI; ++c) {
         acc += hs2_sparse_workspace_bytes(INTS[a], INTS[b], INTS[c] % 17, INTS[c]);
-        acc += hs2_bridge_workspace_bytes(INTS[a], INTS[b], INTS[c]);
         for (int t = 0; t < N64; ++t) {
           acc += hs2_full_attn_workspace_bytes(INTS[a], INTS[b], INTS[c] % 17, I64S[t], c % 4);
           acc += hs2_select_workspace_bytes(INTS[a], INTS[b], I64S[t], I64S[(t + c) % N64]);
@@ -78,10 +77,20 @@ int main(void) {
   expect("sparse: max_sel 0", hs2_sparse_attn_reuse(FAKE, HS2_BF16, 1, 1, 16, 256, FAKE, FAKE, HS2_BF16, NULL, NULL,
                                                     100, FAKE, FAKE, 0, 0.0625f, FAKE, NULL, FAKE, 1 << 30, NULL),
          HS2_ERR_SHAPE);
-  expect("bridge: D=16", hs2_bridge_kv_proj(FAKE, 4096, 16, FAKE, FAKE, 4, 256, FAKE, FAKE, 4096 * 256, NULL, 0, NULL),
+  expect("noalloc: too many pieces", hs2_sparse_attn_reuse_noalloc(FAKE, HS2_BF16, 64, 1, 16, 256, FAKE, FAKE,
+                                                                    HS2_BF16, NULL, NULL, 100000, FAKE, FAKE, 4096,
+                                                                    0.0625f, FAKE, FAKE, NULL),
+         HS2_ERR_WORKSPACE);
+  expect("swa: window 0", hs2_swa_attn(FAKE, 1, 16, 16, 256, FAKE, FAKE, 100, 50, 0, 0.0625f, FAKE, FAKE, NULL),
+         HS2_ERR_SHAPE);
+  expect("rope: dims not a multiple of 8", hs2_rope_partial(FAKE, FAKE, 100, 16, 256, 0, 60, 10000.0, NULL),
+         HS2_ERR_UNSUPPORTED);
+  expect("rope: overlapping x and y", hs2_rope_partial(FAKE, (char*)FAKE + 512, 100, 16, 256, 0, 64, 10000.0, NULL),
+         HS2_ERR_SHAPE);
+  expect("bridge: D=16", hs2_bridge_kv_proj(FAKE, 4096, 16, FAKE, FAKE, 4, 256, FAKE, FAKE, 4096 * 256, NULL),
          HS2_ERR_SHAPE);
   expect("bridge8: null scale", hs2_bridge_kv_proj_fp8(FAKE, 4096, 2048, FAKE, FAKE, 4, 256, FAKE, FAKE, NULL, FAKE,
-                                                       4096 * 256, 4096, NULL, 0, NULL), HS2_ERR_NULL);
+                                                       4096 * 256, 4096, NULL), HS2_ERR_NULL);
 
   /* ---- sweeps: every call returns a status (an argument error, or HS2_ERR_HIP
    * where the arguments are valid: no device) and leaves no sanitizer report */
@@ -100,6 +109,20 @@ int main(void) {
           expect_status(buf, hs2_sparse_attn_reuse(FAKE, HS2_F32, nq, INTS[(a + 3) % NI], H, 256, FAKE, FAKE,
                                                    HS2_F32, NULL, NULL, T, FAKE, FAKE, (int)(q0 & 0x7FFFFFFF),
                                                    0.0625f, FAKE, FAKE, FAKE, (size_t)1 << 40, NULL));
+          expect_status("noalloc", hs2_sparse_attn_reuse_noalloc(FAKE, HS2_BF16, 1, nq, H, 256, FAKE, FAKE,
+                                                                 HS2_FP8E4M3, FAKE, FAKE, T, FAKE, FAKE,
+                                                                 (int)(q0 & 0x7FFFFFFF), 0.0625f, FAKE, FAKE, NULL));
+          expect_status("swa", hs2_swa_attn(FAKE, INTS[(a + 5) % NI], nq, H, 256, FAKE, FAKE, T, q0,
+                                            INTS[(t + u) % NI], 0.0625f, FAKE, FAKE, NULL));
+          {
+            /* rope_dims 0 in place has nothing to do: that valid call returns HS2_OK without a launch */
+            const int rd = INTS[(a + t) % NI];
+            const int rc = hs2_rope_partial(FAKE, FAKE, T, H, 256, q0, rd, 10000.0, NULL);
+            if (rd == 0 && rc == HS2_OK)
+              ++n_checked;
+            else
+              expect_status("rope", rc);
+          }
         }
         for (int w = 0; w < NI; w += 5) {
           expect_status(buf, hs2_select_topk_window(FAKE, I64S[(t + u) % N64], 1, nq, T, q0, INTS[w],
@@ -107,10 +130,9 @@ int main(void) {
           expect_status(buf, hs2_select_blocks_window(FAKE, T, INTS[w], nq, T, q0, 128, 1024, INTS[(w + u) % NI],
                                                       FAKE, FAKE, FAKE, (size_t)1 << 40, NULL));
         }
-        expect_status(buf, hs2_bridge_kv_proj(FAKE, T, INTS[a], FAKE, FAKE, INTS[u % NI], 256, FAKE, FAKE, q0, NULL,
-                                              0, NULL));
+        expect_status(buf, hs2_bridge_kv_proj(FAKE, T, INTS[a], FAKE, FAKE, INTS[u % NI], 256, FAKE, FAKE, q0, NULL));
         expect_status(buf, hs2_bridge_kv_proj_fp8(FAKE, T, 2048, FAKE, FAKE, 4, 256, FAKE, FAKE, FAKE, FAKE, q0,
-                                                  I64S[(t + u) % N64], NULL, 0, NULL));
+                                                  I64S[(t + u) % N64], NULL));
       }
   printf("checked %d calls (%d reached a launch), %d failed\n", n_checked, n_launched, n_failed);
   return n_failed || n_launched == 0 ? 1 : 0;

@@ -19,13 +19,13 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = hs2.header_symbols()
-    assert len(names) == 17
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.hs2_version() == 10000
+    assert lib.hs2_version() == 10100
     for code in range(0, -8, -1):
         assert lib.hs2_status_str(code).decode().startswith("HS2_")
     assert b"unknown" in lib.hs2_status_str(-99)
@@ -77,7 +77,6 @@ def test_workspace_sizes(lib):
     assert lib.hs2_full_attn_workspace_bytes(1, 2048, 4, 2048, F32) == 0
     assert lib.hs2_full_attn_workspace_bytes(1, 32768, 16, 131072, BF16) >= 32768 * 16 * 4   # lse pass -> P/V pass
     assert lib.hs2_full_attn_workspace_bytes(16, 1, 16, 32768, BF16) >= 16 * 32768 * 16 * 4
-    assert lib.hs2_bridge_workspace_bytes(4, 2048, 256) == 0
     # few long rows (decode) use the multi-workgroup selector: histograms + per-segment counts
     assert lib.hs2_select_workspace_bytes(1, 1, 1 << 20, (1 << 20) - 1) >= 3 * 2048 * 4 + (1 << 20) // 4096 * 8
     assert lib.hs2_select_workspace_bytes(1, 32768, 131072, 98304) == 0     # many rows: one workgroup per row
@@ -170,10 +169,10 @@ def test_sparse_noalloc_rejects(lib, kw, code):
 
 
 def bridge(lib, **kw):
-    a = dict(x=A, L=4096, D=2048, wk=A, wv=A, n=4, d=256, ko=A, vo=A, st=4096 * 256, ws=None, wsb=0)
+    a = dict(x=A, L=4096, D=2048, wk=A, wv=A, n=4, d=256, ko=A, vo=A, st=4096 * 256)
     a.update(kw)
     return lib.hs2_bridge_kv_proj(a["x"], a["L"], a["D"], a["wk"], a["wv"], a["n"], a["d"], a["ko"], a["vo"],
-                                  a["st"], a["ws"], a["wsb"], None)
+                                  a["st"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -193,11 +192,10 @@ def test_bridge_rejects(lib, kw, code):
 
 
 def bridge8(lib, **kw):
-    a = dict(x=A, L=4096, D=2048, wk=A, wv=A, n=4, d=256, ko=A, vo=A, ks=A, vs=A, st=4096 * 256, sst=4096, ws=None,
-             wsb=0)
+    a = dict(x=A, L=4096, D=2048, wk=A, wv=A, n=4, d=256, ko=A, vo=A, ks=A, vs=A, st=4096 * 256, sst=4096)
     a.update(kw)
     return lib.hs2_bridge_kv_proj_fp8(a["x"], a["L"], a["D"], a["wk"], a["wv"], a["n"], a["d"], a["ko"], a["vo"],
-                                      a["ks"], a["vs"], a["st"], a["sst"], a["ws"], a["wsb"], None)
+                                      a["ks"], a["vs"], a["st"], a["sst"], None)
 
 
 @pytest.mark.parametrize("kw,code", [

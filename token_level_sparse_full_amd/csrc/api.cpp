@@ -91,7 +91,7 @@ int kv_kind(int dtype) { return dtype == HS2_F32 ? hs2::KV_F32 : (dtype == HS2_B
 
 extern "C" {
 
-int hs2_version(void) { return 10000; }
+int hs2_version(void) { return 10100; }
 
 const char* hs2_last_error(void) { return g_last_error; }
 
@@ -305,11 +305,8 @@ int hs2_swa_attn(const void* q, int B, int n_q, int H, int d, const void* k, con
   return hip_status(hs2::launch_swa(p, (hipStream_t)stream), "hs2_swa_attn");
 }
 
-size_t hs2_bridge_workspace_bytes(int n_layers, int D, int d) { return hs2::bridge_workspace_bytes(n_layers, D, d); }
-
 int hs2_bridge_kv_proj(const void* x, int64_t L, int D, const void* w_k, const void* w_v, int n_layers, int d,
-                       void* k_out, void* v_out, int64_t out_layer_stride, void* workspace, size_t ws_bytes,
-                       void* stream) {
+                       void* k_out, void* v_out, int64_t out_layer_stride, void* stream) {
   if (!x || !w_k || !w_v || !k_out || !v_out) return fail(HS2_ERR_NULL, "x, w_k, w_v, k_out and v_out are required");
   if (d != HS2_HEAD_DIM) return fail(HS2_ERR_UNSUPPORTED, "projection width %d unsupported (only %d)", d, HS2_HEAD_DIM);
   if (L < 1 || L > kMaxBridgeRows || D < 32 || D % 32 != 0 || D > 65536)
@@ -319,17 +316,15 @@ int hs2_bridge_kv_proj(const void* x, int64_t L, int D, const void* w_k, const v
   if ((L + 255) / 256 * (int64_t)(2 * n_layers) > 0x7FFFFFFF) return fail(HS2_ERR_SHAPE, "L too large");
   if (!aligned(x, 16) || !aligned(w_k, 16) || !aligned(w_v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16))
     return fail(HS2_ERR_ALIGN, "x, w_k, w_v, k_out and v_out must be 16-byte aligned");
-  const size_t need = hs2::bridge_workspace_bytes(n_layers, D, d);
-  if (need > 0 && (!workspace || ws_bytes < need)) return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes required", need);
   hs2::BridgeParams p;
   p.x = x; p.w_k = w_k; p.w_v = w_v; p.k_out = k_out; p.v_out = v_out;
   p.L = L; p.D = D; p.n_layers = n_layers; p.out_layer_stride = out_layer_stride;
-  return hip_status(hs2::launch_bridge(p, workspace, ws_bytes, (hipStream_t)stream), "hs2_bridge_kv_proj");
+  return hip_status(hs2::launch_bridge(p, (hipStream_t)stream), "hs2_bridge_kv_proj");
 }
 
 int hs2_bridge_kv_proj_fp8(const void* x, int64_t L, int D, const void* w_k, const void* w_v, int n_layers, int d,
                            uint8_t* k_out, uint8_t* v_out, float* k_scale, float* v_scale, int64_t out_layer_stride,
-                           int64_t scale_layer_stride, void* workspace, size_t ws_bytes, void* stream) {
+                           int64_t scale_layer_stride, void* stream) {
   if (!x || !w_k || !w_v || !k_out || !v_out || !k_scale || !v_scale)
     return fail(HS2_ERR_NULL, "x, w_k, w_v, k_out, v_out, k_scale and v_scale are required");
   if (d != HS2_HEAD_DIM) return fail(HS2_ERR_UNSUPPORTED, "projection width %d unsupported (only %d)", d, HS2_HEAD_DIM);
@@ -342,13 +337,11 @@ int hs2_bridge_kv_proj_fp8(const void* x, int64_t L, int D, const void* w_k, con
   if (!aligned(x, 16) || !aligned(w_k, 16) || !aligned(w_v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16))
     return fail(HS2_ERR_ALIGN, "x, w_k, w_v, k_out and v_out must be 16-byte aligned");
   if (!aligned(k_scale, 4) || !aligned(v_scale, 4)) return fail(HS2_ERR_ALIGN, "k_scale and v_scale must be 4-byte aligned");
-  const size_t need = hs2::bridge_workspace_bytes(n_layers, D, d);
-  if (need > 0 && (!workspace || ws_bytes < need)) return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes required", need);
   hs2::BridgeParams p;
   p.x = x; p.w_k = w_k; p.w_v = w_v; p.k_out = k_out; p.v_out = v_out;
   p.L = L; p.D = D; p.n_layers = n_layers; p.out_layer_stride = out_layer_stride;
   p.fp8 = true; p.k_scale = k_scale; p.v_scale = v_scale; p.scale_layer_stride = scale_layer_stride;
-  return hip_status(hs2::launch_bridge(p, workspace, ws_bytes, (hipStream_t)stream), "hs2_bridge_kv_proj_fp8");
+  return hip_status(hs2::launch_bridge(p, (hipStream_t)stream), "hs2_bridge_kv_proj_fp8");
 }
 
 }  // extern "C"

@@ -223,9 +223,7 @@ __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParam
 
 }  // namespace
 
-size_t bridge_workspace_bytes(int, int, int) { return 0; }
-
-hipError_t launch_bridge(const BridgeParams& p, void*, size_t, hipStream_t stream) {
+hipError_t launch_bridge(const BridgeParams& p, hipStream_t stream) {
   const int64_t mtiles = (p.L + BM - 1) / BM;
   const int ntiles = (2 * p.n_layers * 256) / BN;
   const dim3 grid((unsigned)(mtiles * ntiles)), block(BR_THREADS);

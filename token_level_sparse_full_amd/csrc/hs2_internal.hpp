@@ -125,7 +125,6 @@ struct BridgeParams {
   float* v_scale = nullptr;
   int64_t scale_layer_stride = 0;
 };
-size_t bridge_workspace_bytes(int n_layers, int D, int d);
-hipError_t launch_bridge(const BridgeParams& p, void* ws, size_t ws_bytes, hipStream_t stream);
+hipError_t launch_bridge(const BridgeParams& p, hipStream_t stream);
 
 }  // namespace hs2

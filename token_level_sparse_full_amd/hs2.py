@@ -37,9 +37,8 @@ _PROTOS = {
     "hs2_sparse_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "hs2_sparse_attn_reuse_noalloc": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp, _i64, _vp, _vp, _i, _f,
                                            _vp, _vp, _vp]),
-    "hs2_bridge_kv_proj": (_i, [_vp, _i64, _i, _vp, _vp, _i, _i, _vp, _vp, _i64, _vp, _sz, _vp]),
-    "hs2_bridge_workspace_bytes": (_sz, [_i, _i, _i]),
-    "hs2_bridge_kv_proj_fp8": (_i, [_vp, _i64, _i, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _sz, _vp]),
+    "hs2_bridge_kv_proj": (_i, [_vp, _i64, _i, _vp, _vp, _i, _i, _vp, _vp, _i64, _vp]),
+    "hs2_bridge_kv_proj_fp8": (_i, [_vp, _i64, _i, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _i64, _i64, _vp]),
     "hs2_rope_partial": (_i, [_vp, _vp, _i64, _i, _i, _i64, _i, ctypes.c_double, _vp]),
     "hs2_swa_attn": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _i64, _i64, _i, _f, _vp, _vp, _vp]),
     "hs2_status_str": (ctypes.c_char_p, [_i]),
@@ -258,10 +257,8 @@ def hs2_bridge_kv_proj(x, w_k, w_v, *, k_out=None, v_out=None, out_layer_stride:
         v_out = torch.empty((n_layers, L, d), dtype=torch.bfloat16, device=x.device)
     if out_layer_stride is None:
         out_layer_stride = k_out.stride(0) if k_out.dim() == 3 else L * d
-    need = int(lib().hs2_bridge_workspace_bytes(n_layers, D, d))
-    ws = workspace(need, x.device)
     rc = lib().hs2_bridge_kv_proj(_ptr(x), L, D, _ptr(w_k), _ptr(w_v), n_layers, d, _ptr(k_out), _ptr(v_out),
-                                  out_layer_stride, _ptr(ws), need, _stream(stream))
+                                  out_layer_stride, _stream(stream))
     check("hs2_bridge_kv_proj", rc)
     return k_out, v_out
 
@@ -284,10 +281,8 @@ def hs2_bridge_kv_proj_fp8(x, w_k, w_v, *, k_out=None, v_out=None, k_scale=None,
         out_layer_stride = k_out.stride(0) if k_out.dim() == 3 else L * d
     if scale_layer_stride is None:
         scale_layer_stride = k_scale.stride(0) if k_scale.dim() == 2 else L
-    need = int(lib().hs2_bridge_workspace_bytes(n_layers, D, d))
-    ws = workspace(need, x.device)
     rc = lib().hs2_bridge_kv_proj_fp8(_ptr(x), L, D, _ptr(w_k), _ptr(w_v), n_layers, d, _ptr(k_out), _ptr(v_out),
                                       _ptr(k_scale), _ptr(v_scale), out_layer_stride, scale_layer_stride,
-                                      _ptr(ws), need, _stream(stream))
+                                      _stream(stream))
     check("hs2_bridge_kv_proj_fp8", rc)
     return k_out, v_out, k_scale, v_scale
