@@ -183,7 +183,12 @@ __global__ __launch_bounds__(SW_THREADS, 2) void swa_kernel(const SwaParams p) {
       tmax = fmaxf(tmax, x[r]);
     }
     tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
+    // Lazy rescale: the reference max m_run moves only when the tile's max
+    // exceeds it by more than 8 (log2 units), so the probabilities stay below
+    // 2^8 and O (in AGPRs: a read, a multiply and a write per element) is
+    // rescaled only then -- after the first tile of a window almost never.
+    // exp2(x - m) / sum exp2(x - m) is the same softmax for any reference m.
+    const float m_new = tmax > m_run + 8.f ? tmax : m_run;
     const float m_use = m_new == kNegInf ? 0.f : m_new;   // nothing seen yet: every term is 0
     const float alpha = fast_exp2(m_run - m_use);          // 0 on the first keys (O and z are 0)
     float psum = 0.f;
@@ -195,8 +200,10 @@ __global__ __launch_bounds__(SW_THREADS, 2) void swa_kernel(const SwaParams p) {
       pb[r >> 3][r & 7] = to_bf16(e);
     }
     z_run = z_run * alpha + psum;
+    // O is still 0 while m_run is -inf: no rescale needed then
+    const bool rescale = alpha != 1.f && m_run != kNegInf;
     m_run = m_new;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+    if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
 #pragma unroll
       for (int n = 0; n < 8; ++n) oacc[n] *= alpha;
     }
