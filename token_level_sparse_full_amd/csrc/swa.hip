@@ -107,18 +107,27 @@ __global__ __launch_bounds__(SW_THREADS, 2) void swa_kernel(const SwaParams p) {
   const char* kg = (const char*)p.k + (int64_t)b * p.T * 512;
   const char* vg = (const char*)p.v + (int64_t)b * p.T * 512;
 
-  // ---- queries (B operand of S^T): row l32, dims 16 s + 8 hb .. +7
-  bf16x8 qf[16];
-  {
-    const bf16* qp = (const bf16*)p.q + q_row * kHeadDim + 8 * hb;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) qf[s] = as_bf16x8(*(const u32x4*)(qp + 16 * s));
-  }
-
-  // ---- LDS DMA of one tile image: 17 wave-instructions of 64 x 16 B (lane l of
-  // instruction i fills chunk 64 i + l of the padded image), instruction i
-  // issued by wave i % 4.  Pad chunks load a valid chunk and are never read.
+  // The wave's 32 rows (32/H tokens x H heads) are one contiguous 16 KB run of
+  // q and of o: both move in whole rows, so that every global access
+  // instruction covers 1 KB of consecutive bytes, and LDS turns them to and
+  // from the MFMA layout (a row per lane).  Read or written in that layout,
+  // each instruction would touch 32 rows and issue 32 partial-line requests.
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int tok_w0 = tok_blk0 + wv * TPW;
+  const int64_t row_w0 = ((int64_t)b * p.n_q + tok_w0) * H;          // first row of the wave
+  const int rows_w = max(0, min(TPW, p.n_q - tok_w0)) * H;             // rows of real tokens
+  char* const wbuf = wv == 0 ? lds_k1 : wv == 1 ? lds_v1 : wv == 2 ? lds_k0 : lds_v0;   // the wave's O staging
+  // buffer resources over the wave's rows of q and o: loads past the last
+  // token return zeros, stores there are dropped
+  auto rows_rsrc = [&](const void* base) __attribute__((always_inline)) {
+    const uint64_t a = (uint64_t)((const char*)base + row_w0 * 512);
+    return __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a)),
+        0, __builtin_amdgcn_readfirstlane(rows_w * 512), 0x00020000);
+  };
+  const __amdgpu_buffer_rsrc_t rqo_q = rows_rsrc(p.q);
+
   uint32_t koff[5], voff[5];
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
@@ -143,6 +152,29 @@ __global__ __launch_bounds__(SW_THREADS, 2) void swa_kernel(const SwaParams p) {
       }
     }
   };
+
+  // ---- queries (B operand of S^T): row l32, dims 16 s + 8 hb .. +7.  Loaded
+  // as whole rows (instruction j: rows 2j and 2j + 1, rows past the last token
+  // as zeros) while the first tile's DMA is in flight, then turned into
+  // fragments through LDS: in the two buffers of the second tile, waves 0 and
+  // 1 first, then waves 2 and 3.
+  bf16x8 qf[16];
+  {
+    u32x4 raw[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      raw[j] = __builtin_amdgcn_raw_buffer_load_b128(rqo_q, (2 * j + hb) * 512 + 16 * l32, 0, 0);
+    dma(kt0, lds_k0, lds_v0);
+    auto stage = [&](char* sb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) *(u32x4*)(sb + (2 * j + hb) * SW_KP + 16 * l32) = raw[j];
+#pragma unroll
+      for (int s = 0; s < 16; ++s) qf[s] = as_bf16x8(*(const u32x4*)(sb + l32 * SW_KP + (2 * s + hb) * 16));
+    };
+    if (wv < 2) stage(wv == 0 ? lds_k1 : lds_v1);
+    __syncthreads();
+    if (wv >= 2) stage(wv == 2 ? lds_k1 : lds_v1);
+  }
 
   float m_run = kNegInf, z_run = 0.f;
   f32x16 oacc[8];
@@ -233,7 +265,6 @@ __global__ __launch_bounds__(SW_THREADS, 2) void swa_kernel(const SwaParams p) {
   // into that buffer is issued right away and lands while tile kt computes.
   // The buffers are picked at run time: one copy of the loop body, so that the
   // accumulators keep their registers from one tile to the next.
-  dma(kt0, lds_k0, lds_v0);
   for (int kt = kt0; kt <= kt1; ++kt) {
     const bool odd = (kt - kt0) & 1;
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA of tile kt
@@ -242,11 +273,13 @@ __global__ __launch_bounds__(SW_THREADS, 2) void swa_kernel(const SwaParams p) {
     step(kt, odd ? lds_k1 : lds_k0, odd ? lds_v1 : lds_v0);
   }
 
-  // ---- outputs: lane l holds O[row l32][32n + 8(r/4) + 4hb + r%4]
+  // ---- outputs: lane l holds O[row l32][32n + 8(r/4) + 4hb + r%4].  The
+  // normalised bf16 rows go to the wave's staging buffer (pitch 33 chunks: the
+  // 8-byte writes of 16 rows hit distinct banks), then out as whole rows.
   const float z = z_run + shfl_xor(z_run, 32);
   const float inv = z > 0.f ? 1.f / z : 0.f;
-  if (!row_ok) return;
-  bf16* orow = (bf16*)p.o + q_row * kHeadDim;
+  if (hb == 0 && row_ok && p.lse) p.lse[q_row] = z > 0.f ? (m_run + fast_log2(z)) * kLn2 : kNegInf;
+  __syncthreads();   // every wave is done with the last tile
 #pragma unroll
   for (int n = 0; n < 8; ++n)
 #pragma unroll
@@ -254,9 +287,16 @@ __global__ __launch_bounds__(SW_THREADS, 2) void swa_kernel(const SwaParams p) {
       bf16x4 w;
 #pragma unroll
       for (int j = 0; j < 4; ++j) w[j] = to_bf16(oacc[n][4 * a + j] * inv);
-      *(bf16x4*)(orow + 32 * n + 8 * a + 4 * hb) = w;
+      *(bf16x4*)(wbuf + l32 * SW_KP + 64 * n + 16 * a + 8 * hb) = w;
     }
-  if (hb == 0 && p.lse) p.lse[q_row] = z > 0.f ? (m_run + fast_log2(z)) * kLn2 : kNegInf;
+  // instruction j: rows 2j (lanes 0..31) and 2j + 1 (lanes 32..63), 16 B a lane
+  const __amdgpu_buffer_rsrc_t ro = rows_rsrc(p.o);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int row = 2 * j + hb;
+    const u32x4 v = *(const u32x4*)(wbuf + row * SW_KP + 16 * l32);
+    __builtin_amdgcn_raw_buffer_store_b128(v, ro, row * 512 + 16 * l32, 0, 0);
+  }
 }
 
 }  // namespace
