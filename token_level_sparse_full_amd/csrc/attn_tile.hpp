@@ -162,6 +162,41 @@ __device__ __forceinline__ void store_v_rows(char* stage, int l, const u32x4* vr
   }
 }
 
+// K rows of a step as whole rows (loaded with load_v_rows, so that each load
+// instruction covers whole cache lines) -> LDS -> MFMA fragments.  Fragment
+// reads of 16 rows at one offset hit distinct banks at these pitches (bf16
+// 528 B, e4m3 codes 272 B: rows shift by 4 banks).  The bf16 image (16.5 KB)
+// fits the V stage, which the same wave fills after reading the fragments.
+template <int KV>
+struct KStage {
+  static constexpr int PITCH_B = KV == KV_BF16 ? 528 : 272;
+};
+static_assert(32 * 528 <= kTileStageBytes, "K stage");
+template <int KV>
+__device__ __forceinline__ void store_k_rows(char* stage, int l, const u32x4* kr) {
+  constexpr int PB = KStage<KV>::PITCH_B;
+  if constexpr (KV == KV_BF16) {
+#pragma unroll
+    for (int it = 0; it < 16; ++it) *(u32x4*)(stage + (2 * it + (l >> 5)) * PB + 16 * (l & 31)) = kr[it];
+  } else {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) *(u32x4*)(stage + (4 * it + (l >> 4)) * PB + 16 * (l & 15)) = kr[it];
+  }
+}
+// This lane's K fragment of 16-key tile mt of the staged rows (the layout of
+// load_k_tile).
+template <int KV>
+__device__ __forceinline__ void read_k_tile(const char* stage, int mt, int c16, int g, u32x4* kr) {
+  const char* row = stage + (16 * mt + c16) * KStage<KV>::PITCH_B;
+  if constexpr (KV == KV_BF16) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kr[s] = *(const u32x4*)(row + (32 * s + 8 * g) * 2);
+  } else {
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) kr[s2] = *(const u32x4*)(row + 64 * s2 + 16 * g);
+  }
+}
+
 // Stage the V rows of one step into LDS.
 template <int KV, typename RowPtr>
 __device__ __forceinline__ void stage_v(char* stage, int l, RowPtr rowptr) {

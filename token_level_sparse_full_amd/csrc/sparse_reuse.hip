@@ -12,9 +12,11 @@
 //    end (no atomics, deterministic);
 //  * the H <= 16 query heads share every K/V row (MQA), so they form the N
 //    axis of 16x16 MFMA tiles (attn_tile.hpp);
-//  * K fragments go straight from HBM/L2 into registers (four lanes cover 64
-//    contiguous bytes of a gathered row per load instruction); V rows are
-//    staged row-major in LDS and read back transposed;
+//  * K and V rows are gathered whole (each load instruction covers two bf16
+//    or four e4m3 rows), then pass through the wave's LDS stage: K read back
+//    as MFMA fragments, then V, row-major, read back transposed.  Loaded
+//    straight into the fragment layout, a K load instruction would cover 16
+//    rows x 64 B and request every cache line twice;
 //  * e4m3 caches are widened to bf16 exactly in registers; the row scales
 //    multiply the logits (K) and are folded into P (V);
 //  * few queries (decode: B * n_q <= 64) would leave most CUs idle, so their
@@ -135,10 +137,21 @@ __global__ __launch_bounds__(SP_THREADS, 2) void sparse_attn_kernel(const Sparse
     }
     u32x4 kr[NMT][FragRegs<KV>::K], vr[FragRegs<KV>::V];
     auto load_v = [&] { load_v_rows<KV, false>(l, [&](int slot) { return vseq + (int64_t)max(tab[slot], 0) * ROWB; }, vr); };
+    if constexpr (KV == KV_F32) {
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) load_k_tile<KV>(kseq + (int64_t)max(tab[16 * mt + c16], 0) * ROWB, g, kr[mt]);
+      for (int mt = 0; mt < NMT; ++mt) load_k_tile<KV>(kseq + (int64_t)max(tab[16 * mt + c16], 0) * ROWB, g, kr[mt]);
+    } else {
+      static_assert(NMT * FragRegs<KV>::K == FragRegs<KV>::V, "K rows fill the fragment registers");
+      load_v_rows<KV, false>(l, [&](int slot) { return kseq + (int64_t)max(tab[slot], 0) * ROWB; }, &kr[0][0]);
+    }
     if constexpr (V_EARLY) load_v();
     key = fetch_key(st + SP_WAVES);
+    if constexpr (KV != KV_F32) {
+      store_k_rows<KV>(stage, l, &kr[0][0]);
+      wave_lds_order();
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) read_k_tile<KV>(stage, mt, c16, g, kr[mt]);
+    }
 
     f32x4 sacc[NMT];
 #pragma unroll
