@@ -13,7 +13,9 @@
 // stream into LDS by buffer loads to LDS (16 B per lane, no register staging)
 // through four stage buffers, three chunks ahead of the MFMAs; each wave's
 // eight DMA instructions of a chunk are spread over the 32 MFMAs of the chunk
-// before.  The swizzled LDS layouts are made by the per-lane source offsets
+// before, and the operand fragments of a chunk's second K-step are read from
+// LDS while the MFMAs of its first run.  The tile order gives each XCD a few
+// weight blocks for all of its row tiles.  The swizzled LDS layouts are made by the per-lane source offsets
 // of the DMA.  The weights are read in their natural [D][d] layout:
 // ds_read_b64_tr_b16 turns the [k][n] LDS tile into the k-contiguous B
 // operand, so no transposed copy of W is needed.  Rows past L read as zeros
@@ -75,7 +77,15 @@ __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParam
   const int wm = wave >> 1, wn = wave & 1;  // wave tile (128 x 128) inside the workgroup tile
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int n_ntiles = (2 * p.n_layers * 256) / BN;
-  const int mt_blk = blockIdx.x / n_ntiles, nt_blk = blockIdx.x % n_ntiles;
+  // Tile order: each XCD (blocks are dealt to the 8 XCDs round-robin) takes a
+  // contiguous range of a grouped order -- GN column tiles side by side for
+  // every row tile -- so that its L2 holds GN weight blocks (1 MB each) and
+  // each x tile is fetched into it once for GN workgroups.
+  const int mtiles = (int)(gridDim.x / n_ntiles);
+  const int tt = xcd_remap(blockIdx.x, gridDim.x);
+  const int GN = n_ntiles % 4 == 0 ? 4 : 2;   // n_ntiles = 2 n_layers is even
+  const int grp = tt / (GN * mtiles), rem_t = tt - grp * (GN * mtiles);
+  const int mt_blk = rem_t / GN, nt_blk = GN * grp + rem_t % GN;
   const int64_t m0 = (int64_t)mt_blk * BM;
   const int n0 = nt_blk * BN;                 // global column of the concatenated weights
   const int layer = n0 / 512, which = (n0 / 256) & 1;
@@ -128,28 +138,36 @@ __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParam
     // visible and ends every wave's reads of chunk kc - 1
     __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
     dma_barrier();
+    // fragments of K-step 1 are read while the MFMAs of step 0 run
+    auto rd_a = [&](int ks, int i) __attribute__((always_inline)) {
+      const int row = wm * 128 + 32 * i + l32;
+      return as_bf16x8(*(const u32x4*)(buf + a_off(row, 2 * ks + hb)));
+    };
+    // B[k][n] for k = 16ks + 8(G/2) + i, n = wn*128 + 32j + 16(G%2) + s16
+    auto rd_b = [&](int ks, int j) __attribute__((always_inline)) {
+      const int krow = 16 * ks + 8 * (G >> 1) + (s16 >> 2);
+      const int col = wn * 128 + 32 * j + 16 * (G & 1) + 4 * (s16 & 3);
+      const int ch = col >> 3, half = (col >> 2) & 1;
+      const char* b0 = buf + A_BYTES + b_off(krow, ch) + half * 8;
+      const char* b1 = buf + A_BYTES + b_off(krow + 4, ch) + half * 8;
+      return cat8(lds_tr16((const bf16*)b0), lds_tr16((const bf16*)b1));
+    };
+    bf16x8 af[2][4], bfr[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      af[0][i] = rd_a(0, i);
+      bfr[0][i] = rd_b(0, i);
+    }
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 128 + 32 * i + l32;
-        af[i] = as_bf16x8(*(const u32x4*)(buf + a_off(row, 2 * ks + hb)));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // B[k][n] for k = 16ks + 8(G/2) + i, n = wn*128 + 32j + 16(G%2) + s16
-        const int krow = 16 * ks + 8 * (G >> 1) + (s16 >> 2);
-        const int col = wn * 128 + 32 * j + 16 * (G & 1) + 4 * (s16 & 3);
-        const int ch = col >> 3, half = (col >> 2) & 1;
-        const char* b0 = buf + A_BYTES + b_off(krow, ch) + half * 8;
-        const char* b1 = buf + A_BYTES + b_off(krow + 4, ch) + half * 8;
-        bfr[j] = cat8(lds_tr16((const bf16*)b0), lds_tr16((const bf16*)b1));
-      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[ks][i], bfr[ks][j], acc[i][j]);
+        if (ks == 0) {
+          af[1][i] = rd_a(1, i);
+          bfr[1][i] = rd_b(1, i);
+        }
         dma_one(kc + 3, nxt, 4 * ks + i);
         __builtin_amdgcn_sched_barrier(0);
       }
