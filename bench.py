@@ -68,12 +68,12 @@ GROUPS = {
     "sparse_prefill": ("prefill_sparse", ["sparse_attn_kernel"], ["sparse_reuse.hip", "attn_tile.hpp"], 1),
     "full_attn_decode_b16_32k": ("decode_b16_32k", ["decode_stream_kernel", "decode_merge_kernel",
                                                     "decode_merge_score_kernel"], ["attn_decode.hip", "attn_tile.hpp"], 1),
-    "select_decode_b16_32k": ("decode_b16_32k", ["select_kernel", "mb_"], ["select.hip"], 1),
+    "select_decode_b16_32k": ("decode_b16_32k", ["select_kernel", "fr_"], ["select.hip"], 1),
     "sparse_decode_b16_32k": ("decode_b16_32k", ["sparse_attn_kernel", "sparse_merge_kernel"],
                               ["sparse_reuse.hip", "attn_tile.hpp"], 3),
     "full_attn_decode_1m_fp8": ("decode_1m_fp8", ["decode_stream_kernel", "decode_merge_kernel",
                                                   "decode_merge_score_kernel"], ["attn_decode.hip", "attn_tile.hpp"], 1),
-    "select_decode_1m_fp8": ("decode_1m_fp8", ["select_kernel", "mb_"], ["select.hip"], 1),
+    "select_decode_1m_fp8": ("decode_1m_fp8", ["select_kernel", "fr_"], ["select.hip"], 1),
     "sparse_decode_1m_fp8": ("decode_1m_fp8", ["sparse_attn_kernel", "sparse_merge_kernel"],
                              ["sparse_reuse.hip", "attn_tile.hpp"], 4),
 }

@@ -138,10 +138,12 @@ int hs2_select_topk_window(const float* scores, int64_t ld_scores, int B, int n_
 
 /* Workspace of hs2_select_topk_window for these shapes (an upper bound over
  * every window >= 1).  It is 0 when the rows are many or short (one workgroup
- * per row); few long rows (at most 64 rows, 32768 or more candidates, the
- * decode case) are split over many workgroups and need per-row histograms
- * and per-segment counts there.  The contents are scratch: nothing persists
- * between calls, and calls that share a workspace must not overlap. */
+ * per row); few long rows (at most 64 rows, 24576 or more candidates, the
+ * decode case) are split over many workgroups and need, per row, a threshold
+ * estimate and, per segment of 4096 candidates, a count and up to 512 kept
+ * (score, index) pairs there (about 1 byte per candidate).  The contents are
+ * scratch: nothing persists between calls, and calls that share a workspace
+ * must not overlap. */
 size_t hs2_select_workspace_bytes(int B, int n_q, int64_t T, int64_t q_pos0);
 
 /*

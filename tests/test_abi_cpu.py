@@ -77,10 +77,13 @@ def test_workspace_sizes(lib):
     assert lib.hs2_full_attn_workspace_bytes(1, 2048, 4, 2048, F32) == 0
     assert lib.hs2_full_attn_workspace_bytes(1, 32768, 16, 131072, BF16) >= 32768 * 16 * 4   # lse pass -> P/V pass
     assert lib.hs2_full_attn_workspace_bytes(16, 1, 16, 32768, BF16) >= 16 * 32768 * 16 * 4
-    # few long rows (decode) use the multi-workgroup selector: histograms + per-segment counts
-    assert lib.hs2_select_workspace_bytes(1, 1, 1 << 20, (1 << 20) - 1) >= 3 * 2048 * 4 + (1 << 20) // 4096 * 8
+    # few long rows (decode) use the multi-workgroup selector: per segment of 4096 candidates
+    # a count and up to 512 kept (pattern, index) pairs
+    assert lib.hs2_select_workspace_bytes(1, 1, 1 << 20, (1 << 20) - 1) >= (1 << 20) // 4096 * (4 + 512 * 8)
+    assert lib.hs2_select_workspace_bytes(16, 1, 32768, 32767) >= 16 * 8 * (4 + 512 * 8)
     assert lib.hs2_select_workspace_bytes(1, 32768, 131072, 98304) == 0     # many rows: one workgroup per row
-    assert lib.hs2_select_workspace_bytes(16, 1, 32768, 32767) == 0         # 16 rows below 32768 candidates
+    assert lib.hs2_select_workspace_bytes(65, 1, 32768, 32767) == 0         # more than 64 rows
+    assert lib.hs2_select_workspace_bytes(16, 1, 24000, 23999) == 0         # rows below 24576 candidates
     # few queries (decode) split each selected set into 128-key pieces: per piece max, sum and output
     assert lib.hs2_sparse_workspace_bytes(16, 1, 16, 1152) >= 16 * 9 * 16 * 258 * 4
     assert lib.hs2_sparse_workspace_bytes(1, 64, 16, 1152) > 0

@@ -1,8 +1,10 @@
 """Every entry point run twice on the same inputs gives the same bytes.
 
-The library promises deterministic results (no floating-point atomics on any
-output path; the multi-workgroup selector merges its histograms with integer
-atomics, whose sums do not depend on the order).  Outputs are filled with
+The library promises deterministic results: there are no floating-point
+atomics and no global-memory atomics (every partial result has its own slot,
+and the multi-workgroup selector places each segment's candidates by a scan
+of the segment counts); the selectors' LDS histograms count with integer
+atomics, whose sums do not depend on the order.  Outputs are filled with
 different bytes before each run, so an output element that a run does not
 write also shows up as a difference.
 """

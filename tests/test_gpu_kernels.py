@@ -140,6 +140,38 @@ def test_select_sink_and_ties(q_pos0, n_q, T):
     _select_case(sc, q_pos0, T, 128, 1024)
 
 
+# Few long rows (the multi-workgroup form, from 24576 candidates on): each segment of 4096
+# candidates stores at most 512 of those at or above the row's threshold estimate, so rows
+# whose best candidates crowd into one or two segments take the path that reads such a
+# segment again; a row that keeps too few or too many over the estimate takes the exact
+# multi-pass path.  Just above the size where the form starts, and at 70k.
+@pytest.mark.parametrize("q_pos0,n_q,T", [(24720, 2, 24730), (70000, 1, 70001)])
+def test_select_few_rows_crowded(q_pos0, n_q, T):
+    say("select crowded", q_pos0, n_q, T)
+    rng = np.random.default_rng(q_pos0 + 11)
+    ld = (q_pos0 + n_q + 3) // 4 * 4
+    B = 5
+    sc = np.zeros((B, n_q, ld), dtype=np.float32)
+    for b in range(B):
+        for i in range(n_q):
+            n = q_pos0 + i + 1
+            nc = n - 128
+            row = rng.random(n, dtype=np.float32) / n
+            mode = (b * n_q + i) % 5
+            if mode == 0:      # 2000 strong candidates inside one segment
+                row[8192 + rng.choice(4096, size=2000, replace=False)] += np.float32(8.0 / n)
+            elif mode == 1:    # a strong run across a segment boundary, with ties in it
+                row[3000:7500] = np.float32(4.0 / n) + np.float32(1.0 / n) * rng.integers(0, 4, 4500)
+            elif mode == 2:    # decreasing: the best candidates are the first ones
+                row[:nc] = (np.arange(nc, 0, -1, dtype=np.float64) / (float(n) * n)).astype(np.float32)
+            elif mode == 3:    # a crowded segment at the end of the candidates
+                row[nc - 3000:nc] += np.float32(2.0 / n)
+            else:              # heavy ties everywhere: the estimate keeps too many
+                row = (rng.integers(0, 3, n) / 64.0).astype(np.float32)
+            sc[b, i, :n] = row
+    _select_case(sc, q_pos0, T, 128, 1024)
+
+
 def _score_rows(rng, B, n_q, q_pos0, ld):
     sc = np.zeros((B, n_q, ld), dtype=np.float32)
     for b in range(B):

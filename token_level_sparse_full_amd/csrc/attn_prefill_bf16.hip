@@ -195,8 +195,35 @@ __global__ __launch_bounds__(PB_THREADS, (PHASE == 1 && !SC) ? 2 : 1) void prefi
     // Online max / sum of one tile (lane: rows l32 and 32 + l32, keys kt*32 +
     // 8(r/4) + 4hb + r%4).  Tiles left of the diagonal need no causal mask:
     // that path is the bulk of the work, so it is kept free of selects.
+    //
+    // Left of the diagonal the running maximum is a lazy reference: a tile's
+    // exponentials are taken against it as it stands, and it is raised (with
+    // the rescale of the sum) only when a tile's sum of 16 terms per row
+    // block exceeds 2^64, i.e. when some logit lies more than 60 (log2 units)
+    // above it.  The terms stay below 2^64 and the sum below 2^81, far inside
+    // float32, and terms far below the reference underflow as they would
+    // against the true maximum; the sum carries the same relative rounding
+    // either way.  This drops the tile maximum (16 max per row block) from
+    // the common case.  The test is wave-uniform: if any lane fails it, the
+    // whole wave redoes the tile against the true maximum.
     auto lse_update = [&](Pair& st, int kt, bool masked) __attribute__((always_inline)) {
       const int kbase = kt * PB_KT;
+      if (!masked) {
+        float accl[2];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          float a = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) a += fast_exp2(st.v[n][r] * p.scale_log2 - m_run[n]);
+          accl[n] = a;
+        }
+        // !(a <= 2^64) also catches a first tile (m_run = -inf: a = +inf)
+        if (!__any(!(accl[0] <= 0x1p64f) || !(accl[1] <= 0x1p64f))) {
+          z_run[0] += accl[0];
+          z_run[1] += accl[1];
+          return;
+        }
+      }
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         if (!masked) {

@@ -232,182 +232,89 @@ __device__ void lds_radix_select(const uint32_t* v, int n, int k, uint32_t lo, u
   need_eq = krem;
 }
 
-__global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void select_kernel(const SelectParams p) {
-  __shared__ SelShared sh;
-  __shared__ uint32_t cval[SEL_CAP];
-  __shared__ int32_t cidx[SEL_CAP];
+// Threshold estimate for a row of more than SEL_CAP candidates: the bit
+// pattern that about `aim` candidates reach, from 128 evenly spaced blocks of
+// 32 consecutive scores (each one 128-byte line: about 3 % of a 114k row;
+// single strided values would touch up to every line of the row).  Two
+// digits (20 bits below the sample's common prefix) are precise enough.
+// cval is LDS scratch of SEL_SAMPLE entries.
+__device__ __forceinline__ uint32_t sample_estimate(const float* row, int64_t n_cand, int64_t aim, uint32_t* cval,
+                                                    SelShared& sh, int& par) {
   const int tid = threadIdx.x;
-  const int qid = xcd_remap(blockIdx.x, gridDim.x);
-  const int i = qid % p.n_q;
-  const int64_t pos = p.q_pos0 + i;
-  const int64_t n = pos + 1;
-  const int max_sel = p.window + p.topk;
-  int32_t* out = p.idx + (int64_t)qid * max_sel;
-  const float* row = p.scores + (int64_t)qid * p.ld_scores;
-  const int64_t n_cand = n > p.window ? n - p.window : 0;
-  int par = 0;  // slot of the next single-barrier scan
+  uint32_t smin = 0xFFFFFFFFu, smax = 0u;
+#pragma unroll
+  for (int h = 0; h < SEL_SPT / 4; ++h) {
+    const int i = tid + h * SEL_THREADS;
+    const int64_t blk = i >> 3;
+    const int64_t start = (blk * (n_cand - 32) / (SEL_SAMPLE / 32 - 1)) & ~(int64_t)31;
+    const f32x4 v = *(const f32x4*)(row + start + 4 * (i & 7));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t u = fbits(v[e]);
+      cval[4 * i + e] = u;
+      smin = min(smin, u);
+      smax = max(smax, u);
+    }
+  }
+  block_min_max(smin, smax, sh);
+  const int r = (int)min<int64_t>(SEL_SAMPLE, max<int64_t>(1, (aim * SEL_SAMPLE + n_cand - 1) / n_cand));
+  uint32_t u_est;
+  int unused;
+  lds_radix_select(cval, SEL_SAMPLE, r, smin, smax, 2, sh, par, u_est, unused);
+  return u_est;
+}
 
-  if (n_cand <= p.topk) {  // every key 0..p is selected
-    for (int j = tid; j < max_sel; j += SEL_THREADS) out[j] = j < n ? j : -1;
-    if (tid == 0) p.count[qid] = (int32_t)n;
-    return;
+// The topk picks among kept candidates held in LDS in index order
+// (cval/cidx[0..kept), topk <= kept, every pick among them, patterns in
+// [kmin, kmax]) -> out[0..topk), ascending.  tau is found exactly: the
+// search runs until every bit below the common prefix is resolved (a 31-bit
+// range, e.g. scores on both sides of 2.0 when they are summed over heads,
+// takes 4 digits of 10 bits).  A pick's output slot is the number of picks
+// before it: the values above tau before it plus the first need_eq ties; one
+// scan of the packed counts (above << 16 | ties) per 4 * SEL_THREADS values.
+__device__ __forceinline__ void pick_from_lds(const uint32_t* cval, const int32_t* cidx, int kept, uint32_t kmin,
+                                              uint32_t kmax, int topk, int32_t* out, SelShared& sh, int& par) {
+  const int tid = threadIdx.x;
+  uint32_t tau;
+  int need_eq;
+  lds_radix_select(cval, kept, topk, kmin, kmax, kRadixExact, sh, par, tau, need_eq);
+  int gt_seen = 0, eq_seen = 0;
+  for (int base = 0; base < kept; base += 4 * SEL_THREADS) {
+    const int j0 = base + 4 * tid;
+    uint32_t u[4];
+    int ngt = 0, neq = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      u[e] = j0 + e < kept ? cval[j0 + e] : 0u;
+      ngt += (j0 + e < kept && u[e] > tau) ? 1 : 0;
+      neq += (j0 + e < kept && u[e] == tau) ? 1 : 0;
+    }
+    int tot;
+    const int pre = block_excl_scan1((ngt << 16) | neq, tid, sh, par, tot);
+    int gt_b = gt_seen + (pre >> 16), eq_b = eq_seen + (pre & 0xffff);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (j0 + e >= kept) continue;
+      if (u[e] > tau) {
+        const int opos = gt_b + min(eq_b, need_eq);
+        if (opos < topk) out[opos] = cidx[j0 + e];
+        ++gt_b;
+      } else if (u[e] == tau) {
+        if (eq_b < need_eq && gt_b + eq_b < topk) out[gt_b + eq_b] = cidx[j0 + e];
+        ++eq_b;
+      }
+    }
+    gt_seen += tot >> 16;
+    eq_seen += tot & 0xffff;
   }
+}
 
-  // ---- sampled path: threshold estimate (0 = keep everything for short rows)
-  uint32_t u_est = 0u;
-  if (n_cand > SEL_CAP) {
-    // 128 evenly spaced blocks of 32 consecutive scores, each one 128-byte
-    // line: about 3 % of the row's bytes (single strided values would touch
-    // up to every line of the row)
-    uint32_t smin = 0xFFFFFFFFu, smax = 0u;
-#pragma unroll
-    for (int h = 0; h < SEL_SPT / 4; ++h) {
-      const int i = tid + h * SEL_THREADS;
-      const int64_t blk = i >> 3;
-      const int64_t start = (blk * (n_cand - 32) / (SEL_SAMPLE / 32 - 1)) & ~(int64_t)31;
-      const f32x4 v = *(const f32x4*)(row + start + 4 * (i & 7));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t u = fbits(v[e]);
-        cval[4 * i + e] = u;
-        smin = min(smin, u);
-        smax = max(smax, u);
-      }
-    }
-    block_min_max(smin, smax, sh);
-    // aim at about 2 topk candidates at or above the estimate (less for a
-    // topk above SEL_CAP / 3, to stay inside the LDS); two digits (20 bits
-    // below the sample's common prefix) are precise enough
-    const int64_t aim = min<int64_t>(2 * (int64_t)p.topk, ((int64_t)p.topk + SEL_CAP) / 2);
-    const int r = (int)min<int64_t>(SEL_SAMPLE, max<int64_t>(1, (aim * SEL_SAMPLE + n_cand - 1) / n_cand));
-    int unused;
-    lds_radix_select(cval, SEL_SAMPLE, r, smin, smax, 2, sh, par, u_est, unused);
-  }
-  // one read of the row: candidates >= u_est into LDS, in index order.  A
-  // round covers 4096 candidates: wave wv takes PIECE consecutive ones, its
-  // kept positions come from ballots and mbcnt, and one barrier orders the
-  // waves.  The loads of the next round are issued before the barrier.  The
-  // smallest and largest kept pattern bound the exact search below.
-  constexpr int PER = 8;
-  constexpr int ROUND = PER * SEL_THREADS;  // candidates per round
-  constexpr int PIECE = PER * kWave;        // consecutive candidates of one wave per round
-  const int lane = tid & 63, wv = tid >> 6;
-  // load q of lane l is the float4 at 256 q + 4 l of the wave's piece
-  auto load16 = [&](int64_t base, uint32_t (&u)[PER]) {
-#pragma unroll
-    for (int q = 0; q < PER / 4; ++q) {
-      const int64_t j = base + PIECE * wv + 256 * q + 4 * lane;
-      if (j + 3 < n_cand) {
-        const f32x4 v = *(const f32x4*)(row + j);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) u[4 * q + e] = fbits(v[e]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) u[4 * q + e] = (j + e < n_cand) ? fbits(row[j + e]) : 0u;
-      }
-    }
-  };
-  int kept = 0;
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  uint32_t ucur[PER], unext[PER];
-  load16(0, ucur);
-  for (int64_t base = 0; base < n_cand; base += ROUND) {
-    if (base + ROUND < n_cand) load16(base + ROUND, unext);
-    uint64_t bal[PER];
-    int wtot = 0;
-#pragma unroll
-    for (int q = 0; q < PER / 4; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t j = base + PIECE * wv + 256 * q + 4 * lane + e;
-        const bool keep = j < n_cand && ucur[4 * q + e] >= u_est;
-        bal[4 * q + e] = __ballot(keep);
-        wtot += __popcll(bal[4 * q + e]);
-        kmin = min(kmin, keep ? ucur[4 * q + e] : 0xFFFFFFFFu);
-        kmax = max(kmax, keep ? ucur[4 * q + e] : 0u);
-      }
-    int* wt = sh.wave_tot2[par];
-    if (lane == 0) wt[wv] = wtot;
-    __syncthreads();
-    int before = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < SEL_WAVES; ++w) {
-      const int t = wt[w];
-      before += (w < wv) ? t : 0;
-      tot += t;
-    }
-    par ^= 1;
-    int pos = kept + before;
-#pragma unroll
-    for (int q = 0; q < PER / 4; ++q) {
-      int p = pos;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        p += __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[4 * q + e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal[4 * q + e], 0));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if ((bal[4 * q + e] >> lane) & 1) {
-          if (p < SEL_CAP) {
-            cval[p] = ucur[4 * q + e];
-            cidx[p] = (int32_t)(base + PIECE * wv + 256 * q + 4 * lane + e);
-          }
-          ++p;
-        }
-        pos += __popcll(bal[4 * q + e]);
-      }
-    }
-    kept += tot;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) ucur[e] = unext[e];
-  }
-  block_min_max(kmin, kmax, sh);
-  if (kept >= p.topk && kept <= SEL_CAP) {
-    // every pick is at or above u_est (at least topk candidates are), so the
-    // exact tau of the row is the topk-th largest of the kept ones.  The pick
-    // code below needs tau exact: the search runs until every bit below the
-    // common prefix is resolved (a 31-bit range, e.g. scores on both sides of
-    // 2.0 when they are summed over heads, takes 4 digits of 10 bits).
-    uint32_t tau;
-    int need_eq;
-    lds_radix_select(cval, kept, p.topk, kmin, kmax, kRadixExact, sh, par, tau, need_eq);
-    // a pick's output slot is the number of picks before it: the values above
-    // tau before it plus the first need_eq ties.  One scan of the packed
-    // counts (above << 16 | ties) per 4 * SEL_THREADS kept values.
-    int gt_seen = 0, eq_seen = 0;
-    for (int base = 0; base < kept; base += 4 * SEL_THREADS) {
-      const int j0 = base + 4 * tid;
-      uint32_t u[4];
-      int ngt = 0, neq = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        u[e] = j0 + e < kept ? cval[j0 + e] : 0u;
-        ngt += (j0 + e < kept && u[e] > tau) ? 1 : 0;
-        neq += (j0 + e < kept && u[e] == tau) ? 1 : 0;
-      }
-      int tot;
-      const int pre = block_excl_scan1((ngt << 16) | neq, tid, sh, par, tot);
-      int gt_b = gt_seen + (pre >> 16), eq_b = eq_seen + (pre & 0xffff);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (j0 + e >= kept) continue;
-        if (u[e] > tau) {
-          const int opos = gt_b + min(eq_b, need_eq);
-          if (opos < p.topk) out[opos] = cidx[j0 + e];
-          ++gt_b;
-        } else if (u[e] == tau) {
-          if (eq_b < need_eq && gt_b + eq_b < p.topk) out[gt_b + eq_b] = cidx[j0 + e];
-          ++eq_b;
-        }
-      }
-      gt_seen += tot >> 16;
-      eq_seen += tot & 0xffff;
-    }
-    for (int w = tid; w < p.window; w += SEL_THREADS) out[p.topk + w] = (int32_t)(n_cand + w);
-    if (tid == 0) p.count[qid] = max_sel;
-    return;
-  }
-  // the estimate was off (too few or too many kept): exact multi-pass radix
-
+// The exact multi-pass selection over a whole row of n_cand > topk
+// candidates -> out[0..topk), ascending: a min/max pass, radix histogram
+// passes below the common prefix, then a block-wide ordered compaction that
+// stops as soon as topk candidates are out.
+__device__ void exact_row(const float* row, int64_t n_cand, int topk, int32_t* out, SelShared& sh, int& par) {
+  const int tid = threadIdx.x;
   // ---- pass 0: smallest and largest candidate bit pattern
   uint32_t mx = 0u, mn = 0xFFFFFFFFu;
   const int64_t n4 = n_cand & ~(int64_t)3;
@@ -425,35 +332,19 @@ __global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(8))
     mx = max(mx, u);
     mn = min(mn, u);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
-  }
-  if ((tid & 63) == 0) {
-    sh.wave_u[tid >> 6] = mx;
-    sh.wave_u[SEL_WAVES + (tid >> 6)] = mn;
-  }
-  __syncthreads();
-  mx = 0u;
-  mn = 0xFFFFFFFFu;
-#pragma unroll
-  for (int w = 0; w < SEL_WAVES; ++w) {
-    mx = max(mx, sh.wave_u[w]);
-    mn = min(mn, sh.wave_u[SEL_WAVES + w]);
-  }
+  block_min_max(mn, mx, sh);
 
   // ---- radix passes below the common prefix
   uint32_t tau;
   int need_eq;  // how many candidates equal to tau are taken (in index order)
   if (mx == mn) {
     tau = mx;
-    need_eq = p.topk;
+    need_eq = topk;
   } else {
     const int hb = 31 - __builtin_clz(mx ^ mn);
     int shift = hb + 1;
     uint64_t prefix = (uint64_t)mx >> shift << shift;  // common high bits
-    int krem = p.topk;
+    int krem = topk;
     while (shift > 0) {
       const int w = shift < SEL_DIGIT ? shift : SEL_DIGIT;
       shift -= w;
@@ -485,7 +376,7 @@ __global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(8))
 
   // ---- ordered compaction: above tau, then the first need_eq ties
   int eq_seen = 0, sel_seen = 0;
-  for (int64_t base = 0; base < n_cand && sel_seen < p.topk; base += 4 * SEL_THREADS) {
+  for (int64_t base = 0; base < n_cand && sel_seen < topk; base += 4 * SEL_THREADS) {
     const int64_t j0 = base + 4 * (int64_t)tid;
     uint32_t u[4];
     if (j0 + 3 < n_cand) {
@@ -516,260 +407,361 @@ __global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(8))
     int opos = sel_seen + block_excl_scan(sel_cnt, tid, sh, sel_total);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (sel[e] && opos < p.topk) out[opos++] = (int32_t)(j0 + e);
+      if (sel[e] && opos < topk) out[opos++] = (int32_t)(j0 + e);
     eq_seen += eq_total;
     sel_seen += sel_total;
   }
+}
+
+// One read of candidates [c0, c0 + 8 * SEL_THREADS) of a row (n_cand of
+// them): wave wv takes the 512 consecutive ones from c0 + 512 wv, lane l the
+// float4s at 256 q + 4 l of that piece (patterns past n_cand read as 0).
+constexpr int SEL_PER = 8;
+constexpr int SEL_ROUND = SEL_PER * SEL_THREADS;  // candidates per round
+constexpr int SEL_PIECE = SEL_PER * kWave;        // consecutive candidates of one wave per round
+__device__ __forceinline__ void load_round(const float* row, int64_t n_cand, int64_t c0, uint32_t (&u)[SEL_PER]) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < SEL_PER / 4; ++q) {
+    const int64_t j = c0 + SEL_PIECE * wv + 256 * q + 4 * lane;
+    if (j + 3 < n_cand) {
+      const f32x4 v = *(const f32x4*)(row + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[4 * q + e] = fbits(v[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[4 * q + e] = (j + e < n_cand) ? fbits(row[j + e]) : 0u;
+    }
+  }
+}
+__device__ __forceinline__ int64_t round_index(int64_t c0, int q, int e) {
+  return c0 + SEL_PIECE * (threadIdx.x >> 6) + 256 * q + 4 * (threadIdx.x & 63) + e;
+}
+
+__global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void select_kernel(const SelectParams p) {
+  __shared__ SelShared sh;
+  __shared__ uint32_t cval[SEL_CAP];
+  __shared__ int32_t cidx[SEL_CAP];
+  const int tid = threadIdx.x;
+  const int qid = xcd_remap(blockIdx.x, gridDim.x);
+  const int i = qid % p.n_q;
+  const int64_t pos = p.q_pos0 + i;
+  const int64_t n = pos + 1;
+  const int max_sel = p.window + p.topk;
+  int32_t* out = p.idx + (int64_t)qid * max_sel;
+  const float* row = p.scores + (int64_t)qid * p.ld_scores;
+  const int64_t n_cand = n > p.window ? n - p.window : 0;
+  int par = 0;  // slot of the next single-barrier scan
+
+  if (n_cand <= p.topk) {  // every key 0..p is selected
+    for (int j = tid; j < max_sel; j += SEL_THREADS) out[j] = j < n ? j : -1;
+    if (tid == 0) p.count[qid] = (int32_t)n;
+    return;
+  }
+
+  // ---- sampled path: threshold estimate (0 = keep everything for short rows)
+  // aiming at about 2 topk candidates (less for a topk above SEL_CAP / 3, to
+  // stay inside the LDS)
+  uint32_t u_est = 0u;
+  if (n_cand > SEL_CAP)
+    u_est = sample_estimate(row, n_cand, min<int64_t>(2 * (int64_t)p.topk, ((int64_t)p.topk + SEL_CAP) / 2), cval,
+                            sh, par);
+  // one read of the row: candidates >= u_est into LDS, in index order.  A
+  // round covers 4096 candidates: each wave takes SEL_PIECE consecutive ones,
+  // its kept positions come from ballots and mbcnt, and one barrier orders the
+  // waves.  The loads of the next round are issued before the barrier.  The
+  // smallest and largest kept pattern bound the exact search below.
+  const int lane = tid & 63, wv = tid >> 6;
+  int kept = 0;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  uint32_t ucur[SEL_PER], unext[SEL_PER];
+  load_round(row, n_cand, 0, ucur);
+  for (int64_t base = 0; base < n_cand; base += SEL_ROUND) {
+    if (base + SEL_ROUND < n_cand) load_round(row, n_cand, base + SEL_ROUND, unext);
+    uint64_t bal[SEL_PER];
+    int wtot = 0;
+#pragma unroll
+    for (int q = 0; q < SEL_PER / 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool keep = round_index(base, q, e) < n_cand && ucur[4 * q + e] >= u_est;
+        bal[4 * q + e] = __ballot(keep);
+        wtot += __popcll(bal[4 * q + e]);
+        kmin = min(kmin, keep ? ucur[4 * q + e] : 0xFFFFFFFFu);
+        kmax = max(kmax, keep ? ucur[4 * q + e] : 0u);
+      }
+    int* wt = sh.wave_tot2[par];
+    if (lane == 0) wt[wv] = wtot;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < SEL_WAVES; ++w) {
+      const int t = wt[w];
+      before += (w < wv) ? t : 0;
+      tot += t;
+    }
+    par ^= 1;
+    int pos = kept + before;
+#pragma unroll
+    for (int q = 0; q < SEL_PER / 4; ++q) {
+      int p = pos;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        p += __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[4 * q + e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal[4 * q + e], 0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if ((bal[4 * q + e] >> lane) & 1) {
+          if (p < SEL_CAP) {
+            cval[p] = ucur[4 * q + e];
+            cidx[p] = (int32_t)round_index(base, q, e);
+          }
+          ++p;
+        }
+        pos += __popcll(bal[4 * q + e]);
+      }
+    }
+    kept += tot;
+#pragma unroll
+    for (int e = 0; e < SEL_PER; ++e) ucur[e] = unext[e];
+  }
+  block_min_max(kmin, kmax, sh);
+  // every pick is at or above u_est when at least topk candidates are, so the
+  // exact tau of the row is the topk-th largest of the kept ones; otherwise
+  // (the estimate was off: too few or too many kept) the exact multi-pass radix
+  if (kept >= p.topk && kept <= SEL_CAP)
+    pick_from_lds(cval, cidx, kept, kmin, kmax, p.topk, out, sh, par);
+  else
+    exact_row(row, n_cand, p.topk, out, sh, par);
   for (int w = tid; w < p.window; w += SEL_THREADS) out[p.topk + w] = (int32_t)(n_cand + w);
   if (tid == 0) p.count[qid] = max_sel;
 }
 
 // ---------------------------------------------------------------------------
-// Few long rows (decode): the same selection, spread over many workgroups per
-// row.  The radix digits are fixed (bits 30-20, 19-9, 8-0 of the non-negative
-// float32 pattern); each pass is one launch that histograms its segment of
-// the row (LDS, then integer atomics into the row's global histogram, so the
-// counts do not depend on the order).  Every workgroup of a later launch
-// derives the digits picked so far from those histograms itself.  Then one
-// launch counts, per segment, the candidates above tau and equal to tau, and
-// the last one writes each segment's picks at their ascending positions.
-constexpr int MB_THREADS = 256;
-constexpr int MB_PER_THREAD = 16;
-constexpr int MB_SEG = MB_THREADS * MB_PER_THREAD;  // candidates per workgroup
-constexpr int MB_MAX_ROWS = 64;
-constexpr int MB_MIN_CAND = 32768;
-constexpr int MB_BINS = 2048;
+// Few long rows (decode: at most 64 rows of at least FR_MIN_CAND candidates):
+// the same selection with the row's one read spread over many workgroups.
+//   fr_compact_kernel: grid (segments of 4096 candidates, rows).  Every
+//     workgroup of a row derives the same threshold estimate from the same
+//     sample (no launch and no wait for it), then compacts the candidates of
+//     its segment at or above it, in index order, into the segment's slot of
+//     the workspace (at most FR_SCAP of them) and writes how many there are.
+//   fr_final_kernel: one workgroup per row.  A scan of the segment counts
+//     places each segment's candidates; they are gathered into LDS in index
+//     order (a segment that kept more than its slot holds is read again from
+//     the row), and the LDS selection of the single-read path picks tau and
+//     the output.  When the estimate kept fewer than topk or more than
+//     FR_KCAP candidates, the exact multi-pass selection reads the row instead.
+// Every count has its own slot and every position comes from a scan, so the
+// result does not depend on timing; nothing needs clearing between calls.
+constexpr int FR_SEG = SEL_ROUND;   // candidates per segment workgroup (one round)
+constexpr int FR_SCAP = 512;        // kept candidates stored per segment
+constexpr int FR_KCAP = 8192;       // kept candidates of a row gathered into LDS (64 KB)
+constexpr int FR_MAX_ROWS = 64;
+constexpr int FR_MIN_CAND = 24576;
 
-struct MbWs {
-  int* hist;     // [rows][3][MB_BINS]
-  int* bcount;   // [rows][nblk][2]: candidates above tau, equal to tau
-  int nblk;
+struct FrWs {
+  uint32_t* u_est;   // [rows]: the threshold estimate of each row
+  int* count;        // [rows][nseg]: candidates at or above it in each segment
+  uint2* kept;       // [rows][nseg][FR_SCAP]: (pattern, index) of the first FR_SCAP of them
+  int nseg;
 };
 
-__device__ __forceinline__ int mb_shift(int pass) { return pass == 0 ? 20 : (pass == 1 ? 9 : 0); }
-__device__ __forceinline__ int mb_width(int pass) { return pass == 2 ? 9 : 11; }
-
-struct MbShared {
-  int part[MB_THREADS];
-  int digit, above;
-  int cnt[2 * MB_THREADS / kWave];
-  int lh[MB_BINS];
-};
-
-// Digits of passes 0..npass-1 from the row's histograms: returns the common
-// prefix (bits above the next digit) and how many picks remain inside it.
-__device__ void mb_prefix(const int* hist_row, int npass, int topk, MbShared& sh, uint32_t& prefix, int& krem) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  prefix = 0u;
-  krem = topk;
-  for (int pass = 0; pass < npass; ++pass) {
-    const int nb = 1 << mb_width(pass);
-    const int per = nb / MB_THREADS;             // 8 (11-bit digits) or 2 (9-bit)
-    const int* h = hist_row + pass * MB_BINS;
-    // thread t owns digits nb-1-per*t down to nb-per*(t+1): the scan runs from
-    // the top digit down
-    int c = 0;
-    for (int i = 0; i < per; ++i) c += h[nb - 1 - per * tid - i];
-    const int inc = wave_incl_scan(c, lane);
-    if (lane == 63) sh.cnt[wave] = inc;
-    __syncthreads();
-    int before = inc - c;
-    for (int w = 0; w < wave; ++w) before += sh.cnt[w];
-    if (before < krem && krem <= before + c) {   // exactly one thread: the total is >= krem
-      int cum = before, d = nb - 1 - per * tid;
-      for (int i = 0; i < per - 1; ++i, --d) {
-        const int hv = h[d];
-        if (cum + hv >= krem) break;
-        cum += hv;
-      }
-      sh.digit = d;
-      sh.above = cum;
-    }
-    __syncthreads();
-    prefix |= (uint32_t)sh.digit << mb_shift(pass);
-    krem -= sh.above;
-    __syncthreads();
-  }
+// about 3 topk candidates at or above the estimate: a sample of 4096 then
+// misses below topk or above FR_KCAP rarely even on rows of 2^20 candidates
+__device__ __forceinline__ int64_t fr_aim(int topk) {
+  return min<int64_t>(3 * (int64_t)topk, ((int64_t)topk + FR_KCAP) / 2);
 }
 
-__global__ __launch_bounds__(256) void mb_zero_kernel(int* p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
-}
-
-template <int PASS>
-__global__ __launch_bounds__(MB_THREADS) void mb_hist_kernel(const SelectParams p, const MbWs ws) {
-  __shared__ MbShared sh;
-  const int tid = threadIdx.x, row = blockIdx.y;
+__global__ __launch_bounds__(SEL_THREADS) void fr_compact_kernel(const SelectParams p, const FrWs ws) {
+  __shared__ SelShared sh;
+  __shared__ uint32_t cval[SEL_SAMPLE];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int row = blockIdx.y, seg = blockIdx.x;
   const int64_t n_cand = p.q_pos0 + row % p.n_q + 1 - p.window;
-  const int64_t s0 = (int64_t)blockIdx.x * MB_SEG;
-  if (n_cand <= p.topk || s0 >= n_cand) return;
-  int* hist_row = ws.hist + (int64_t)row * 3 * MB_BINS;
-  uint32_t prefix;
-  int krem;
-  mb_prefix(hist_row, PASS, p.topk, sh, prefix, krem);
-  for (int b = tid; b < MB_BINS; b += MB_THREADS) sh.lh[b] = 0;
-  __syncthreads();
-  const int sh_lo = mb_shift(PASS), w = mb_width(PASS);
-  const uint32_t want = PASS == 0 ? 0u : prefix >> (sh_lo + w);
+  const int64_t c0 = (int64_t)seg * FR_SEG;
+  if (n_cand <= p.topk || c0 >= n_cand) return;
   const float* rowp = p.scores + (int64_t)row * p.ld_scores;
+  uint32_t u[SEL_PER];
+  load_round(rowp, n_cand, c0, u);   // in flight during the estimate
+  int par = 0;
+  const uint32_t u_est = sample_estimate(rowp, n_cand, fr_aim(p.topk), cval, sh, par);
+  uint64_t bal[SEL_PER];
+  int wtot = 0;
 #pragma unroll
-  for (int r = 0; r < MB_PER_THREAD / 4; ++r) {
-    const int64_t j = s0 + 1024 * r + 4 * tid;
-    uint32_t u[4];
-    if (j + 3 < n_cand) {
-      const f32x4 v = *(const f32x4*)(rowp + j);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) u[e] = fbits(v[e]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) u[e] = (j + e < n_cand) ? fbits(rowp[j + e]) : 0xFFFFFFFFu;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (u[e] != 0xFFFFFFFFu && (u[e] >> (sh_lo + w)) == want) atomicAdd(&sh.lh[(u[e] >> sh_lo) & ((1 << w) - 1)], 1);
-  }
-  __syncthreads();
-  int* gh = hist_row + PASS * MB_BINS;
-  for (int b = tid; b < (1 << w); b += MB_THREADS)
-    if (sh.lh[b]) atomicAdd(&gh[b], sh.lh[b]);
-}
-
-// Candidates above tau and equal to tau in each segment.
-__global__ __launch_bounds__(MB_THREADS) void mb_count_kernel(const SelectParams p, const MbWs ws) {
-  __shared__ MbShared sh;
-  const int tid = threadIdx.x, row = blockIdx.y;
-  const int64_t n_cand = p.q_pos0 + row % p.n_q + 1 - p.window;
-  const int64_t s0 = (int64_t)blockIdx.x * MB_SEG;
-  if (n_cand <= p.topk || s0 >= n_cand) return;
-  uint32_t tau;
-  int need_eq;
-  mb_prefix(ws.hist + (int64_t)row * 3 * MB_BINS, 3, p.topk, sh, tau, need_eq);
-  const float* rowp = p.scores + (int64_t)row * p.ld_scores;
-  int above = 0, eq = 0;
-#pragma unroll
-  for (int r = 0; r < MB_PER_THREAD / 4; ++r) {
-    const int64_t j = s0 + 1024 * r + 4 * tid;
+  for (int q = 0; q < SEL_PER / 4; ++q)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (j + e < n_cand) {
-        const uint32_t u = fbits(rowp[j + e]);
-        above += u > tau;
-        eq += u == tau;
-      }
+      const bool keep = round_index(c0, q, e) < n_cand && u[4 * q + e] >= u_est;
+      bal[4 * q + e] = __ballot(keep);
+      wtot += __popcll(bal[4 * q + e]);
     }
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    above += __shfl_xor(above, o, kWave);
-    eq += __shfl_xor(eq, o, kWave);
-  }
-  if ((tid & 63) == 0) {
-    sh.cnt[2 * (tid >> 6)] = above;
-    sh.cnt[2 * (tid >> 6) + 1] = eq;
-  }
+  int* wt = sh.wave_tot2[par];
+  if (lane == 0) wt[wv] = wtot;
   __syncthreads();
-  if (tid == 0) {
-    int a = 0, q = 0;
-    for (int wv = 0; wv < MB_THREADS / kWave; ++wv) {
-      a += sh.cnt[2 * wv];
-      q += sh.cnt[2 * wv + 1];
+  int pos = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < SEL_WAVES; ++w) {
+    const int t = wt[w];
+    pos += (w < wv) ? t : 0;
+    tot += t;
+  }
+  const int64_t slot = (int64_t)row * ws.nseg + seg;
+  uint2* dst = ws.kept + slot * FR_SCAP;
+#pragma unroll
+  for (int q = 0; q < SEL_PER / 4; ++q) {
+    int pp = pos;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      pp += __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[4 * q + e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal[4 * q + e], 0));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if ((bal[4 * q + e] >> lane) & 1) {
+        if (pp < FR_SCAP) dst[pp] = make_uint2(u[4 * q + e], (uint32_t)round_index(c0, q, e));
+        ++pp;
+      }
+      pos += __popcll(bal[4 * q + e]);
     }
-    int* bc = ws.bcount + ((int64_t)row * ws.nblk + blockIdx.x) * 2;
-    bc[0] = a;
-    bc[1] = q;
+  }
+  if (tid == 0) {
+    ws.count[slot] = tot;
+    if (seg == 0) ws.u_est[row] = u_est;
   }
 }
 
-// Each segment writes its picks at their ascending positions; segment 0 also
-// writes the window, the count, and the rows that keep every key.
-__global__ __launch_bounds__(MB_THREADS) void mb_write_kernel(const SelectParams p, const MbWs ws) {
-  __shared__ MbShared sh;
-  __shared__ SelShared ssh;
-  const int tid = threadIdx.x, row = blockIdx.y;
-  const int64_t pos = p.q_pos0 + row % p.n_q;
-  const int64_t n = pos + 1;
+__global__ __launch_bounds__(SEL_THREADS) void fr_final_kernel(const SelectParams p, const FrWs ws) {
+  __shared__ SelShared sh;
+  __shared__ uint32_t cval[FR_KCAP];
+  __shared__ int32_t cidx[FR_KCAP];
+  __shared__ int seg_cnt[SEL_THREADS], seg_pos[SEL_THREADS];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int row = blockIdx.x;
+  const int64_t n = p.q_pos0 + row % p.n_q + 1;
   const int64_t n_cand = n - p.window;
   const int max_sel = p.window + p.topk;
   int32_t* out = p.idx + (int64_t)row * max_sel;
-  const int64_t s0 = (int64_t)blockIdx.x * MB_SEG;
-  if (n_cand <= p.topk) {
-    if (blockIdx.x == 0) {
-      for (int j = tid; j < max_sel; j += MB_THREADS) out[j] = j < n ? j : -1;
-      if (tid == 0) p.count[row] = (int32_t)n;
-    }
+  if (n_cand <= p.topk) {  // every key 0..p is selected
+    for (int j = tid; j < max_sel; j += SEL_THREADS) out[j] = j < n ? (int32_t)j : -1;
+    if (tid == 0) p.count[row] = (int32_t)n;
     return;
   }
-  if (blockIdx.x == 0) {
-    for (int w = tid; w < p.window; w += MB_THREADS) out[p.topk + w] = (int32_t)(n_cand + w);
-    if (tid == 0) p.count[row] = max_sel;
-  }
-  if (s0 >= n_cand) return;
-  uint32_t tau;
-  int need_eq;
-  mb_prefix(ws.hist + (int64_t)row * 3 * MB_BINS, 3, p.topk, sh, tau, need_eq);
-  // picks and ties in the segments before this one
-  int sel_before = 0, eq_before = 0;
-  const int* bc = ws.bcount + (int64_t)row * ws.nblk * 2;
-  for (int b = tid; b < (int)blockIdx.x; b += MB_THREADS) {
-    sel_before += bc[2 * b];
-    eq_before += bc[2 * b + 1];
-  }
-  int tot;
-  (void)block_excl_scan_n<MB_THREADS>(sel_before, tid, ssh, tot);
-  sel_before = tot;
-  (void)block_excl_scan_n<MB_THREADS>(eq_before, tid, ssh, tot);
-  eq_before = tot;
-  // ties taken before this segment: the first need_eq ties in index order
-  sel_before += min(eq_before, need_eq);
   const float* rowp = p.scores + (int64_t)row * p.ld_scores;
-  int eq_seen = eq_before, sel_seen = sel_before;
+  const int nseg = (int)((n_cand + FR_SEG - 1) / FR_SEG);
+  const int* cnt = ws.count + (int64_t)row * ws.nseg;
+  int par = 0;
+  // candidates kept over the whole row
+  int64_t total = 0;
+  for (int s0 = 0; s0 < nseg; s0 += SEL_THREADS) {
+    int t;
+    (void)block_excl_scan1(s0 + tid < nseg ? cnt[s0 + tid] : 0, tid, sh, par, t);
+    total += t;
+  }
+  if (total >= p.topk && total <= FR_KCAP) {
+    const uint32_t u_est = ws.u_est[row];
+    int64_t placed = 0;
+    for (int s0 = 0; s0 < nseg; s0 += SEL_THREADS) {
+      const int c = s0 + tid < nseg ? cnt[s0 + tid] : 0;
+      int t;
+      const int before = block_excl_scan1(c, tid, sh, par, t);
+      seg_cnt[tid] = c;
+      seg_pos[tid] = (int)placed + before;
+      __syncthreads();
+      const int nb = min(SEL_THREADS, nseg - s0);
+      // the stored candidates: a thread per kept position of the batch, the
+      // segment found by a binary search of the positions, every load issued
+      // before the first LDS write (one memory latency for the batch)
+      constexpr int PER_T = FR_KCAP / SEL_THREADS;
+      uint2 ev[PER_T];
+      int dst[PER_T];
 #pragma unroll
-  for (int r = 0; r < MB_PER_THREAD / 4; ++r) {
-    const int64_t j0 = s0 + 1024 * r + 4 * tid;
-    uint32_t u[4];
+      for (int r = 0; r < PER_T; ++r) {
+        const int j = tid + r * SEL_THREADS;   // position inside the batch
+        dst[r] = -1;
+        if (j < t) {
+          int lo = 0, hi = nb - 1;   // the last segment that starts at or before j
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (seg_pos[mid] - (int)placed <= j) lo = mid; else hi = mid - 1;
+          }
+          if (seg_cnt[lo] <= FR_SCAP) {
+            ev[r] = ws.kept[((int64_t)row * ws.nseg + s0 + lo) * FR_SCAP + (j - (seg_pos[lo] - (int)placed))];
+            dst[r] = (int)placed + j;
+          }
+        }
+      }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) u[e] = (j0 + e < n_cand) ? fbits(rowp[j0 + e]) : 0u;
-    int eq_cnt = 0;
+      for (int r = 0; r < PER_T; ++r) {
+        if (dst[r] >= 0) {
+          cval[dst[r]] = ev[r].x;
+          cidx[dst[r]] = (int32_t)ev[r].y;
+        }
+      }
+      for (int s = wv; s < nb; s += SEL_WAVES) {
+        const int cs = seg_cnt[s], ps = seg_pos[s];
+        if (cs > FR_SCAP) {
+          // more than the slot holds: this wave compacts the segment again
+          // from the row (the same candidates, the same order)
+          const int64_t c0 = (int64_t)(s0 + s) * FR_SEG;
+          const int64_t c1 = min(n_cand, c0 + FR_SEG);
+          int wpos = ps;
+          for (int64_t j0 = c0; j0 < c1; j0 += 4 * kWave) {
+            const int64_t j = j0 + 4 * lane;
+            uint32_t u4[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) eq_cnt += (j0 + e < n_cand && u[e] == tau) ? 1 : 0;
-    int eq_total;
-    int eq_rank = eq_seen + block_excl_scan_n<MB_THREADS>(eq_cnt, tid, ssh, eq_total);
-    bool sel[4];
-    int sel_cnt = 0;
+            for (int e = 0; e < 4; ++e) u4[e] = j + e < c1 ? fbits(rowp[j + e]) : 0u;
+            uint64_t b4[4];
+            int pp = wpos;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool valid = j0 + e < n_cand;
-      const bool gt = valid && u[e] > tau;
-      const bool eq = valid && u[e] == tau;
-      sel[e] = gt || (eq && eq_rank < need_eq);
-      eq_rank += eq ? 1 : 0;
-      sel_cnt += sel[e] ? 1 : 0;
+            for (int e = 0; e < 4; ++e) {
+              b4[e] = __ballot(j + e < c1 && u4[e] >= u_est);
+              pp += __builtin_amdgcn_mbcnt_hi((uint32_t)(b4[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b4[e], 0));
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if ((b4[e] >> lane) & 1) {
+                cval[pp] = u4[e];
+                cidx[pp] = (int32_t)(j + e);
+                ++pp;
+              }
+              wpos += __popcll(b4[e]);
+            }
+          }
+        }
+      }
+      placed += t;
+      __syncthreads();
     }
-    int sel_total;
-    int opos = sel_seen + block_excl_scan_n<MB_THREADS>(sel_cnt, tid, ssh, sel_total);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (sel[e] && opos < p.topk) out[opos++] = (int32_t)(j0 + e);
-    eq_seen += eq_total;
-    sel_seen += sel_total;
+    const int kept = (int)total;
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    for (int j = tid; j < kept; j += SEL_THREADS) {
+      kmin = min(kmin, cval[j]);
+      kmax = max(kmax, cval[j]);
+    }
+    block_min_max(kmin, kmax, sh);
+    pick_from_lds(cval, cidx, kept, kmin, kmax, p.topk, out, sh, par);
+  } else {
+    exact_row(rowp, n_cand, p.topk, out, sh, par);
   }
+  for (int w = tid; w < p.window; w += SEL_THREADS) out[p.topk + w] = (int32_t)(n_cand + w);
+  if (tid == 0) p.count[row] = max_sel;
 }
 
-bool select_multi_block(int B, int n_q, int64_t q_pos0, int window) {
+bool select_few_rows(int B, int n_q, int64_t q_pos0, int window) {
   const int64_t max_cand = q_pos0 + n_q - window;
-  return (int64_t)B * n_q <= MB_MAX_ROWS && max_cand >= MB_MIN_CAND;
+  return (int64_t)B * n_q <= FR_MAX_ROWS && max_cand >= FR_MIN_CAND;
 }
 
-size_t mb_layout(int rows, int64_t max_cand, char* base, MbWs* ws) {
-  const int nblk = (int)((max_cand + MB_SEG - 1) / MB_SEG);
-  const size_t hist_bytes = ((size_t)rows * 3 * MB_BINS * 4 + 255) & ~(size_t)255;
-  const size_t cnt_bytes = ((size_t)rows * nblk * 2 * 4 + 255) & ~(size_t)255;
+size_t fr_layout(int rows, int64_t max_cand, char* base, FrWs* ws) {
+  const int64_t nseg = (max_cand + FR_SEG - 1) / FR_SEG;
+  auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t est_bytes = a256((size_t)rows * 4);
+  const size_t cnt_bytes = a256((size_t)rows * nseg * 4);
+  const size_t kept_bytes = a256((size_t)rows * nseg * FR_SCAP * 8);
   if (ws) {
-    ws->hist = (int*)base;
-    ws->bcount = (int*)(base + hist_bytes);
-    ws->nblk = nblk;
+    ws->u_est = (uint32_t*)base;
+    ws->count = (int*)(base + est_bytes);
+    ws->kept = (uint2*)(base + est_bytes + cnt_bytes);
+    ws->nseg = (int)nseg;
   }
-  return hist_bytes + cnt_bytes;
+  return est_bytes + cnt_bytes + kept_bytes;
 }
 
 // ---- block-level selection (the granularity token-level selection replaces) ----
@@ -899,28 +891,21 @@ __global__ __launch_bounds__(SEL_THREADS) void block_select_kernel(const SelectP
 // Sized for the smallest window (1), which has the most candidates: the launch
 // with the caller's window needs at most this much, or none.
 size_t select_workspace_bytes(int B, int n_q, int64_t /*T*/, int64_t q_pos0) {
-  if (!select_multi_block(B, n_q, q_pos0, 1)) return 0;
-  return mb_layout(B * n_q, q_pos0 + n_q - 1, nullptr, nullptr);
+  if (!select_few_rows(B, n_q, q_pos0, 1)) return 0;
+  return fr_layout(B * n_q, q_pos0 + n_q - 1, nullptr, nullptr);
 }
 
 hipError_t launch_select(const SelectParams& p, void* ws_ptr, size_t /*ws_bytes*/, hipStream_t stream) {
   if (p.B * p.n_q == 0) return hipSuccess;
-  if (!select_multi_block(p.B, p.n_q, p.q_pos0, p.window)) {
+  if (!select_few_rows(p.B, p.n_q, p.q_pos0, p.window)) {
     hipLaunchKernelGGL(select_kernel, dim3((unsigned)(p.B * p.n_q)), dim3(SEL_THREADS), 0, stream, p);
     return hipGetLastError();
   }
   const int rows = p.B * p.n_q;
-  MbWs ws;
-  mb_layout(rows, p.q_pos0 + p.n_q - p.window, (char*)ws_ptr, &ws);
-  const int64_t nh = (int64_t)rows * 3 * MB_BINS;
-  hipLaunchKernelGGL(mb_zero_kernel, dim3((unsigned)((nh + 255) / 256 < 1024 ? (nh + 255) / 256 : 1024)), dim3(256), 0,
-                     stream, ws.hist, nh);
-  const dim3 grid((unsigned)ws.nblk, (unsigned)rows);
-  hipLaunchKernelGGL(mb_hist_kernel<0>, grid, dim3(MB_THREADS), 0, stream, p, ws);
-  hipLaunchKernelGGL(mb_hist_kernel<1>, grid, dim3(MB_THREADS), 0, stream, p, ws);
-  hipLaunchKernelGGL(mb_hist_kernel<2>, grid, dim3(MB_THREADS), 0, stream, p, ws);
-  hipLaunchKernelGGL(mb_count_kernel, grid, dim3(MB_THREADS), 0, stream, p, ws);
-  hipLaunchKernelGGL(mb_write_kernel, grid, dim3(MB_THREADS), 0, stream, p, ws);
+  FrWs ws;
+  fr_layout(rows, p.q_pos0 + p.n_q - p.window, (char*)ws_ptr, &ws);
+  hipLaunchKernelGGL(fr_compact_kernel, dim3((unsigned)ws.nseg, (unsigned)rows), dim3(SEL_THREADS), 0, stream, p, ws);
+  hipLaunchKernelGGL(fr_final_kernel, dim3((unsigned)rows), dim3(SEL_THREADS), 0, stream, p, ws);
   return hipGetLastError();
 }
 

@@ -40,6 +40,7 @@ constexpr int kSmemBytes = (SP_WAVES * kWaveBytes > kRedBytes) ? SP_WAVES * kWav
 
 constexpr int SP_SPLIT_KEYS = 128;   // selected keys per workgroup in the split form
 constexpr int SP_SPLIT_MAXQ = 64;     // queries (B * n_q) up to which the set is split
+constexpr int SP_MAX_PIECES = (kMaxSelect + SP_SPLIT_KEYS - 1) / SP_SPLIT_KEYS;   // pieces of the largest set
 
 struct SparseWs {
   float* m;   // [B*n_q][nsplit][16]
@@ -273,20 +274,30 @@ template <int QKIND>
 __global__ __launch_bounds__(256) void sparse_merge_kernel(const SparseParams p, const SparseWs ws) {
   const int qid = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
   const int64_t b0 = (int64_t)qid * ws.nsplit * 16 + h;
+  // every piece's (max, sum, O) is loaded up front (indices past the last
+  // piece repeat it and are masked), so the merge costs one memory latency
+  float mc[SP_MAX_PIECES], zc[SP_MAX_PIECES], oc[SP_MAX_PIECES];
+#pragma unroll
+  for (int i = 0; i < SP_MAX_PIECES; ++i) {
+    const int64_t c = b0 + (int64_t)min(i, ws.nsplit - 1) * 16;
+    mc[i] = ws.m[c];
+    zc[i] = ws.z[c];
+    oc[i] = ws.o[c * kHeadDim + d];
+  }
   float M = kNegInf;
-  for (int i = 0; i < ws.nsplit; ++i) M = fmaxf(M, ws.m[b0 + i * 16]);
+#pragma unroll
+  for (int i = 0; i < SP_MAX_PIECES; ++i) {
+    if (i >= ws.nsplit) mc[i] = kNegInf;
+    M = fmaxf(M, mc[i]);
+  }
   float Z = 0.f, acc = 0.f;
-  // no branch around the loads, so that several pieces are in flight at once;
   // a piece without keys is masked by a select (its z and o may hold any bits)
-#pragma unroll 8
-  for (int i = 0; i < ws.nsplit; ++i) {
-    const float mi = ws.m[b0 + i * 16];
-    const float zi = ws.z[b0 + i * 16];
-    const float oi = ws.o[(b0 + i * 16) * kHeadDim + d];
-    const bool ok = mi != kNegInf;
-    const float f = fast_exp2(mi - M);
-    Z += ok ? zi * f : 0.f;
-    acc += ok ? oi * f : 0.f;
+#pragma unroll
+  for (int i = 0; i < SP_MAX_PIECES; ++i) {
+    const bool ok = mc[i] != kNegInf;
+    const float f = fast_exp2(mc[i] - M);
+    Z += ok ? zc[i] * f : 0.f;
+    acc += ok ? oc[i] * f : 0.f;
   }
   const float out = Z > 0.f ? acc / Z : 0.f;
   const int64_t oi = ((int64_t)qid * gridDim.y + h) * kHeadDim + d;
