@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--chunk", type=int, default=32768, help="queries per full-attention call")
     ap.add_argument("--workload", default="prefill_128k")
-    ap.add_argument("--cpu-rows", type=int, default=74, help="oracle sample size (rows)")
+    ap.add_argument("--cpu-rows", type=int, default=160, help="oracle sample size (rows)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the decode (16 x 32k, 1M FP8) and bridge (64k) workload lines")
@@ -647,10 +647,16 @@ def other_workloads(dev, rec=None, with_cpu=True):
     win, topk, ms = 128, 1024, 128 + 1024
     scale = 1.0 / 16
 
-    def decode_step(q, qs, k, v, T, p, ks=None, vs=None):
+    graph_rec = {}
+
+    def decode_step(q, qs, k, v, T, p, ks=None, vs=None, graph_key=None):
+        """Stage times (ms) of one decode step; with graph_key, the same step is also captured
+        as one HIP graph, replayed (cold, like the eager step) and checked against the eager
+        outputs byte for byte; the result goes to graph_rec[graph_key]."""
         B, _, H, _ = q.shape
         kvd = hs2._dtype_code(k)
         ws = hs2.workspace(hs2.full_attn_workspace_bytes(B, 1, H, T, kvd), dev)
+        ws_sel = hs2.workspace(hs2.select_workspace_bytes(B, 1, T, p), dev)
         o = torch.empty_like(q)
         lse = torch.empty((B, 1, H), dtype=torch.float32, device=dev)
         ld = (p + 1 + 3) // 4 * 4
@@ -665,13 +671,37 @@ def other_workloads(dev, rec=None, with_cpu=True):
             hs2.hs2_full_attn_scored(q, k, v, q_pos0=p, sm_scale=scale, k_scale=ks, v_scale=vs, o=o, lse=lse,
                                      scores=sc, ld_scores=ld, ws=ws)
             mark()
-            hs2.hs2_select_topk_window(sc, q_pos0=p, T=T, idx=idx, count=cnt)
+            hs2.hs2_select_topk_window(sc, q_pos0=p, T=T, idx=idx, count=cnt, ws=ws_sel)
             mark()
             for i, x in enumerate(qs):
                 hs2.hs2_sparse_attn_reuse(x, k, v, idx, cnt, sm_scale=scale, k_scale=ks, v_scale=vs, o=o2[i],
                                           lse=l2[i], ws=ws_sp)
             mark()
-        return _timed(run, 3, flush=flush)
+        t = _timed(run, 3, flush=flush)
+        if graph_key is not None:
+            outs = [o, lse, sc, idx, cnt, *o2, *l2]
+            ref = [x.clone() for x in outs]
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                run(lambda: None)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                run(lambda: None)
+            same = True
+            for x in outs:
+                x.fill_(7)
+            g.replay()
+            torch.cuda.synchronize()
+            for a, b in zip(ref, outs):
+                same &= bool(torch.equal(a.view(torch.uint8), b.view(torch.uint8)))
+            tg = _timed(lambda mark: (g.replay(), mark()), 1, flush=flush)
+            graph_rec[graph_key] = {"graph_ms_per_step": float(tg[0]), "eager_ms_per_step": float(t.sum()),
+                                    "graph_replay_matches_eager": same}
+            del g
+        return t
 
     def prefill_over_bridge(wl, kl, vl, ksl=None, vsl=None):
         """Every prompt position runs the cross-decoder on the bridged cache: per full layer,
@@ -732,7 +762,7 @@ def other_workloads(dev, rec=None, with_cpu=True):
     wl = inputs.WORKLOADS["decode_b16_32k"]
     inp = inputs.attention_inputs(B=wl.B, n_q=1, T=wl.T, H=wl.H, d=D, kv="bf16", n_sparse=wl.n_sparse, seed=wl.seed,
                                   device=dev)
-    t_fa, t_sel, t_sp = decode_step(inp["q"], inp["q_sparse"], inp["k"], inp["v"], wl.T, wl.T - 1)
+    t_fa, t_sel, t_sp = decode_step(inp["q"], inp["q_sparse"], inp["k"], inp["v"], wl.T, wl.T - 1, graph_key=wl.name)
     kv_bytes = 2.0 * wl.B * wl.T * 512
     sp_bytes = wl.B * (ms * 2 * 512 + 2 * wl.H * D * 2 + ms * 4)
     fa_gbs = kv_bytes / (t_fa * 1e-3) / 1e9
@@ -747,7 +777,9 @@ def other_workloads(dev, rec=None, with_cpu=True):
                                **_traffic(rec, "full_attn_" + wl.name, t_fa * 1e-3)},
         "select_counters": _traffic(rec, "select_" + wl.name, t_sel * 1e-3),
         "sparse_counters": _traffic(rec, "sparse_" + wl.name, t_sp * 1e-3 / wl.n_sparse),
-        "note": "cold: a 512 MiB write between reps; K/V 512 MiB per step"}
+        "hip_graph": graph_rec.get(wl.name),
+        "note": "cold: a 512 MiB write between reps; K/V 512 MiB per step; hip_graph: the whole step "
+                "captured as one HIP graph and replayed, same conditions"}
     if with_cpu:
         t_cpu = _oracle_decode(inp["q"], inp["q_sparse"], inp["k"], inp["v"], wl.T, wl.T - 1)
         out[wl.name]["cpu_baseline"] = _cpu_entry(1.0 / t_cpu, "queries/s", t_cpu,
@@ -765,7 +797,7 @@ def other_workloads(dev, rec=None, with_cpu=True):
         q = inputs.cast(inputs.normal((1, 1, wl.H, 256), inputs.STD_QKV, wl.seed, inputs.S_Q + 10 * st, dev), "bf16")
         qs = [inputs.cast(inputs.normal((1, 1, wl.H, 256), inputs.STD_QKV, wl.seed, inputs.S_QSPARSE + 10 * st + i,
                                         dev), "bf16") for i in range(wl.n_sparse)]
-        steps.append(decode_step(q, qs, k, v, wl.T, p, ks, vs))
+        steps.append(decode_step(q, qs, k, v, wl.T, p, ks, vs, graph_key=wl.name if st == wl.steps - 1 else None))
     t_fa = sum(x[0] for x in steps) / len(steps)
     t_sel = sum(x[1] for x in steps) / len(steps)
     t_sp = sum(x[2] for x in steps) / len(steps)
@@ -781,7 +813,9 @@ def other_workloads(dev, rec=None, with_cpu=True):
                                **_traffic(rec, "full_attn_" + wl.name, t_fa * 1e-3)},
         "select_counters": _traffic(rec, "select_" + wl.name, t_sel * 1e-3),
         "sparse_counters": _traffic(rec, "sparse_" + wl.name, t_sp * 1e-3 / wl.n_sparse),
-        "note": "mean of the 4 steps (p = T-4 .. T-1); cold between reps"}
+        "hip_graph": graph_rec.get(wl.name),
+        "note": "mean of the 4 steps (p = T-4 .. T-1); cold between reps; hip_graph: the last step captured "
+                "as one HIP graph and replayed (its eager time beside it)"}
     if with_cpu:
         t_cpu = _oracle_decode(q, qs, k, v, wl.T, wl.T - 1, ks, vs)
         out[wl.name]["cpu_baseline"] = _cpu_entry(1.0 / t_cpu, "queries/s", t_cpu,
@@ -931,6 +965,10 @@ def cpu_baseline(args, inp, needles, step, keep_rows, idx, cnt, o_full, o_sp, L,
 
     edge = [0, 1, 127, 128, 129, 1151, 1152, 1153, L // 2, L - 1]
     rows = sorted(set(edge + [i for _, i in needles]))[: max(args.cpu_rows, len(edge))]
+    # evenly spaced rows up to the requested sample size (about 10 s of host work at 160)
+    extra = args.cpu_rows - len(rows)
+    if extra > 0:
+        rows = sorted(set(rows) | {int((j + 0.5) * L / extra) for j in range(extra)})
     # one more pass that also keeps the score rows of the sampled queries
     step(sample_rows=rows)
     torch.cuda.synchronize()
@@ -973,7 +1011,8 @@ def cpu_baseline(args, inp, needles, step, keep_rows, idx, cnt, o_full, o_sp, L,
     worst["needles"] = len(needles)
     worst["rows"] = len(rows)
     base = _cpu_entry(len(rows) / t_cpu, "tokens/s", t_cpu,
-                      f"{len(rows)} query rows of the same 128k sequence (64 needle targets + edge positions), "
+                      f"{len(rows)} query rows of the same 128k sequence (the 64 needle targets, edge positions "
+                      f"and evenly spaced rows), "
                       f"each through full attention + select + {len(qs_np)} sparse layers in float64")
     return base, worst
 

@@ -135,8 +135,12 @@ def hs2_full_attn_scored(q, k, v, *, q_pos0: int, sm_scale: float | None = None,
     return o, lse, scores
 
 
+def select_workspace_bytes(B: int, n_q: int, T: int, q_pos0: int) -> int:
+    return int(lib().hs2_select_workspace_bytes(B, n_q, T, q_pos0))
+
+
 def hs2_select_topk_window(scores, *, q_pos0: int, T: int, n_q: int | None = None, window: int = 128,
-                           topk: int = 1024, idx=None, count=None, stream=None):
+                           topk: int = 1024, idx=None, count=None, ws=None, stream=None):
     """Token-level top-k with forced window.  scores [B,n_q,ld]; returns (idx, count)."""
     B, nq_s, ld = scores.shape
     n_q = nq_s if n_q is None else n_q
@@ -144,10 +148,10 @@ def hs2_select_topk_window(scores, *, q_pos0: int, T: int, n_q: int | None = Non
         idx = torch.empty((B, n_q, window + topk), dtype=torch.int32, device=scores.device)
     if count is None:
         count = torch.empty((B, n_q), dtype=torch.int32, device=scores.device)
-    need = int(lib().hs2_select_workspace_bytes(B, n_q, T, q_pos0))
-    ws = workspace(need, scores.device)
+    if ws is None:
+        ws = workspace(select_workspace_bytes(B, n_q, T, q_pos0), scores.device)
     rc = lib().hs2_select_topk_window(_ptr(scores), ld, B, n_q, T, q_pos0, window, topk, _ptr(idx), _ptr(count),
-                                      _ptr(ws), need, _stream(stream))
+                                      _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     check("hs2_select_topk_window", rc)
     return idx, count
 
