@@ -94,7 +94,7 @@ __device__ __forceinline__ void mfma32v_last2(f32x16& acc0, f32x16& acc1, bf16x8
 // rounded to bf16 for the PV product, the arithmetic of the e4m3 path of
 // attn_prefill.hip; each tile's scales ride along with its K or V DMA.
 template <int H, int PHASE, bool SC>
-__global__ __launch_bounds__(PB_THREADS, (PHASE == 1 && !SC) ? 2 : 1) void prefill_bf16_kernel(const AttnParams p, float* lse2) {
+__global__ __launch_bounds__(PB_THREADS, PHASE == 1 ? 2 : 1) void prefill_bf16_kernel(const AttnParams p, float* lse2) {
   constexpr int TPW = PB_RW / H;       // tokens per wave
   constexpr int TPB = PB_WAVES * TPW;  // tokens per workgroup
 
@@ -193,8 +193,10 @@ __global__ __launch_bounds__(PB_THREADS, (PHASE == 1 && !SC) ? 2 : 1) void prefi
     float m_run[2] = {kNegInf, kNegInf}, z_run[2] = {0.f, 0.f};
     const int my_pos[2] = {(int)pos_of_row(l32), (int)pos_of_row(32 + l32)};
     // Online max / sum of one tile (lane: rows l32 and 32 + l32, keys kt*32 +
-    // 8(r/4) + 4hb + r%4).  Tiles left of the diagonal need no causal mask:
-    // that path is the bulk of the work, so it is kept free of selects.
+    // 8(r/4) + 4hb + r%4); cf[r] is the logit factor of key r: the softmax
+    // scale in log2 units, times the key's row scale in the scaled form.
+    // Tiles left of the diagonal need no causal mask: that path is the bulk of
+    // the work, so it is kept free of selects.
     //
     // Left of the diagonal the running maximum is a lazy reference: a tile's
     // exponentials are taken against it as it stands, and it is raised (with
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(PB_THREADS, (PHASE == 1 && !SC) ? 2 : 1) void prefi
     // either way.  This drops the tile maximum (16 max per row block) from
     // the common case.  The test is wave-uniform: if any lane fails it, the
     // whole wave redoes the tile against the true maximum.
-    auto lse_update = [&](Pair& st, int kt, bool masked) __attribute__((always_inline)) {
+    auto lse_update = [&](Pair& st, int kt, bool masked, const float (&cf)[16]) __attribute__((always_inline)) {
       const int kbase = kt * PB_KT;
       if (!masked) {
         float accl[2];
@@ -214,7 +216,7 @@ __global__ __launch_bounds__(PB_THREADS, (PHASE == 1 && !SC) ? 2 : 1) void prefi
         for (int n = 0; n < 2; ++n) {
           float a = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) a += fast_exp2(st.v[n][r] * p.scale_log2 - m_run[n]);
+          for (int r = 0; r < 16; ++r) a += fast_exp2(st.v[n][r] * cf[r] - m_run[n]);
           accl[n] = a;
         }
         // !(a <= 2^64) also catches a first tile (m_run = -inf: a = +inf)
@@ -226,45 +228,36 @@ __global__ __launch_bounds__(PB_THREADS, (PHASE == 1 && !SC) ? 2 : 1) void prefi
       }
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
-        if (!masked) {
-          float tmax = kNegInf;
+        float tmax = kNegInf;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st.v[n][r]);
-          const float m_new = fmaxf(m_run[n], tmax * p.scale_log2);  // scale > 0: max commutes
-          float acc = 0.f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc += fast_exp2(st.v[n][r] * p.scale_log2 - m_new);
-          z_run[n] = z_run[n] * fast_exp2(m_run[n] - m_new) + acc;  // exp2(-inf) = 0 on the first tile
-          m_run[n] = m_new;
-        } else {
-          float tmax = kNegInf;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float x = st.v[n][r] * p.scale_log2;
-            x = (kbase + 8 * (r >> 2) + 4 * hb + (r & 3) <= my_pos[n]) ? x : kNegInf;
-            st.v[n][r] = x;
-            tmax = fmaxf(tmax, x);
-          }
-          const float m_new = fmaxf(m_run[n], tmax);
-          const float m_use = m_new == kNegInf ? 0.f : m_new;  // all masked so far: every term is 0
-          float acc = 0.f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc += fast_exp2(st.v[n][r] - m_use);
-          z_run[n] = z_run[n] * fast_exp2(m_run[n] - m_use) + acc;
-          m_run[n] = m_new;
+        for (int r = 0; r < 16; ++r) {
+          float x = st.v[n][r] * cf[r];
+          if (masked) x = (kbase + 8 * (r >> 2) + 4 * hb + (r & 3) <= my_pos[n]) ? x : kNegInf;
+          st.v[n][r] = x;
+          tmax = fmaxf(tmax, x);
         }
+        const float m_new = fmaxf(m_run[n], tmax);
+        const float m_use = m_new == kNegInf ? 0.f : m_new;  // all masked so far: every term is 0
+        float acc = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc += fast_exp2(st.v[n][r] - m_use);
+        z_run[n] = z_run[n] * fast_exp2(m_run[n] - m_use) + acc;   // exp2(-inf) = 0 on the first tile
+        m_run[n] = m_new;
       }
     };
     // Tile kt sits in kc; K(kt+2) goes to kd, which held K(kt-1) (past the last
     // tile the buffer resource is empty and the DMA writes zeros, so that every
     // tile issues the same instructions).  K(kt+1) may still be in flight at
     // the wait: each wave keeps its last batch of DMA instructions (5 for wave
-    // 0, 4 for the others) outstanding.  The batch is spread over the first
-    // ten MFMA steps (one instruction every second step): issued that early
-    // it has landed by the wait two tiles later.
-    auto step1 = [&](int kt, const char* kc, char* kd) __attribute__((always_inline)) {
-      if (wv == 0) __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5)
-      else __builtin_amdgcn_s_waitcnt(0x0F74);           // vmcnt(4)
+    // 0, 4 for the others, 5 for wave 1 in the scaled form, which also carries
+    // the tile's 32 K row scales) outstanding.  The batch is spread over the
+    // first ten MFMA steps (one instruction every second step): issued that
+    // early it has landed by the wait two tiles later.  In the scaled form the
+    // factors of tile kt are read from its scale buffer ksc after the MFMAs
+    // (the DMA that reuses that buffer is issued in the next step).
+    auto step1 = [&](int kt, const char* kc, char* kd, const float* ksc, float* ksd) __attribute__((always_inline)) {
+      if (wv == 0 || (SC && wv == 1)) __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5)
+      else __builtin_amdgcn_s_waitcnt(0x0F74);                              // vmcnt(4)
       __syncthreads();
       const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kg, kt + 2);
       Pair st;
@@ -278,125 +271,44 @@ __global__ __launch_bounds__(PB_THREADS, (PHASE == 1 && !SC) ? 2 : 1) void prefi
         if (s + PB_AHEAD < 16) kf[s + PB_AHEAD] = kfrag(kc, s + PB_AHEAD);
         st.v[1] = mfma32(kf[s], qf[1][s], s == 0 ? f32x16{} : st.v[1]);
         if (s % 2 == 0 && s < 10) dma_one(rk, kd, koff, s / 2);
+        if constexpr (SC) {
+          if (s == 10 && wv == 1) dma_scales(p.k_scale, kt + 2, ksd);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      lse_update(st, kt, (int64_t)kt * PB_KT + PB_KT - 1 > pos_first);
-    };
-
-    // ---- scaled form (e4m3 codes widened to bf16, per-key scales): a logit
-    // is S * (scale * k_scale[key]).  That update does not fit two waves per
-    // SIMD, so this form runs one, and keeps the MFMA pipe busy by itself: the
-    // update of tile kt - 1 is cut into 16 pieces that run on the VALU inside
-    // the 16 MFMA steps of tile kt.  Pieces 0-1 of a row block take the logits
-    // and their max, 2-7 the exponentials; piece 7 folds the tile into the
-    // running state.  The logit factors of a tile are read from LDS at the
-    // start of its own step and kept for the next one (the DMA of later
-    // scales reuses the buffer).
-    float tm[2], mn[2], mu[2], acc[2];
-    auto lse_piece = [&](Pair& st, const f32x4 (&cs)[4], int kt, int s, auto masked) __attribute__((always_inline)) {
-      constexpr bool MASK = decltype(masked)::value;
-      const int n = s >> 3, k = s & 7;
-      if (k < 2) {
-        float t = k == 0 ? kNegInf : tm[n];
+      float cf[16];
+      if constexpr (SC) {
 #pragma unroll
-        for (int r = 8 * k; r < 8 * k + 8; ++r) {
-          float x = st.v[n][r] * cs[r >> 2][r & 3];
-          if constexpr (MASK) x = (kt * PB_KT + 8 * (r >> 2) + 4 * hb + (r & 3) <= my_pos[n]) ? x : kNegInf;
-          st.v[n][r] = x;
-          t = fmaxf(t, x);
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 c4 = *(const f32x4*)(ksc + 8 * q + 4 * hb);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) cf[4 * q + e] = c4[e] * p.scale_log2;
         }
-        tm[n] = t;
-        if (k == 1) {
-          mn[n] = fmaxf(m_run[n], t);
-          mu[n] = mn[n] == kNegInf ? 0.f : mn[n];   // all masked so far: every term is 0
-          acc[n] = 0.f;
-        }
-        return;
-      }
-      const int r0 = k < 6 ? 3 * (k - 2) : 12 + 2 * (k - 6), r1 = k < 6 ? r0 + 3 : r0 + 2;
+      } else {
 #pragma unroll
-      for (int r = r0; r < r1; ++r) acc[n] += fast_exp2(st.v[n][r] - mu[n]);
-      if (k == 7) {
-        z_run[n] = z_run[n] * fast_exp2(m_run[n] - mu[n]) + acc[n];   // exp2(-inf) = 0 on the first tile
-        m_run[n] = mn[n];
+        for (int r = 0; r < 16; ++r) cf[r] = p.scale_log2;
       }
+      lse_update(st, kt, (int64_t)kt * PB_KT + PB_KT - 1 > pos_first, cf);
     };
-    // as step1, plus: wave 1 carries the DMA of tile kt + 2's scales into ksd
-    // (the buffer of tile kt - 1, whose factors are already in registers)
-    auto step1s = [&](int kt, const char* kc, char* kd, const float* ksc, float* ksd, Pair& prev, f32x4 (&pcs)[4],
-                      auto masked) __attribute__((always_inline)) {
-      if (wv <= 1) __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5)
-      else __builtin_amdgcn_s_waitcnt(0x0F74);           // vmcnt(4)
-      __syncthreads();
-      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kg, kt + 2);
-      f32x4 cs[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) cs[q] = *(const f32x4*)(ksc + 8 * q + 4 * hb) * p.scale_log2;
-      Pair st;
-      bf16x8 kf[16];
-#pragma unroll
-      for (int s = 0; s < PB_AHEAD; ++s) kf[s] = kfrag(kc, s);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        st.v[0] = mfma32(kf[s], qf[0][s], s == 0 ? f32x16{} : st.v[0]);
-        if (s + PB_AHEAD < 16) kf[s + PB_AHEAD] = kfrag(kc, s + PB_AHEAD);
-        st.v[1] = mfma32(kf[s], qf[1][s], s == 0 ? f32x16{} : st.v[1]);
-        if (s % 2 == 0 && s < 10) dma_one(rk, kd, koff, s / 2);
-        if (s == 10 && wv == 1) dma_scales(p.k_scale, kt + 2, ksd);
-        if (kt > 0) lse_piece(prev, pcs, kt - 1, s, masked);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      prev = st;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) pcs[q] = cs[q];
-    };
-    if constexpr (SC) {
+    {
       float* const ks0 = lds_ks[0];
-      float* const ks1 = lds_ks[1];
-      float* const ks2 = lds_ks[2];
+      float* const ks1 = lds_ks[SC ? 1 : 0];
+      float* const ks2 = lds_ks[SC ? 2 : 0];
       // issue order per wave: K(0), scales(0), K(1), scales(1), so that the
       // first wait (all but the last batch) covers tile 0 and its scales
       dma(kg, 0, lds_k0, koff);
-      if (wv == 1) dma_scales(p.k_scale, 0, ks0);
+      if (SC && wv == 1) dma_scales(p.k_scale, 0, ks0);
       dma(kg, 1, lds_k1, koff);
-      if (wv == 1) dma_scales(p.k_scale, 1, ks1);
-      const int t_mask = (int)((pos_first + 1) / PB_KT);   // tiles >= t_mask need the causal mask
-      Pair prev;
-      f32x4 pcs[4];
-      int kt = 0;
-      // left of the diagonal: the buffers rotate, unrolled; tile kt's update
-      // runs in step kt + 1, so it is unmasked while kt + 1 < t_mask
-      for (; kt + 3 < t_mask; kt += 3) {
-        step1s(kt, lds_k0, lds_k2, ks0, ks2, prev, pcs, std::false_type{});
-        step1s(kt + 1, lds_k1, lds_k0, ks1, ks0, prev, pcs, std::false_type{});
-        step1s(kt + 2, lds_k2, lds_k1, ks2, ks1, prev, pcs, std::false_type{});
-      }
-      // the rest (the diagonal tiles, and up to three before them) picks its
-      // buffers at run time and masks every update: one copy of the body
-      for (; kt < ntiles; ++kt) {
-        const int r3 = kt % 3;
-        const char* kc = r3 == 0 ? lds_k0 : (r3 == 1 ? lds_k1 : lds_k2);
-        char* kd = r3 == 0 ? lds_k2 : (r3 == 1 ? lds_k0 : lds_k1);
-        const float* ksc = r3 == 0 ? ks0 : (r3 == 1 ? ks1 : ks2);
-        float* ksd = r3 == 0 ? ks2 : (r3 == 1 ? ks0 : ks1);
-        step1s(kt, kc, kd, ksc, ksd, prev, pcs, std::true_type{});
-      }
-#pragma unroll
-      for (int s = 0; s < 16; ++s) lse_piece(prev, pcs, ntiles - 1, s, std::true_type{});
-      wait_dma();   // the zero-filling DMA past the last tile
-    } else {
-      dma(kg, 0, lds_k0, koff);
-      dma(kg, 1, lds_k1, koff);
+      if (SC && wv == 1) dma_scales(p.k_scale, 1, ks1);
       int kt = 0;
       for (; kt + 2 < ntiles; kt += 3) {
-        step1(kt, lds_k0, lds_k2);
-        step1(kt + 1, lds_k1, lds_k0);
-        step1(kt + 2, lds_k2, lds_k1);
+        step1(kt, lds_k0, lds_k2, ks0, ks2);
+        step1(kt + 1, lds_k1, lds_k0, ks1, ks0);
+        step1(kt + 2, lds_k2, lds_k1, ks2, ks1);
       }
-      if (kt < ntiles) step1(kt, lds_k0, lds_k2);
-      if (kt + 1 < ntiles) step1(kt + 1, lds_k1, lds_k0);
+      if (kt < ntiles) step1(kt, lds_k0, lds_k2, ks0, ks2);
+      if (kt + 1 < ntiles) step1(kt + 1, lds_k1, lds_k0, ks1, ks0);
       wait_dma();   // the zero-filling DMA past the last tile
     }
 #pragma unroll
