@@ -129,48 +129,51 @@ __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParam
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  // chunk kc from stage buffer buf; the DMA of chunk kc + 3 into nxt (which
-  // held chunk kc - 1) is spread over its MFMAs, one instruction after every
-  // fourth
-  auto step = [&](int kc, const char* buf, char* nxt) __attribute__((always_inline)) {
-    // chunk kc has landed once at most the 16 DMA instructions of the two
-    // chunks after it are outstanding; the barrier makes every wave's part
-    // visible and ends every wave's reads of chunk kc - 1
-    __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
-    dma_barrier();
-    // fragments of K-step 1 are read while the MFMAs of step 0 run
-    auto rd_a = [&](int ks, int i) __attribute__((always_inline)) {
-      const int row = wm * 128 + 32 * i + l32;
-      return as_bf16x8(*(const u32x4*)(buf + a_off(row, 2 * ks + hb)));
-    };
-    // B[k][n] for k = 16ks + 8(G/2) + i, n = wn*128 + 32j + 16(G%2) + s16
-    auto rd_b = [&](int ks, int j) __attribute__((always_inline)) {
-      const int krow = 16 * ks + 8 * (G >> 1) + (s16 >> 2);
-      const int col = wn * 128 + 32 * j + 16 * (G & 1) + 4 * (s16 & 3);
-      const int ch = col >> 3, half = (col >> 2) & 1;
-      const char* b0 = buf + A_BYTES + b_off(krow, ch) + half * 8;
-      const char* b1 = buf + A_BYTES + b_off(krow + 4, ch) + half * 8;
-      return cat8(lds_tr16((const bf16*)b0), lds_tr16((const bf16*)b1));
-    };
-    bf16x8 af[2][4], bfr[2][4];
+  // Chunk kc from stage buffer buf, its K-step 0 fragments already in
+  // registers.  The MFMAs of K-step 0 run while the fragments of K-step 1 are
+  // read; then chunk kc + 1 (in nbuf) is waited for, and the barrier sits
+  // between the two halves, with the MFMAs of K-step 0 still in flight; the
+  // MFMAs of K-step 1 run while the K-step 0 fragments of chunk kc + 1 are
+  // read.  So no fragment read waits behind a barrier.  The DMA of chunk kc + 3
+  // into nxt (which held chunk kc - 1, whose fragments were all read before
+  // the previous step's barrier) is spread over the MFMAs, one instruction
+  // after every fourth.
+  bf16x8 af[2][4], bfr[2][4];
+  auto rd_a = [&](const char* buf, int ks, int i) __attribute__((always_inline)) {
+    const int row = wm * 128 + 32 * i + l32;
+    return as_bf16x8(*(const u32x4*)(buf + a_off(row, 2 * ks + hb)));
+  };
+  // B[k][n] for k = 16ks + 8(G/2) + i, n = wn*128 + 32j + 16(G%2) + s16
+  auto rd_b = [&](const char* buf, int ks, int j) __attribute__((always_inline)) {
+    const int krow = 16 * ks + 8 * (G >> 1) + (s16 >> 2);
+    const int col = wn * 128 + 32 * j + 16 * (G & 1) + 4 * (s16 & 3);
+    const int ch = col >> 3, half = (col >> 2) & 1;
+    const char* b0 = buf + A_BYTES + b_off(krow, ch) + half * 8;
+    const char* b1 = buf + A_BYTES + b_off(krow + 4, ch) + half * 8;
+    return cat8(lds_tr16((const bf16*)b0), lds_tr16((const bf16*)b1));
+  };
+  auto step = [&](int kc, const char* buf, const char* nbuf, char* nxt) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      af[0][i] = rd_a(0, i);
-      bfr[0][i] = rd_b(0, i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[0][i], bfr[0][j], acc[i][j]);
+      af[1][i] = rd_a(buf, 1, i);
+      bfr[1][i] = rd_b(buf, 1, i);
+      dma_one(kc + 3, nxt, i);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // chunk kc + 1 has landed once at most the 12 DMA instructions issued after
+    // it (chunk kc + 2 and the first half of chunk kc + 3) are outstanding
+    __builtin_amdgcn_s_waitcnt(0x0F7C);  // vmcnt(12)
+    dma_barrier();
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[ks][i], bfr[ks][j], acc[i][j]);
-        if (ks == 0) {
-          af[1][i] = rd_a(1, i);
-          bfr[1][i] = rd_b(1, i);
-        }
-        dma_one(kc + 3, nxt, 4 * ks + i);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[1][i], bfr[1][j], acc[i][j]);
+      af[0][i] = rd_a(nbuf, 0, i);
+      bfr[0][i] = rd_b(nbuf, 0, i);
+      dma_one(kc + 3, nxt, 4 + i);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -180,11 +183,19 @@ __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParam
   for (int j = 0; j < 8; ++j) dma_one(1, st1, j);
 #pragma unroll
   for (int j = 0; j < 8; ++j) dma_one(2, st2, j);
+  // chunk 0 has landed once at most the 16 instructions of chunks 1 and 2 are outstanding
+  __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
+  dma_barrier();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    af[0][i] = rd_a(st0, 0, i);
+    bfr[0][i] = rd_b(st0, 0, i);
+  }
   for (int kc = 0; kc < nk; kc += 4) {
-    step(kc, st0, st3);
-    if (kc + 1 < nk) step(kc + 1, st1, st0);
-    if (kc + 2 < nk) step(kc + 2, st2, st1);
-    if (kc + 3 < nk) step(kc + 3, st3, st2);
+    step(kc, st0, st1, st3);
+    if (kc + 1 < nk) step(kc + 1, st1, st2, st0);
+    if (kc + 2 < nk) step(kc + 2, st2, st3, st1);
+    if (kc + 3 < nk) step(kc + 3, st3, st0, st2);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the zero-filling DMA past the last chunk
 
@@ -203,8 +214,10 @@ __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParam
   } else {
     // row maxima of |v| over this wave's 128 columns (4 per lane, then the 32
     // lanes of the half-wave), then over the partner wave's half through LDS
-    float* red = (float*)st0;   // [wm][wn][128 rows]; the DMA has drained
-    dma_barrier();              // every wave is done reading the stage buffers
+    float* red = (float*)st0;            // [wm][wn][128 rows]; the DMA has drained
+    float* rsc = red + 4 * 128;          // [256 rows] scale of each row of the tile
+    float* rrc = rsc + 256;              // [256 rows] its correctly rounded reciprocal
+    dma_barrier();                       // every wave is done reading the stage buffers
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -214,27 +227,51 @@ __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParam
         if (l32 == 0) red[(wm * 2 + wn) * 128 + 32 * i + 8 * (r >> 2) + 4 * hb + (r & 3)] = m;
       }
     dma_barrier();
-    uint8_t* out = (uint8_t*)(which ? p.v_out : p.k_out) + (int64_t)layer * p.out_layer_stride;
+    // one thread per row of the tile: the scale (and its reciprocal) is
+    // computed once, not by every lane that holds part of the row
     float* sc = (which ? p.v_scale : p.k_scale) + (int64_t)layer * p.scale_layer_stride;
+    {
+      const int row = tid, rw = row >> 7, rr = row & 127;
+      const float amax = fmaxf(red[(rw * 2) * 128 + rr], red[(rw * 2 + 1) * 128 + rr]);
+      const float scale = amax > 0.f ? amax / 448.f : 1.f;
+      rsc[row] = scale;
+      rrc[row] = 1.f / scale;
+      if (m0 + row < p.L) sc[m0 + row] = scale;
+    }
+    dma_barrier();
+    uint8_t* out = (uint8_t*)(which ? p.v_out : p.k_out) + (int64_t)layer * p.out_layer_stride;
+    // A lane holds the codes of columns 32j + l32 (j = 0..3) of a row; a 4 x 4
+    // byte transpose inside each quad of lanes (two DPP swaps and two byte
+    // permutes) gives lane 4a + t the codes of columns 32t + 4a .. +3, stored
+    // as one dword: a half-wave writes a row's 128 codes as one 128-byte line.
+    const int qt = l32 & 3;
+    // byte selectors of __builtin_amdgcn_perm(hi, lo, sel): bytes 0-3 of lo are
+    // 0-3, bytes of hi are 4-7; the first byte of the result is sel's low byte
+    const uint32_t sel1 = (qt & 1) ? 0x03070105u : 0x06020400u;   // odd: {X.b1, D.b1, X.b3, D.b3}
+    const uint32_t sel2 = (qt & 2) ? 0x03020706u : 0x05040100u;   // lanes 2, 3: {Y.b2, Y.b3, A.b2, A.b3}
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 32 * i + 8 * (r >> 2) + 4 * hb + (r & 3);
         const int64_t grow = m0 + wm * 128 + row;
-        const float amax = fmaxf(red[(wm * 2) * 128 + row], red[(wm * 2 + 1) * 128 + row]);
-        const float scale = amax > 0.f ? amax / 448.f : 1.f;
-        const float rcp = 1.f / scale;
-        if (grow >= p.L) continue;
-        if (wn == 0 && l32 == 0) sc[grow] = scale;
+        const float scale = rsc[wm * 128 + row], rcp = rrc[wm * 128 + row];
+        float y[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float a = acc[i][j][r];
           const float q0 = a * rcp;
           const float q = __builtin_fmaf(__builtin_fmaf(-q0, scale, a), rcp, q0);  // fl32(a / scale)
-          const float y = __builtin_amdgcn_fmed3f(q, 448.f, -448.f);
-          out[grow * 256 + wn * 128 + 32 * j + l32] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xFF);
+          y[j] = __builtin_amdgcn_fmed3f(q, 448.f, -448.f);
         }
+        int d = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);   // bytes 0, 1: j = 0, 1
+        d = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], d, true);        // bytes 2, 3: j = 2, 3
+        const int x = __builtin_amdgcn_mov_dpp(d, 0xB1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+        const int aa = (int)__builtin_amdgcn_perm((uint32_t)x, (uint32_t)d, sel1);
+        const int yy = __builtin_amdgcn_mov_dpp(aa, 0x4E, 0xf, 0xf, false); // quad_perm [2,3,0,1]
+        const int bb = (int)__builtin_amdgcn_perm((uint32_t)yy, (uint32_t)aa, sel2);
+        if (grow < p.L)
+          *(int*)(out + grow * 256 + wn * 128 + 32 * qt + 4 * (l32 >> 2)) = bb;
       }
   }
 }
