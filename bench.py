@@ -76,11 +76,17 @@ GROUPS = {
     "select_decode_1m_fp8": ("decode_1m_fp8", ["select_kernel", "fr_"], ["select.hip"], 1),
     "sparse_decode_1m_fp8": ("decode_1m_fp8", ["sparse_attn_kernel", "sparse_merge_kernel"],
                              ["sparse_reuse.hip", "attn_tile.hpp"], 4),
+    "swa_128k": ("swa_128k", ["swa_kernel"], ["swa.hip"], 1),
+    "rope_128k": ("swa_128k", ["rope_kernel"], ["swa.hip"], 2),
+    "bridge_64k": ("bridge_64k", ["bridge_kernel<false>"], ["bridge.hip"], 1),
+    "bridge_64k_fp8": ("bridge_64k_fp8", ["bridge_kernel<true>"], ["bridge.hip"], 1),
 }
+# groups that also get the SQ counter pass (MFMA busy cycles, held clock)
+SQ_GROUPS = ("full_attn_prefill", "swa_128k", "bridge_64k", "bridge_64k_fp8")
 # the probe's phases in launch order; the "_setup" phases (input generation, warm-ups, cache
 # flushes) are measured by nobody
 PHASES = ["prefill", "prefill_sparse", "_setup_b16", "decode_b16_32k", "_setup_1m", "decode_1m_fp8",
-          "_setup_calib", "calibration"]
+          "_setup_swa", "swa_128k", "_setup_bridge", "bridge_64k", "bridge_64k_fp8", "_setup_calib", "calibration"]
 MARKER = "FillFunctor<double>"   # a float64 fill marks the start of each probe phase and the end
 SQ_CTRS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"]
 
@@ -173,7 +179,8 @@ def collect_traffic(args):
         "# HBM-side traffic per launch of each kernel group of the path, from rocprofv3 counter passes",
         "# over one probe run (bench.py --pmc-probe: one warm-up step of the 128k prefill, then its",
         f"# {n_chunks} scored full-attention + select calls, one sparse layer, one decode step of each decode",
-        "# workload with K/V pushed out of the caches first, and a 1 GiB copy).",
+        "# workload with K/V pushed out of the caches first, the self-decoder SWA over the 128k prompt",
+        "# (cold), the bf16 and the FP8 bridge of the 64k hidden state (warm), and a 1 GiB copy).",
         "# command: python bench.py --collect-traffic   (one pass per counter set:)",
         f"#   rocprofv3 --pmc <FETCH_SIZE | WRITE_SIZE | {' '.join(SQ_CTRS)}> --output-format csv -d <dir> -o p"
         f" -- python bench.py --pmc-probe --chunk {args.chunk}",
@@ -198,7 +205,7 @@ def collect_traffic(args):
                   f"launches = {launches}", f"fetch_bytes_per_launch = {fetch:.4e}",
                   f"write_bytes_per_launch = {write:.4e}", f"traffic_bytes_per_launch = {fetch + write:.4e}",
                   f"seconds_per_launch_under_counters = {sum(x[3] for x in f_disp) / launches:.6f}"]
-        if g == "full_attn_prefill":
+        if g in SQ_GROUPS:
             s_disp = sel(sq[phase])
             tot = {c: sum(x[2].get(c, 0.0) for x in s_disp) / launches for c in SQ_CTRS}
             dur = sum(x[3] for x in s_disp) / launches
@@ -283,6 +290,45 @@ def pmc_probe(args):
         torch.cuda.synchronize()
         del k, v, ks, vs
         torch.cuda.empty_cache()
+    # the self-decoder SWA over the 128k prompt: the rotary embedding of K and Q in place, then the
+    # attention, cold as bench.py times it
+    w = inputs.WORKLOADS["self_decoder_swa_128k"]
+    sw = inputs.attention_inputs(B=1, n_q=w.L, T=w.L, H=w.H, d=D, kv="bf16", n_sparse=0, seed=w.seed, device=dev)
+
+    def swa():
+        hs2.hs2_rope_partial(sw["k"][0], pos0=0, rope_dims=w.rope_dims, rope_base=10000.0, out=sw["k"][0])
+        hs2.hs2_rope_partial(sw["q"][0], pos0=0, rope_dims=w.rope_dims, rope_base=10000.0, out=sw["q"][0])
+        hs2.hs2_swa_attn(sw["q"], sw["k"], sw["v"], q_pos0=0, window=w.window, sm_scale=scale)
+    swa()                                         # warm-up (and the allocations)
+    junk.fill_(1)
+    marker()
+    swa()
+    marker()
+    torch.cuda.synchronize()
+    del sw
+    torch.cuda.empty_cache()
+    # the bf16 and the FP8 bridge of the 64k hidden state, warm as bench.py times them
+    w = inputs.WORKLOADS["bridge_64k"]
+    br = inputs.bridge_inputs(L=w.L, D=w.D, n_layers=w.n_full, d=256, seed=w.seed, device=dev)
+    kb = torch.empty((w.n_full, w.L, 256), dtype=torch.bfloat16, device=dev)
+    vb = torch.empty_like(kb)
+    k8 = torch.empty((w.n_full, w.L, 256), dtype=torch.uint8, device=dev)
+    v8 = torch.empty_like(k8)
+    s8 = torch.empty((2, w.n_full, w.L), dtype=torch.float32, device=dev)
+    bridge = lambda: hs2.hs2_bridge_kv_proj(br["x"], br["w_k"], br["w_v"], k_out=kb, v_out=vb)  # noqa: E731
+    bridge8 = lambda: hs2.hs2_bridge_kv_proj_fp8(br["x"], br["w_k"], br["w_v"], k_out=k8, v_out=v8,  # noqa: E731
+                                                 k_scale=s8[0], v_scale=s8[1])
+    bridge()                                      # warm-up
+    bridge8()
+    torch.cuda.synchronize()
+    marker()
+    bridge()
+    marker()
+    bridge8()
+    marker()
+    torch.cuda.synchronize()
+    del br, kb, vb, k8, v8, s8
+    torch.cuda.empty_cache()
     a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
     marker()
@@ -587,6 +633,14 @@ def _timed(run, stages: int, reps: int = 10, warm: int = 3, flush=None):
     return np.median(np.array(per), axis=0)
 
 
+def _bridge_counters(rec, group, ms):
+    """Counter bytes of one bridge launch, and its MFMA busy fraction and held clock from the
+    SQ pass (null without a current record)."""
+    return {**_traffic(rec, group, ms * 1e-3),
+            "mfma_busy_frac_counters": _rec_float(rec, group, "mfma_busy_frac_at_2p4ghz"),
+            "clock_ghz_counters": _rec_float(rec, group, "mean_clock_ghz_from_grbm")}
+
+
 def _traffic(rec, group, seconds_per_launch):
     """Counter bytes per launch of a kernel group, their rate and its fraction of the HBM
     peak ({"traffic": None} without a current record)."""
@@ -852,7 +906,10 @@ def other_workloads(dev, rec=None, with_cpu=True):
         "rope_ms": float(t_rope), "rope_gbs": rope_bytes / (t_rope * 1e-3) / 1e9, "attn_ms": float(t_sw),
         "roofline": {"kernel": "hs2_swa_attn (swa_kernel)", "bound": "hbm", "achieved": sw_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": sw_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": sw_bytes,
-                     "mfma_tflops_algorithmic": sw_flop / (t_sw * 1e-3) / 1e12},
+                     "mfma_tflops_algorithmic": sw_flop / (t_sw * 1e-3) / 1e12,
+                     **_traffic(rec, "swa_128k", t_sw * 1e-3),
+                     "mfma_busy_frac_counters": _rec_float(rec, "swa_128k", "mfma_busy_frac_at_2p4ghz")},
+        "rope_counters": _traffic(rec, "rope_128k", t_rope * 1e-3 / 2),
         "note": "window 128, rope_dims 64, base 10000, H = 16, bf16: the rotary embedding of K and Q (in place), "
                 "then the attention; cold (512 MiB write between reps)"}
     if with_cpu:
@@ -896,6 +953,7 @@ def other_workloads(dev, rec=None, with_cpu=True):
     out[wl.name] = {
         "bridge_ms": float(t_br), "bridge_tflops": br_flop / (t_br * 1e-3) / 1e12,
         "bridge_mfma_frac": br_flop / (t_br * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+        "bridge_counters": _bridge_counters(rec, "bridge_64k", t_br),
         "cross_decoder_step_ms": t_cross, "prefill_tokens_per_s": wl.L / ((t_br + t_cross) * 1e-3),
         "note": "bridge warm (inputs resident); the 4 bridged decode steps cold"}
     if with_cpu:
@@ -945,6 +1003,7 @@ def other_workloads(dev, rec=None, with_cpu=True):
     out[wl.name + "_fp8"] = {
         "bridge_ms": float(t_br8), "bridge_tflops": br_flop / (t_br8 * 1e-3) / 1e12,
         "bridge_mfma_frac": br_flop / (t_br8 * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+        "bridge_counters": _bridge_counters(rec, "bridge_64k_fp8", t_br8),
         "cross_decoder_step_ms": t_cross8, "prefill_tokens_per_s": wl.L / ((t_br8 + t_cross8) * 1e-3),
         "note": "bridge into the e4m3 cache (per-row scales) and the bridged decode steps on it"}
     out[wl.name + "_fp8_every_position"] = reading_b_entry(

@@ -13,9 +13,9 @@
 //  * prefill_pv: S = Q K^T (a lane owns a key: float32 P from the lse, in-lane
 //    head sums for the scores), P -> LDS [key][row] -> transposed reads ->
 //    O += P V.  The 64 x 256 float32 O accumulator of a wave fills the AGPR
-//    file (one wave per SIMD); rows 0..31 of the wave's queries stay in VGPRs,
-//    rows 32..63 are parked in LDS, and operands are read three MFMA steps
-//    ahead of their use.
+//    file (one wave per SIMD); with 16 heads all 64 query rows of the wave
+//    stay in VGPRs (with fewer heads rows 32..63 are parked in LDS), and
+//    operands are read three MFMA steps ahead of their use.
 //
 // Both stream K (and V) in 32-key tiles through LDS with global_load_lds_dwordx4
 // (no register staging), one barrier per tile.  Every buffer is its own LDS
