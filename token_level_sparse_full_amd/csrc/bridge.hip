@@ -191,11 +191,21 @@ __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParam
     af[0][i] = rd_a(st0, 0, i);
     bfr[0][i] = rd_b(st0, 0, i);
   }
-  for (int kc = 0; kc < nk; kc += 4) {
+  // The main loop runs whole groups of four chunks with no conditions inside:
+  // with a conditional step in the body, the compiler could no longer tell
+  // which stage buffer each outstanding DMA writes and waited for all but the
+  // newest DMA before the first fragment read of a chunk (measured 6 % slower).
+  int kc = 0;
+  for (; kc + 4 <= nk; kc += 4) {
+    step(kc, st0, st1, st3);
+    step(kc + 1, st1, st2, st0);
+    step(kc + 2, st2, st3, st1);
+    step(kc + 3, st3, st0, st2);
+  }
+  if (kc < nk) {
     step(kc, st0, st1, st3);
     if (kc + 1 < nk) step(kc + 1, st1, st2, st0);
     if (kc + 2 < nk) step(kc + 2, st2, st3, st1);
-    if (kc + 3 < nk) step(kc + 3, st3, st0, st2);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the zero-filling DMA past the last chunk
 
