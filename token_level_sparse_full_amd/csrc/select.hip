@@ -415,7 +415,9 @@ __device__ void exact_row(const float* row, int64_t n_cand, int topk, int32_t* o
 
 // One read of candidates [c0, c0 + 8 * SEL_THREADS) of a row (n_cand of
 // them): wave wv takes the 512 consecutive ones from c0 + 512 wv, lane l the
-// float4s at 256 q + 4 l of that piece (patterns past n_cand read as 0).
+// float4s at 256 q + 4 l of that piece.  Entries at or past n_cand hold
+// whatever the row has there: every caller tests round_index < n_cand before
+// it uses an entry.
 constexpr int SEL_PER = 8;
 constexpr int SEL_ROUND = SEL_PER * SEL_THREADS;  // candidates per round
 constexpr int SEL_PIECE = SEL_PER * kWave;        // consecutive candidates of one wave per round
@@ -424,14 +426,16 @@ __device__ __forceinline__ void load_round(const float* row, int64_t n_cand, int
 #pragma unroll
   for (int q = 0; q < SEL_PER / 4; ++q) {
     const int64_t j = c0 + SEL_PIECE * wv + 256 * q + 4 * lane;
-    if (j + 3 < n_cand) {
-      const f32x4 v = *(const f32x4*)(row + j);
+    // One float4 load on every path and no use of the data here, so that the
+    // compiler counts the loads in flight and waits only where the entries
+    // are used (a load under a condition, or a select on the loaded value,
+    // made it wait right after the loads, which undid the prefetch of the
+    // next round).  j is a multiple of 4 and a row holds a multiple of 4
+    // scores, more than n_cand, so the float4 at j < n_cand lies inside the
+    // row; lanes past the candidates read the row's first float4.
+    const f32x4 v = *(const f32x4*)(row + (j < n_cand ? j : 0));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) u[4 * q + e] = fbits(v[e]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) u[4 * q + e] = (j + e < n_cand) ? fbits(row[j + e]) : 0u;
-    }
+    for (int e = 0; e < 4; ++e) u[4 * q + e] = fbits(v[e]);
   }
 }
 __device__ __forceinline__ int64_t round_index(int64_t c0, int q, int e) {
@@ -477,7 +481,8 @@ __global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(8))
   uint32_t ucur[SEL_PER], unext[SEL_PER];
   load_round(row, n_cand, 0, ucur);
   for (int64_t base = 0; base < n_cand; base += SEL_ROUND) {
-    if (base + SEL_ROUND < n_cand) load_round(row, n_cand, base + SEL_ROUND, unext);
+    load_round(row, n_cand, base + SEL_ROUND, unext);   // past the row: its first float4s, never used
+    __builtin_amdgcn_sched_barrier(0);                  // the next round's loads go out first
     uint64_t bal[SEL_PER];
     int wtot = 0;
 #pragma unroll
