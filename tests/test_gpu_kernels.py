@@ -382,8 +382,10 @@ def _bf16_from_f32(x):
 # D / 32 chunks of the K dimension: 1, 3, 5, 7 exercise the pipeline's partial rounds of 4 stage
 # buffers and the chunks past the end; L not a multiple of 256 the rows past L
 # 9000 rows x 4 layers are 288 tiles of 256 x 256, more than one round of workgroups.
+# D / 32 chunks of K: the main loop takes groups of four, the tail the other 1, 2 or 3.
 @pytest.mark.parametrize("L,D,n_layers", [(300, 256, 2), (1, 2048, 4), (513, 512, 1), (257, 32, 1), (100, 96, 3),
-                                          (70, 160, 2), (513, 224, 1), (9000, 256, 4), (9000, 160, 4)])
+                                          (70, 160, 2), (513, 224, 1), (130, 192, 2), (40, 64, 1), (9000, 256, 4),
+                                          (9000, 160, 4)])
 def test_bridge_integer_exact(L, D, n_layers):
     say("bridge int", L, D, n_layers)
     rng = np.random.default_rng(L + D)
@@ -419,7 +421,8 @@ def test_bridge_normal_within_one_ulp_and_strided_output():
     assert (k_cache[:, L:] == 0).all() and (v_cache[:, L:] == 0).all()
 
 # --------------------------------------------------------------------------- bridge into an e4m3 cache
-@pytest.mark.parametrize("L,D,n_layers", [(300, 256, 2), (70, 160, 1), (1, 2048, 4), (9000, 256, 4), (9000, 160, 4)])
+@pytest.mark.parametrize("L,D,n_layers", [(300, 256, 2), (70, 160, 1), (1, 2048, 4), (130, 192, 1), (97, 96, 2),
+                                          (40, 64, 1), (9000, 256, 4), (9000, 160, 4)])
 def test_bridge_fp8_integer_exact(L, D, n_layers):
     """Integer inputs make the float32 accumulators exact, so codes and scales
     must equal the oracle's bit for bit (row 0 is all zero: scale 1, codes 0)."""
