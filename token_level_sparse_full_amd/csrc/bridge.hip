@@ -51,21 +51,18 @@ __device__ __forceinline__ int a_off(int row, int ch) { return row * 64 + ((ch ^
 // B tile [BK][BN] bf16: 32 chunks per row, chunk ^ (2 * (row & 3))
 __device__ __forceinline__ int b_off(int row, int ch) { return row * 512 + ((ch ^ (2 * (row & 3))) << 4); }
 
-// Maximum over the 32 lanes of each half-wave, returned to all of them:
+// Row maxima over the 32 lanes of each half-wave, returned to all of them:
 // quad_perm swaps (xor 1, xor 2), the half-row and row mirrors (which pair
 // each lane with one in the other half of its 8- and 16-lane group), then one
-// swizzle between the two 16-lane rows of the half-wave.
+// swizzle between the two 16-lane rows of the half-wave.  The values are the
+// bit patterns of non-negative floats, which order like unsigned integers, so
+// integer maxima give the float maximum (and need no NaN quieting between
+// the steps, which float maxima of DPP results get).
 template <int CTRL>
-__device__ __forceinline__ float dpp_max(float v) {
-  return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false)));
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
+  return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false));
 }
-__device__ __forceinline__ float half_wave_max(float v) {
-  v = dpp_max<0xB1>(v);    // quad_perm [1,0,3,2]
-  v = dpp_max<0x4E>(v);    // quad_perm [2,3,0,1]
-  v = dpp_max<0x141>(v);   // row_half_mirror
-  v = dpp_max<0x140>(v);   // row_mirror
-  return fmaxf(v, shfl_xor(v, 16));
-}
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __builtin_bit_cast(uint32_t, x) & 0x7fffffffu; }
 
 template <bool FP8>
 __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParams p) {
@@ -212,14 +209,17 @@ __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParam
   // epilogue: lane holds column wn*128 + 32j + l32, rows wm*128 + 32i + 8(r/4) + 4hb + r%4
   if constexpr (!FP8) {
     bf16* out = (bf16*)(which ? p.v_out : p.k_out) + (int64_t)layer * p.out_layer_stride;
+    // the tile's rows m0 .. min(L, m0 + 256) - 1: stores past row L are dropped
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)(out + m0 * 256), 0, rows * 512, 0x00020000);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t grow = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * hb + (r & 3);
-        if (grow >= p.L) continue;
+        const int row = wm * 128 + 32 * i + 8 * (r >> 2) + 4 * hb + (r & 3);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) out[grow * 256 + wn * 128 + 32 * j + l32] = to_bf16(acc[i][j][r]);
+        for (int j = 0; j < 4; ++j)
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, to_bf16(acc[i][j][r])), ro,
+                                                (row * 256 + wn * 128 + 32 * j + l32) * 2, 0, 0);
       }
   } else {
     // row maxima of |v| over this wave's 128 columns (4 per lane, then the 32
@@ -228,13 +228,32 @@ __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParam
     float* rsc = red + 4 * 128;          // [256 rows] scale of each row of the tile
     float* rrc = rsc + 256;              // [256 rows] its correctly rounded reciprocal
     dma_barrier();                       // every wave is done reading the stage buffers
+    // eight rows go through each reduction step together, so that no DPP
+    // read waits for the write just before it
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float m = fmaxf(fmaxf(fabsf(acc[i][0][r]), fabsf(acc[i][1][r])), fmaxf(fabsf(acc[i][2][r]), fabsf(acc[i][3][r])));
-        m = half_wave_max(m);
-        if (l32 == 0) red[(wm * 2 + wn) * 128 + 32 * i + 8 * (r >> 2) + 4 * hb + (r & 3)] = m;
+      for (int r0 = 0; r0 < 16; r0 += 8) {
+        uint32_t m[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          m[r] = max(max(abs_bits(acc[i][0][r0 + r]), abs_bits(acc[i][1][r0 + r])),
+                     max(abs_bits(acc[i][2][r0 + r]), abs_bits(acc[i][3][r0 + r])));
+#pragma unroll
+        for (int r = 0; r < 8; ++r) m[r] = dpp_umax<0xB1>(m[r]);    // quad_perm [1,0,3,2]
+#pragma unroll
+        for (int r = 0; r < 8; ++r) m[r] = dpp_umax<0x4E>(m[r]);    // quad_perm [2,3,0,1]
+#pragma unroll
+        for (int r = 0; r < 8; ++r) m[r] = dpp_umax<0x141>(m[r]);   // row_half_mirror
+#pragma unroll
+        for (int r = 0; r < 8; ++r) m[r] = dpp_umax<0x140>(m[r]);   // row_mirror
+#pragma unroll
+        for (int r = 0; r < 8; ++r) m[r] = max(m[r], (uint32_t)__shfl_xor((int)m[r], 16, kWave));
+        if (l32 == 0) {
+#pragma unroll
+          for (int r = 0; r < 8; ++r)
+            red[(wm * 2 + wn) * 128 + 32 * i + 8 * ((r0 + r) >> 2) + 4 * hb + ((r0 + r) & 3)] = __builtin_bit_cast(float, m[r]);
+        }
       }
     dma_barrier();
     // one thread per row of the tile: the scale (and its reciprocal) is
@@ -250,6 +269,8 @@ __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParam
     }
     dma_barrier();
     uint8_t* out = (uint8_t*)(which ? p.v_out : p.k_out) + (int64_t)layer * p.out_layer_stride;
+    // the tile's rows m0 .. min(L, m0 + 256) - 1: stores past row L are dropped
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)(out + m0 * 256), 0, rows * 256, 0x00020000);
     // A lane holds the codes of columns 32j + l32 (j = 0..3) of a row; a 4 x 4
     // byte transpose inside each quad of lanes (two DPP swaps and two byte
     // permutes) gives lane 4a + t the codes of columns 32t + 4a .. +3, stored
@@ -264,7 +285,6 @@ __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParam
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 32 * i + 8 * (r >> 2) + 4 * hb + (r & 3);
-        const int64_t grow = m0 + wm * 128 + row;
         const float scale = rsc[wm * 128 + row], rcp = rrc[wm * 128 + row];
         float y[4];
 #pragma unroll
@@ -280,8 +300,8 @@ __global__ __launch_bounds__(BR_THREADS, 1) void bridge_kernel(const BridgeParam
         const int aa = (int)__builtin_amdgcn_perm((uint32_t)x, (uint32_t)d, sel1);
         const int yy = __builtin_amdgcn_mov_dpp(aa, 0x4E, 0xf, 0xf, false); // quad_perm [2,3,0,1]
         const int bb = (int)__builtin_amdgcn_perm((uint32_t)yy, (uint32_t)aa, sel2);
-        if (grow < p.L)
-          *(int*)(out + grow * 256 + wn * 128 + 32 * qt + 4 * (l32 >> 2)) = bb;
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)bb, ro, (wm * 128 + row) * 256 + wn * 128 + 32 * qt + 4 * (l32 >> 2),
+                                              0, 0);
       }
   }
 }
